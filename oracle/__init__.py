@@ -1,0 +1,23 @@
+"""CPU oracle for the ternary-weight x INT8 matmul: test infrastructure only.
+
+Only ``tests/``, the smoke check in ``__graft_entry__`` and the benchmark's
+CPU-baseline leg may import this package. It shares no code with the HIP
+library or its binding and imports nothing from them.
+"""
+
+from .ternary_ref import (  # noqa: F401
+    GROUP_K,
+    QMAX,
+    OracleError,
+    packed_bytes,
+    pack_ref,
+    unpack_ref,
+    quantize_ref,
+    matmul_loops,
+    matmul_int64,
+    matmul_f64,
+    matmul_ref,
+    matmul_rows_cols,
+    dequant_ref,
+    forward_ref,
+)
