@@ -1,0 +1,189 @@
+/*
+ * bt.h -- C ABI of the ternary-weight x INT8-activation matmul for AMD MI355X (gfx950).
+ *
+ * The operation ("VibeVoice-ASR-BitNet Technical Report", section 2.2.2): the
+ * decoder's linear layers hold weights in {-1, 0, +1} stored in 2 bits, with one
+ * fp32 scale per weight tensor; activations are quantized to INT8 online, per
+ * token; the kernel unpacks the 2-bit codes to INT8 and runs an integer
+ * multiply-add (section 2.4.2, Figure 4: each output is one weight row dotted
+ * with the activation vector, summed exactly). The tiling is chosen at run time
+ * from the matrix dimensions (section 2.4.2); here that is a GEMV for M <= 16
+ * and an MFMA GEMM above.
+ *
+ * Conventions shared by every entry point:
+ *   - Row-major throughout. Activations x / xq are M x K (K contiguous); the
+ *     weight matrix W is N x K (row n feeds output n); y and acc are M x N.
+ *   - The caller allocates and frees every buffer. The library allocates
+ *     nothing, keeps no mutable global state, and may be called from several
+ *     host threads.
+ *   - "host" pointers are ordinary CPU memory and the call is synchronous.
+ *     "device" pointers are GPU memory (hipMalloc or a torch CUDA tensor); such
+ *     calls are enqueued on `stream` and return before the GPU work runs.
+ *   - Arguments are validated on the host before anything is launched. On an
+ *     error nothing is launched and no output is written. Launch failures are
+ *     reported as BT_ERR_DEVICE.
+ *   - Device pointers must be 16-byte aligned (BT_ERR_ALIGN otherwise).
+ *   - Not checked on the device: x must be finite (NaN/Inf rows give
+ *     unspecified results), and a repacked weight buffer must come from
+ *     bt_repack_ternary with the same N and K.
+ */
+#ifndef BT_H
+#define BT_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum bt_status {
+    BT_OK = 0,
+    BT_ERR_NULL = 1,       /* a required pointer is NULL                            */
+    BT_ERR_SHAPE = 2,      /* M, N or K < 1, K % 128 != 0, or a size that overflows */
+    BT_ERR_VALUE = 3,      /* a weight outside {-1,0,1}, a 2-bit code 3, a bad scale */
+    BT_ERR_ALIGN = 4,      /* a device pointer not 16-byte aligned                   */
+    BT_ERR_DEVICE = 5,     /* the HIP runtime reported an error                      */
+    BT_ERR_WORKSPACE = 6   /* workspace missing or smaller than required             */
+} bt_status;
+
+/* Elements per packed group along K (blog post "Paper 說支援 ARM，我大概是第一個真的
+ * 去編譯的人", second postscript: the weight file stores codes in 128-element groups). */
+#define BT_GROUP_K 128
+/* Largest token count served by the GEMV path; larger M uses the MFMA GEMM. */
+#define BT_GEMV_MAX_M 16
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char* bt_status_string(bt_status status);
+
+/* ---------------------------------------------------------------------------
+ * Canonical packed format (host, synchronous).
+ *
+ * Technical report section 2.2.2: ternary weights in 2 bits; the blog post's
+ * second postscript: 128-element groups, interleaved so that the decoding
+ * depends on the group size. Code of a weight = w + 1 (-1 -> 0, 0 -> 1, +1 -> 2;
+ * code 3 is invalid). Row n occupies K/4 bytes; byte 32g + b of the row holds
+ * the elements 128g + 32s + b at bits 2s..2s+1, s = 0..3.
+ * ------------------------------------------------------------------------- */
+
+/* N*K/4 (one eighth of the FP16 matrix), or 0 if N < 1, K < 1 or K % 128 != 0. */
+size_t bt_packed_bytes(int64_t N, int64_t K);
+
+/* Pack w (host, N x K int8, values in {-1,0,1}) into packed (host, N*K/4 bytes).
+ * BT_ERR_VALUE if any weight is outside {-1,0,1}; packed is then left untouched. */
+bt_status bt_pack_ternary(const int8_t* w, int64_t N, int64_t K, uint8_t* packed);
+
+/* Inverse of bt_pack_ternary (host). BT_ERR_VALUE if any 2-bit field is 3. */
+bt_status bt_unpack_ternary(const uint8_t* packed, int64_t N, int64_t K, int8_t* w);
+
+/* ---------------------------------------------------------------------------
+ * Device repack (once per weight tensor, at load time).
+ *
+ * Permutes the canonical bytes into the kernels' fragment order: 16-row tiles,
+ * each 16-element run of one row in one 32-bit word, 256-element steps stored
+ * so that one 128-bit load per lane feeds four matrix-core steps. Rows are
+ * padded to a multiple of 16 with zero weights. The layout is private to the
+ * library; only bt_ternary_matmul* read it.
+ * ------------------------------------------------------------------------- */
+
+/* ceil(N/16)*16 * K/4, or 0 for invalid N, K. */
+size_t bt_repacked_bytes(int64_t N, int64_t K);
+
+/* packed_dev: device, bt_packed_bytes(N,K) canonical bytes.
+ * wdev: device, bt_repacked_bytes(N,K) bytes, written. Must not overlap packed_dev. */
+bt_status bt_repack_ternary(const uint8_t* packed_dev, int64_t N, int64_t K, void* wdev,
+                            hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * Per-token absmax INT8 quantization (technical report section 2.2.2:
+ * activations quantized to INT8 online per token).
+ *
+ * Per row m, each step in IEEE fp32: a = max_k |x[m,k]|; inv = 127 / a
+ * (correctly rounded); q = clamp(round_half_away_from_zero(x * inv), -127, 127);
+ * xscale[m] = a / 127; xsum[m] = sum_k q[m,k]. A row with a == 0, or whose
+ * 127 / a overflows, gives q = 0, xscale = 0, xsum = 0.
+ *
+ * x: device fp32 M x K. xq: device int8 M x K. xscale: device fp32 [M].
+ * xsum: device int32 [M], may be NULL. K need not be a multiple of 128.
+ * ------------------------------------------------------------------------- */
+bt_status bt_quantize_act(const float* x, int64_t M, int64_t K, int8_t* xq, float* xscale,
+                          int32_t* xsum, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * Ternary matmul with fp32 rescale (technical report section 2.4.2, Figure 4).
+ *
+ * acc[m,n] = sum_k xq[m,k] * w[n,k]   (exact int32; |acc| <= 127*K)
+ * y[m,n]   = fl32( fl32(acc[m,n]) * fl32(xscale[m] * w_scale) )
+ *
+ * xq, xscale, xsum: as written by bt_quantize_act (xsum is required: the
+ *   kernels multiply by the codes w+1 and subtract xsum).
+ * wdev: bt_repack_ternary output for this N, K.
+ * y: device fp32 M x N, written. acc: device int32 M x N or NULL.
+ * workspace: device, at least bt_matmul_workspace_bytes(M,N,K) bytes (may be
+ *   NULL when that is 0). It must be zero-filled before its first use; every
+ *   completed call leaves it zero-filled again. Calls that share one workspace
+ *   must be ordered on one stream.
+ * w_scale must be finite (BT_ERR_VALUE otherwise).
+ * ------------------------------------------------------------------------- */
+size_t bt_matmul_workspace_bytes(int64_t M, int64_t N, int64_t K);
+
+bt_status bt_ternary_matmul(int64_t M, int64_t N, int64_t K, const int8_t* xq,
+                            const float* xscale, const int32_t* xsum, const void* wdev,
+                            float w_scale, float* y, int32_t* acc, void* workspace,
+                            size_t workspace_bytes, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * Grouped launches: many independent projections in one kernel launch.
+ *
+ * The technical report's kernels have "batch" tiling variants chosen by shape
+ * (section 2.4.2); here a batch is a list of independent projections (for
+ * example all 112 linear layers of one decode step when their inputs are
+ * ready), so one launch keeps every compute unit streaming weights instead of
+ * paying one launch per small matrix.
+ *
+ * A plan is built once on the host from descriptors, copied by the caller into
+ * device memory (same bytes), and then launched any number of times. plan_host
+ * and plan_dev must hold identical bytes; the host copy sizes the grid and the
+ * device copy is read by the kernels. The buffers the descriptors point to must
+ * stay valid while the plan is in use.
+ * ------------------------------------------------------------------------- */
+typedef struct bt_quant_desc {
+    const float* x;   /* device fp32 M x K  */
+    int8_t* xq;       /* device int8 M x K  */
+    float* xscale;    /* device fp32 [M]    */
+    int32_t* xsum;    /* device int32 [M]   (required in a grouped plan) */
+    int64_t M, K;
+} bt_quant_desc;
+
+typedef struct bt_matmul_desc {
+    int64_t M, N, K;        /* M <= BT_GEMV_MAX_M in a grouped plan */
+    const int8_t* xq;
+    const float* xscale;
+    const int32_t* xsum;
+    const void* wdev;
+    float w_scale;
+    float* y;
+    int32_t* acc;           /* may be NULL */
+} bt_matmul_desc;
+
+size_t bt_quant_plan_bytes(int32_t count);
+bt_status bt_quant_plan_build(const bt_quant_desc* descs, int32_t count, void* plan_host,
+                              size_t plan_bytes);
+bt_status bt_quantize_act_grouped(const void* plan_host, const void* plan_dev,
+                                  hipStream_t stream);
+
+size_t bt_matmul_plan_bytes(int32_t count);
+bt_status bt_matmul_plan_build(const bt_matmul_desc* descs, int32_t count, void* plan_host,
+                               size_t plan_bytes);
+/* Grouped GEMV: every projection of the plan in one launch. A grouped plan never
+ * splits K across workgroups, so it needs no workspace. */
+bt_status bt_ternary_matmul_grouped(const void* plan_host, const void* plan_dev,
+                                    hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BT_H */

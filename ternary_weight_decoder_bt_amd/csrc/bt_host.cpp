@@ -1,0 +1,220 @@
+// Host half of libbt: status strings, the canonical 2-bit format, argument
+// checks shared with the device half, and plan building for grouped launches.
+// Nothing in this file touches the GPU.
+
+#include <string.h>
+
+#include <limits>
+
+#include "bt_internal.h"
+
+using bt::ceil_div;
+
+extern "C" const char* bt_status_string(bt_status s) {
+    switch (s) {
+        case BT_OK: return "ok";
+        case BT_ERR_NULL: return "a required pointer is NULL";
+        case BT_ERR_SHAPE: return "invalid shape (M, N, K >= 1 and K % 128 == 0 required)";
+        case BT_ERR_VALUE: return "invalid value (weight outside {-1,0,1}, code 3, or non-finite scale)";
+        case BT_ERR_ALIGN: return "device pointer not 16-byte aligned";
+        case BT_ERR_DEVICE: return "HIP runtime error";
+        case BT_ERR_WORKSPACE: return "workspace missing or too small";
+    }
+    return "unknown status";
+}
+
+static bool valid_nk(int64_t N, int64_t K) {
+    if (N < 1 || K < 1 || K % BT_GROUP_K) return false;
+    // every byte count and int32 index the kernels form must fit
+    if (N > (int64_t(1) << 30) || K > (int64_t(1) << 30)) return false;
+    const int64_t padded = ceil_div(N, bt::kTileN) * bt::kTileN;
+    return padded <= std::numeric_limits<int64_t>::max() / K;
+}
+
+extern "C" size_t bt_packed_bytes(int64_t N, int64_t K) {
+    return valid_nk(N, K) ? size_t(N) * size_t(K) / 4 : 0;
+}
+
+extern "C" size_t bt_repacked_bytes(int64_t N, int64_t K) {
+    return valid_nk(N, K) ? size_t(ceil_div(N, bt::kTileN) * bt::kTileN) * size_t(K) / 4 : 0;
+}
+
+// Canonical layout (blog post "Paper 說支援 ARM，我大概是第一個真的去編譯的人",
+// second postscript: 128-element groups; technical report section 2.2.2: 2-bit
+// codes). Byte b of group g holds the codes of elements 32s + b, s = 0..3, at
+// bits 2s..2s+1; code = w + 1.
+extern "C" bt_status bt_pack_ternary(const int8_t* w, int64_t N, int64_t K, uint8_t* packed) {
+    if (!w || !packed) return BT_ERR_NULL;
+    if (!valid_nk(N, K)) return BT_ERR_SHAPE;
+    const size_t total = size_t(N) * size_t(K);
+    uint8_t bad = 0;
+    for (size_t i = 0; i < total; ++i) bad |= uint8_t(uint8_t(w[i] + 1) > 2);
+    if (bad) return BT_ERR_VALUE;
+    const int64_t groups = K / BT_GROUP_K;
+    for (int64_t n = 0; n < N; ++n) {
+        const int8_t* row = w + n * K;
+        uint8_t* out = packed + n * (K / 4);
+        for (int64_t g = 0; g < groups; ++g) {
+            const int8_t* src = row + g * BT_GROUP_K;
+            for (int b = 0; b < 32; ++b) {
+                out[g * 32 + b] = uint8_t((src[b] + 1) | ((src[32 + b] + 1) << 2) |
+                                          ((src[64 + b] + 1) << 4) | ((src[96 + b] + 1) << 6));
+            }
+        }
+    }
+    return BT_OK;
+}
+
+extern "C" bt_status bt_unpack_ternary(const uint8_t* packed, int64_t N, int64_t K, int8_t* w) {
+    if (!w || !packed) return BT_ERR_NULL;
+    if (!valid_nk(N, K)) return BT_ERR_SHAPE;
+    const size_t bytes = size_t(N) * size_t(K) / 4;
+    for (size_t i = 0; i < bytes; ++i) {
+        const uint8_t v = packed[i];
+        // a pair equal to 0b11 has both of its bits set
+        if ((v & (v >> 1) & 0x55u) != 0) return BT_ERR_VALUE;
+    }
+    const int64_t groups = K / BT_GROUP_K;
+    for (int64_t n = 0; n < N; ++n) {
+        const uint8_t* in = packed + n * (K / 4);
+        int8_t* row = w + n * K;
+        for (int64_t g = 0; g < groups; ++g) {
+            for (int s = 0; s < 4; ++s)
+                for (int b = 0; b < 32; ++b)
+                    row[g * BT_GROUP_K + 32 * s + b] = int8_t(((in[g * 32 + b] >> (2 * s)) & 3) - 1);
+        }
+    }
+    return BT_OK;
+}
+
+namespace bt {
+
+// Split-K policy of the single-matrix GEMV. A small matrix (e.g. 1536 rows)
+// has too few 16-row tiles to keep 256 compute units streaming, so K is cut
+// into chunks of at least two 256-wide steps until about 1024 workgroups exist.
+void gemv_shape(int64_t M, int64_t N, int64_t K, GemvDesc* d) {
+    memset(d, 0, sizeof(*d));
+    d->M = int32_t(M);
+    d->N = int32_t(N);
+    d->K = int32_t(K);
+    d->tiles = int32_t(ceil_div(N, kTileN));
+    d->full_steps = int32_t(K / kSuperK);
+    d->half_step = int32_t((K % kSuperK) != 0);
+    const int64_t steps = d->full_steps + d->half_step;
+    const int64_t wg_per_chunk = ceil_div(d->tiles, kGemvWaves);
+    constexpr int64_t kTargetBlocks = 1024;
+    constexpr int64_t kMinStepsPerChunk = 2;
+    int64_t chunks = 1;
+    if (wg_per_chunk < kTargetBlocks) {
+        chunks = ceil_div(kTargetBlocks, wg_per_chunk);
+        const int64_t max_chunks = ceil_div(steps, kMinStepsPerChunk);
+        if (chunks > max_chunks) chunks = max_chunks;
+        if (chunks < 1) chunks = 1;
+    }
+    int64_t spc = ceil_div(steps, chunks);
+    chunks = ceil_div(steps, spc);
+    d->chunks = int32_t(chunks);
+    d->steps_per_chunk = int32_t(spc);
+    d->blocks = wg_per_chunk * chunks;
+}
+
+size_t gemv_workspace_bytes(const GemvDesc& d) {
+    if (d.chunks <= 1) return 0;
+    const size_t partial = size_t(d.M) * size_t(d.tiles) * kTileN * sizeof(int32_t);
+    const size_t partial_aligned = (partial + 255) & ~size_t(255);
+    return partial_aligned + ((size_t(d.tiles) * sizeof(uint32_t) + 255) & ~size_t(255));
+}
+
+}  // namespace bt
+
+extern "C" size_t bt_matmul_workspace_bytes(int64_t M, int64_t N, int64_t K) {
+    if (M < 1 || !valid_nk(N, K)) return 0;
+    if (M > BT_GEMV_MAX_M) return 0;   // the GEMM path splits nothing
+    bt::GemvDesc d;
+    bt::gemv_shape(M, N, K, &d);
+    return bt::gemv_workspace_bytes(d);
+}
+
+// ------------------------------------------------------------------ plans
+
+extern "C" size_t bt_quant_plan_bytes(int32_t count) {
+    if (count < 1) return 0;
+    return sizeof(bt::PlanHeader) + size_t(count) * sizeof(bt::QuantDesc);
+}
+
+extern "C" bt_status bt_quant_plan_build(const bt_quant_desc* descs, int32_t count,
+                                         void* plan_host, size_t plan_bytes) {
+    if (!descs || !plan_host) return BT_ERR_NULL;
+    if (count < 1) return BT_ERR_SHAPE;
+    if (plan_bytes < bt_quant_plan_bytes(count)) return BT_ERR_WORKSPACE;
+    auto* hdr = static_cast<bt::PlanHeader*>(plan_host);
+    auto* out = reinterpret_cast<bt::QuantDesc*>(hdr + 1);
+    int64_t rows = 0;
+    for (int32_t i = 0; i < count; ++i) {
+        const bt_quant_desc& q = descs[i];
+        if (!q.x || !q.xq || !q.xscale || !q.xsum) return BT_ERR_NULL;
+        if (q.M < 1 || q.K < 1 || q.K > (int64_t(1) << 30) || q.M > (int64_t(1) << 31))
+            return BT_ERR_SHAPE;
+        if (!bt::aligned16(q.x) || !bt::aligned16(q.xq) || !bt::aligned16(q.xscale) ||
+            !bt::aligned16(q.xsum))
+            return BT_ERR_ALIGN;
+    }
+    for (int32_t i = 0; i < count; ++i) {
+        const bt_quant_desc& q = descs[i];
+        out[i] = bt::QuantDesc{q.x, q.xq, q.xscale, q.xsum, q.M, q.K, rows};
+        rows += q.M;
+    }
+    if (rows > int64_t(1) << 31) return BT_ERR_SHAPE;
+    hdr->magic = bt::kPlanMagicQuant;
+    hdr->count = count;
+    hdr->total_blocks = rows;
+    return BT_OK;
+}
+
+extern "C" size_t bt_matmul_plan_bytes(int32_t count) {
+    if (count < 1) return 0;
+    return sizeof(bt::PlanHeader) + size_t(count) * sizeof(bt::GemvDesc);
+}
+
+extern "C" bt_status bt_matmul_plan_build(const bt_matmul_desc* descs, int32_t count,
+                                          void* plan_host, size_t plan_bytes) {
+    if (!descs || !plan_host) return BT_ERR_NULL;
+    if (count < 1) return BT_ERR_SHAPE;
+    if (plan_bytes < bt_matmul_plan_bytes(count)) return BT_ERR_WORKSPACE;
+    for (int32_t i = 0; i < count; ++i) {
+        const bt_matmul_desc& m = descs[i];
+        if (!m.xq || !m.xscale || !m.xsum || !m.wdev || !m.y) return BT_ERR_NULL;
+        if (m.M < 1 || m.M > BT_GEMV_MAX_M || !valid_nk(m.N, m.K)) return BT_ERR_SHAPE;
+        if (!bt::aligned16(m.xq) || !bt::aligned16(m.xscale) || !bt::aligned16(m.xsum) ||
+            !bt::aligned16(m.wdev) || !bt::aligned16(m.y) || (m.acc && !bt::aligned16(m.acc)))
+            return BT_ERR_ALIGN;
+        if (!(m.w_scale == m.w_scale) || m.w_scale - m.w_scale != 0.0f) return BT_ERR_VALUE;
+    }
+    auto* hdr = static_cast<bt::PlanHeader*>(plan_host);
+    auto* out = reinterpret_cast<bt::GemvDesc*>(hdr + 1);
+    int64_t blocks = 0;
+    for (int32_t i = 0; i < count; ++i) {
+        const bt_matmul_desc& m = descs[i];
+        bt::GemvDesc d;
+        bt::gemv_shape(m.M, m.N, m.K, &d);
+        // a grouped launch has parallelism across problems: never split K
+        d.chunks = 1;
+        d.steps_per_chunk = d.full_steps + d.half_step;
+        d.blocks = ceil_div(d.tiles, bt::kGemvWaves);
+        d.xq = m.xq;
+        d.xscale = m.xscale;
+        d.xsum = m.xsum;
+        d.w = static_cast<const uint8_t*>(m.wdev);
+        d.y = m.y;
+        d.acc = m.acc;
+        d.w_scale = m.w_scale;
+        d.block_begin = blocks;
+        blocks += d.blocks;
+        out[i] = d;
+    }
+    if (blocks > int64_t(1) << 31) return BT_ERR_SHAPE;
+    hdr->magic = bt::kPlanMagicGemv;
+    hdr->count = count;
+    hdr->total_blocks = blocks;
+    return BT_OK;
+}

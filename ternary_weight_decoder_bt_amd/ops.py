@@ -1,0 +1,227 @@
+"""Python binding of the bt C ABI: argument marshalling only.
+
+Every computation runs in libbt (host packing in C++, everything else in HIP
+kernels). PyTorch supplies device memory and the current HIP stream; NumPy
+arrays carry host buffers.
+"""
+
+from __future__ import annotations
+
+import ctypes as C
+
+import numpy as np
+
+from ._lib import BtMatmulDesc, BtQuantDesc, BtError, check, lib
+
+GROUP_K = 128
+GEMV_MAX_M = 16
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _stream(stream=None) -> int:
+    torch = _torch()
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return int(s.cuda_stream)
+
+
+def _ptr(t) -> int | None:
+    return None if t is None else int(t.data_ptr())
+
+
+def _np_ptr(a: np.ndarray) -> int:
+    return a.ctypes.data
+
+
+def _dev(t, dtype, shape, name):
+    torch = _torch()
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError(f"{name} must be a CUDA tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    return t
+
+
+# ------------------------------------------------------------------ sizes
+
+def packed_bytes(n: int, k: int) -> int:
+    return int(lib().bt_packed_bytes(n, k))
+
+
+def repacked_bytes(n: int, k: int) -> int:
+    return int(lib().bt_repacked_bytes(n, k))
+
+
+def matmul_workspace_bytes(m: int, n: int, k: int) -> int:
+    return int(lib().bt_matmul_workspace_bytes(m, n, k))
+
+
+# ------------------------------------------------------------- host format
+
+def pack_ternary(w: np.ndarray) -> np.ndarray:
+    """int8 (N, K) in {-1,0,1} -> canonical uint8 (N, K/4) (host, bt_pack_ternary)."""
+    w = np.ascontiguousarray(w, dtype=np.int8)
+    if w.ndim != 2:
+        raise ValueError("w must be (N, K)")
+    n, k = w.shape
+    out = np.empty((n, max(k // 4, 0)), np.uint8)
+    check(lib().bt_pack_ternary(_np_ptr(w), n, k, _np_ptr(out)), "bt_pack_ternary")
+    return out
+
+
+def unpack_ternary(packed: np.ndarray, k: int) -> np.ndarray:
+    """Canonical uint8 (N, K/4) -> int8 (N, K) (host, bt_unpack_ternary)."""
+    packed = np.ascontiguousarray(packed, dtype=np.uint8)
+    n = packed.shape[0]
+    if packed.shape[1] != k // 4:
+        raise ValueError("packed width must be K/4")
+    out = np.empty((n, k), np.int8)
+    check(lib().bt_unpack_ternary(_np_ptr(packed), n, k, _np_ptr(out)), "bt_unpack_ternary")
+    return out
+
+
+# ------------------------------------------------------------------ device
+
+def repack_ternary(packed_dev, n: int, k: int, out=None, stream=None):
+    """Canonical bytes on the device -> the kernels' tile layout (bt_repack_ternary)."""
+    torch = _torch()
+    _dev(packed_dev, torch.uint8, None, "packed_dev")
+    if packed_dev.numel() != packed_bytes(n, k):
+        raise ValueError("packed_dev must hold N*K/4 bytes")
+    nbytes = repacked_bytes(n, k)
+    if out is None:
+        out = torch.empty(nbytes, dtype=torch.uint8, device=packed_dev.device)
+    _dev(out, torch.uint8, (nbytes,), "out")
+    check(lib().bt_repack_ternary(_ptr(packed_dev), n, k, _ptr(out), _stream(stream)),
+          "bt_repack_ternary")
+    return out
+
+
+def quantize_act(x, xq=None, xscale=None, xsum=None, stream=None):
+    """fp32 (M, K) -> (int8 (M, K), fp32 (M,), int32 (M,)) via bt_quantize_act."""
+    torch = _torch()
+    _dev(x, torch.float32, None, "x")
+    if x.dim() != 2:
+        raise ValueError("x must be (M, K)")
+    m, k = x.shape
+    if xq is None:
+        xq = torch.empty((m, k), dtype=torch.int8, device=x.device)
+    if xscale is None:
+        xscale = torch.empty(m, dtype=torch.float32, device=x.device)
+    if xsum is None:
+        xsum = torch.empty(m, dtype=torch.int32, device=x.device)
+    _dev(xq, torch.int8, (m, k), "xq")
+    _dev(xscale, torch.float32, (m,), "xscale")
+    _dev(xsum, torch.int32, (m,), "xsum")
+    check(lib().bt_quantize_act(_ptr(x), m, k, _ptr(xq), _ptr(xscale), _ptr(xsum),
+                                _stream(stream)), "bt_quantize_act")
+    return xq, xscale, xsum
+
+
+def new_workspace(m: int, n: int, k: int, device="cuda"):
+    """Zero-filled workspace for bt_ternary_matmul (None when none is needed)."""
+    torch = _torch()
+    nbytes = matmul_workspace_bytes(m, n, k)
+    return torch.zeros(nbytes, dtype=torch.uint8, device=device) if nbytes else None
+
+
+def ternary_matmul(xq, xscale, xsum, wdev, n: int, w_scale: float, y=None, acc=None,
+                   workspace=None, want_acc=False, stream=None):
+    """y = (xq @ W^T) * xscale * w_scale via bt_ternary_matmul; returns y (and acc)."""
+    torch = _torch()
+    _dev(xq, torch.int8, None, "xq")
+    m, k = xq.shape
+    _dev(xscale, torch.float32, (m,), "xscale")
+    _dev(xsum, torch.int32, (m,), "xsum")
+    _dev(wdev, torch.uint8, (repacked_bytes(n, k),), "wdev")
+    if y is None:
+        y = torch.empty((m, n), dtype=torch.float32, device=xq.device)
+    _dev(y, torch.float32, (m, n), "y")
+    if acc is None and want_acc:
+        acc = torch.empty((m, n), dtype=torch.int32, device=xq.device)
+    if acc is not None:
+        _dev(acc, torch.int32, (m, n), "acc")
+    need = matmul_workspace_bytes(m, n, k)
+    if need and workspace is None:
+        workspace = new_workspace(m, n, k, xq.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    check(lib().bt_ternary_matmul(m, n, k, _ptr(xq), _ptr(xscale), _ptr(xsum), _ptr(wdev),
+                                  float(w_scale), _ptr(y), _ptr(acc), _ptr(workspace), ws_bytes,
+                                  _stream(stream)), "bt_ternary_matmul")
+    return (y, acc) if (want_acc or acc is not None) else y
+
+
+# ------------------------------------------------------------------ grouped
+
+class _Plan:
+    def __init__(self, host: np.ndarray, device):
+        torch = _torch()
+        self.host = host
+        self.dev = torch.from_numpy(host).to(device)
+        torch.cuda.current_stream(device).synchronize()
+
+    def _ptrs(self):
+        return _np_ptr(self.host), _ptr(self.dev)
+
+
+class QuantPlan(_Plan):
+    """Many independent quantizations in one launch (bt_quantize_act_grouped).
+
+    items: sequence of (x, xq, xscale, xsum) CUDA tensors.
+    """
+
+    def __init__(self, items):
+        descs = (BtQuantDesc * len(items))()
+        self._keep = list(items)
+        for i, (x, xq, xs, xsum) in enumerate(items):
+            m, k = x.shape
+            descs[i] = BtQuantDesc(_ptr(x), _ptr(xq), _ptr(xs), _ptr(xsum), m, k)
+        nbytes = int(lib().bt_quant_plan_bytes(len(items)))
+        host = np.zeros(nbytes, np.uint8)
+        check(lib().bt_quant_plan_build(descs, len(items), _np_ptr(host), nbytes),
+              "bt_quant_plan_build")
+        super().__init__(host, items[0][0].device)
+
+    def launch(self, stream=None):
+        h, d = self._ptrs()
+        check(lib().bt_quantize_act_grouped(h, d, _stream(stream)), "bt_quantize_act_grouped")
+
+
+class MatmulPlan(_Plan):
+    """Many independent GEMVs (M <= 16) in one launch (bt_ternary_matmul_grouped).
+
+    items: sequence of dicts with keys xq, xscale, xsum, wdev, n, w_scale, y,
+    and optionally acc.
+    """
+
+    def __init__(self, items):
+        descs = (BtMatmulDesc * len(items))()
+        self._keep = list(items)
+        for i, it in enumerate(items):
+            m, k = it["xq"].shape
+            descs[i] = BtMatmulDesc(m, it["n"], k, _ptr(it["xq"]), _ptr(it["xscale"]),
+                                    _ptr(it["xsum"]), _ptr(it["wdev"]), float(it["w_scale"]),
+                                    _ptr(it["y"]), _ptr(it.get("acc")))
+        nbytes = int(lib().bt_matmul_plan_bytes(len(items)))
+        host = np.zeros(nbytes, np.uint8)
+        check(lib().bt_matmul_plan_build(descs, len(items), _np_ptr(host), nbytes),
+              "bt_matmul_plan_build")
+        super().__init__(host, items[0]["xq"].device)
+
+    def launch(self, stream=None):
+        h, d = self._ptrs()
+        check(lib().bt_ternary_matmul_grouped(h, d, _stream(stream)), "bt_ternary_matmul_grouped")
+
+
+__all__ = [
+    "BtError", "GROUP_K", "GEMV_MAX_M", "packed_bytes", "repacked_bytes",
+    "matmul_workspace_bytes", "pack_ternary", "unpack_ternary", "repack_ternary",
+    "quantize_act", "new_workspace", "ternary_matmul", "QuantPlan", "MatmulPlan",
+]

@@ -1,0 +1,305 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle.
+
+Bar (from the method's definition: exact integer sums, then one fp32 rescale):
+int8 q, fp32 d, int32 row sums and int32 accumulators bit-exact; fp32 y within
+1e-6 relative (and exactly 0 where the oracle's y is 0). Every output buffer
+is filled with NaN / an impossible integer before each call, so an element a
+kernel forgets to write is caught (the blog post's NaN-at-batch-4/5 bug came
+from a remainder path that left outputs unwritten).
+"""
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+import ternary_weight_decoder_bt_amd as bt  # noqa: E402
+
+RTOL = 1e-6
+POISON_I32 = np.iinfo(np.int32).min   # |acc| <= 127*K never reaches it
+
+
+@pytest.fixture(scope="module")
+def dev():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    return torch.device("cuda:0")
+
+
+def assert_exact(name, got, want):
+    got, want = np.asarray(got), np.asarray(want)
+    assert got.shape == want.shape, (name, got.shape, want.shape)
+    if not np.array_equal(got, want):
+        bad = np.argwhere(got != want)
+        i = tuple(bad[0])
+        raise AssertionError(f"{name}: {len(bad)} mismatches; first {i}: got {got[i]} want {want[i]}")
+
+
+def assert_rel(name, got, want, rtol=RTOL):
+    got = np.asarray(got, np.float64)
+    want = np.asarray(want, np.float64)
+    assert got.shape == want.shape
+    assert np.isfinite(got).all(), f"{name}: non-finite output (unwritten element?)"
+    zero = want == 0
+    assert (got[zero] == 0).all(), f"{name}: nonzero where the oracle is exactly 0"
+    rel = np.abs(got[~zero] - want[~zero]) / np.abs(want[~zero])
+    assert rel.size == 0 or rel.max() <= rtol, f"{name}: max rel err {rel.max():.3e}"
+
+
+def to_dev(a, dev):
+    return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+
+def load_weights(w, dev):
+    n, k = w.shape
+    packed = to_dev(bt.pack_ternary(w).reshape(-1), dev)
+    return bt.repack_ternary(packed, n, k)
+
+
+def run_quantize(x, dev):
+    m, k = x.shape
+    xd = to_dev(x, dev)
+    xq = torch.full((m, k), 99, dtype=torch.int8, device=dev)
+    xs = torch.full((m,), float("nan"), dtype=torch.float32, device=dev)
+    xsum = torch.full((m,), POISON_I32, dtype=torch.int32, device=dev)
+    bt.quantize_act(xd, xq, xs, xsum)
+    return xq, xs, xsum
+
+
+def run_matmul(xq, xs, xsum, wdev, n, w_scale, dev, workspace=None):
+    m = xq.shape[0]
+    y = torch.full((m, n), float("nan"), dtype=torch.float32, device=dev)
+    acc = torch.full((m, n), POISON_I32, dtype=torch.int32, device=dev)
+    bt.ternary_matmul(xq, xs, xsum, wdev, n, w_scale, y=y, acc=acc, workspace=workspace)
+    return y, acc
+
+
+def check_full(case, dev, mode="f64", wdev=None):
+    """The whole path on one projection, every output compared."""
+    x, w, s = case["x"], case["w"], case["w_scale"]
+    n = w.shape[0]
+    ref = oracle.forward_ref(x, w, s, mode)
+    xq, xs, xsum = run_quantize(x, dev)
+    if wdev is None:
+        wdev = load_weights(w, dev)
+    y, acc = run_matmul(xq, xs, xsum, wdev, n, s, dev)
+    torch.cuda.synchronize()
+    assert_exact("q", xq.cpu().numpy(), ref["q"])
+    assert_exact("d", xs.cpu().numpy(), ref["d"])
+    assert_exact("qsum", xsum.cpu().numpy(), ref["qsum"])
+    assert_exact("acc", acc.cpu().numpy(), ref["acc"])
+    assert_rel("y", y.cpu().numpy(), ref["y"])
+    return y, acc
+
+
+# ------------------------------------------------------------ quantization
+
+def test_quantize_single_gemv_input(dev):
+    x = synth.config0()["x"]
+    q, d, s = oracle.quantize_ref(x)
+    xq, xs, xsum = run_quantize(x, dev)
+    assert_exact("q", xq.cpu().numpy(), q)
+    assert_exact("d", xs.cpu().numpy(), d)
+    assert_exact("qsum", xsum.cpu().numpy(), s)
+
+
+@pytest.mark.parametrize("m,k,dist", [(1, 8960, "outlier"), (7, 1536, "t3"), (64, 129, "normal"),
+                                      (3, 20000, "t3"), (5, 6, "normal"), (300, 1536, "outlier")])
+def test_quantize_shapes(dev, m, k, dist):
+    rng = np.random.default_rng(m * 7 + k)
+    x = {"normal": lambda: rng.standard_normal((m, k), dtype=np.float32),
+         "t3": lambda: rng.standard_t(3, (m, k)).astype(np.float32),
+         "outlier": lambda: rng.standard_normal((m, k), dtype=np.float32) *
+         np.where(rng.random((m, k)) < 0.001, np.float32(20), np.float32(1))}[dist]()
+    q, d, s = oracle.quantize_ref(x)
+    xq, xs, xsum = run_quantize(x, dev)
+    assert_exact("q", xq.cpu().numpy(), q)
+    assert_exact("d", xs.cpu().numpy(), d)
+    assert_exact("qsum", xsum.cpu().numpy(), s)
+
+
+def test_quantize_long_prefill_rows(dev):
+    for proj in (0, 3):
+        x = synth.long_prefill_problem(0, proj, with_weights=False)["x"]
+        q, d, s = oracle.quantize_ref(x)
+        xq, xs, xsum = run_quantize(x, dev)
+        assert_exact(f"q[{proj}]", xq.cpu().numpy(), q)
+        assert_exact(f"d[{proj}]", xs.cpu().numpy(), d)
+        assert_exact(f"qsum[{proj}]", xsum.cpu().numpy(), s)
+
+
+def test_quantize_golden_ties(dev, golden):
+    rows = golden("quantize_worked.txt")
+    xs = {r[0]: [np.float32(v) for v in r[2:]] for r in rows if r[1] == "x"}
+    qs = {r[0]: [int(v) for v in r[2:]] for r in rows if r[1] == "q"}
+    labels = sorted(xs)
+    for width in (6, 8, 128):        # scalar path, vector path, vector path with padding
+        x = np.zeros((len(labels), width), np.float32)
+        want = np.zeros((len(labels), width), np.int8)
+        for i, l in enumerate(labels):
+            x[i, :6] = xs[l]
+            want[i, :6] = qs[l]
+        xq, _, _ = run_quantize(x, dev)
+        assert_exact(f"q(width {width})", xq.cpu().numpy(), want)
+
+
+def test_quantize_tiny_and_zero_rows(dev):
+    x = np.zeros((5, 256), np.float32)
+    x[0, 5] = np.float32(1e-39)
+    x[1, 6] = np.float32(-1e-37)
+    x[2, 7], x[2, 8] = np.float32(1e-36), np.float32(-5e-37)
+    x[4] = np.random.default_rng(1).standard_normal(256).astype(np.float32)
+    q, d, s = oracle.quantize_ref(x)
+    assert 0 < d[2] < np.finfo(np.float32).tiny
+    xq, xs, xsum = run_quantize(x, dev)
+    assert_exact("q", xq.cpu().numpy(), q)
+    assert_exact("d", xs.cpu().numpy(), d)
+    assert_exact("qsum", xsum.cpu().numpy(), s)
+
+
+# ----------------------------------------------------------------- matmul
+
+def test_single_gemv_workload(dev):
+    check_full(synth.config0(), dev, mode="int64")
+
+
+@pytest.mark.parametrize("m", list(range(1, 17)))
+def test_gemv_every_m_ragged(dev, m):
+    # N = 40 leaves a partial 16-row tile; K = 384 ends with a 128-wide step
+    check_full(synth.small_problem(2, m, 40, 384), dev, mode="loops" if m <= 2 else "int64")
+
+
+@pytest.mark.parametrize("m,n,k", [(1, 40, 1536), (5, 1536, 1536), (16, 1536, 8960),
+                                   (3, 17, 128), (1, 1, 128), (8, 2048, 1664)])
+def test_gemv_split_k_and_edges(dev, m, n, k):
+    check_full(synth.small_problem(3, m, n, k, "outlier"), dev)
+
+
+_REMAINDER_W = {}
+
+
+@pytest.mark.parametrize("proj", ["gate_up", "down"])
+@pytest.mark.parametrize("m", synth.REMAINDER_MS)
+def test_decode_remainder_sweep(dev, proj, m):
+    c = synth.decode_remainder_problem(proj, m)
+    key = proj
+    if key not in _REMAINDER_W:
+        _REMAINDER_W.clear()
+        _REMAINDER_W[key] = load_weights(c["w"], dev)
+    check_full(c, dev, wdev=_REMAINDER_W[key])
+
+
+@pytest.mark.parametrize("m,n,k", [(17, 40, 384), (33, 200, 128), (100, 2048, 1536),
+                                   (128, 128, 256), (129, 130, 1664), (300, 1536, 8960)])
+def test_gemm_shapes(dev, m, n, k):
+    check_full(synth.small_problem(4, m, n, k, "t3", (0.3, 0.4, 0.3)), dev)
+
+
+@pytest.mark.parametrize("proj", [0, 1, 2, 3])
+def test_prefill_one_layer(dev, proj):
+    check_full(synth.prefill_problem(proj), dev)
+
+
+@pytest.mark.parametrize("layer,proj", [(0, 0), (0, 1), (0, 2), (0, 3), (27, 3)])
+def test_long_prefill_sampled(dev, layer, proj):
+    c = synth.long_prefill_problem(layer, proj)
+    x, w, s = c["x"], c["w"], c["w_scale"]
+    m, n = x.shape[0], w.shape[0]
+    q, d, qs = oracle.quantize_ref(x)
+    xq, xs, xsum = run_quantize(x, dev)
+    y, acc = run_matmul(xq, xs, xsum, load_weights(w, dev), n, s, dev)
+    torch.cuda.synchronize()
+    assert_exact("q", xq.cpu().numpy(), q)
+    assert_exact("d", xs.cpu().numpy(), d)
+    y, acc = y.cpu().numpy(), acc.cpu().numpy()
+    rng = np.random.default_rng(layer * 10 + proj)
+    rows = np.unique(np.r_[0, 1, 127, 128, m - 1, rng.integers(0, m, 6)])
+    cols = np.unique(np.r_[0, 15, 16, n - 1, rng.integers(0, n, 6)])
+    acc_rows = oracle.matmul_ref(q[rows], w, "f64")
+    acc_cols = oracle.matmul_ref(q, w[cols], "f64")
+    assert_exact("acc rows", acc[rows], acc_rows)
+    assert_exact("acc cols", acc[:, cols], acc_cols)
+    assert_rel("y rows", y[rows], oracle.dequant_ref(acc_rows, d[rows], s))
+    assert_rel("y cols", y[:, cols], oracle.dequant_ref(acc_cols, d, s))
+    assert np.isfinite(y).all() and (acc != POISON_I32).all()
+
+
+def test_worst_case_accumulator(dev):
+    k = 8960
+    for m in (1, 32):
+        x = np.ones((m, k), np.float32)
+        w = np.ones((32, k), np.int8)
+        w[16:] = -1
+        y, acc = check_full({"x": x, "w": w, "w_scale": np.float32(0.5)}, dev)
+        a = acc.cpu().numpy()
+        assert (a[:, :16] == 1_137_920).all() and (a[:, 16:] == -1_137_920).all()
+
+
+@pytest.mark.parametrize("m", [1, 4, 16, 48])
+def test_layout_identity_and_one_hot(dev, m):
+    rng = np.random.default_rng(m)
+    k = 256
+    x = rng.standard_normal((m, k), dtype=np.float32)
+    q, _, _ = oracle.quantize_ref(x)
+    xq, xs, xsum = run_quantize(x, dev)
+    _, acc = run_matmul(xq, xs, xsum, load_weights(np.eye(k, dtype=np.int8), dev), k, 1.0, dev)
+    assert_exact("identity", acc.cpu().numpy(), q.astype(np.int32))
+    kstar = rng.integers(0, k, 48)
+    w = np.zeros((48, k), np.int8)
+    w[np.arange(48), kstar] = 1
+    _, acc = run_matmul(xq, xs, xsum, load_weights(w, dev), 48, 1.0, dev)
+    assert_exact("one-hot", acc.cpu().numpy(), q[:, kstar].astype(np.int32))
+
+
+def test_zero_row_in_batch_gives_zero_output(dev):
+    for m in (4, 20):
+        c = synth.small_problem(5, m, 64, 256)
+        c["x"][1] = 0
+        y, _ = check_full(c, dev)
+        assert (y.cpu().numpy()[1] == 0).all()
+
+
+def test_deterministic_and_workspace_left_clean(dev):
+    c = synth.small_problem(6, 16, 1536, 8960)
+    wdev = load_weights(c["w"], dev)
+    xq, xs, xsum = run_quantize(c["x"], dev)
+    ws = bt.new_workspace(16, 1536, 8960, dev)
+    assert ws is not None
+    y1, a1 = run_matmul(xq, xs, xsum, wdev, 1536, c["w_scale"], dev, workspace=ws)
+    y2, a2 = run_matmul(xq, xs, xsum, wdev, 1536, c["w_scale"], dev, workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(a1, a2) and torch.equal(y1.view(torch.int32), y2.view(torch.int32))
+    assert int(ws.count_nonzero()) == 0
+
+
+# ------------------------------------------------------------------ grouped
+
+def test_grouped_decode_layers(dev):
+    items_q, items_m, refs = [], [], []
+    for layer in (0, 27):
+        for proj in range(4):
+            c = synth.decode_problem(layer, proj)
+            m, k, n = c["M"], c["K"], c["N"]
+            x = to_dev(c["x"], dev)
+            xq = torch.full((m, k), 99, dtype=torch.int8, device=dev)
+            xs = torch.full((m,), float("nan"), dtype=torch.float32, device=dev)
+            xsum = torch.full((m,), POISON_I32, dtype=torch.int32, device=dev)
+            y = torch.full((m, n), float("nan"), dtype=torch.float32, device=dev)
+            acc = torch.full((m, n), POISON_I32, dtype=torch.int32, device=dev)
+            items_q.append((x, xq, xs, xsum))
+            items_m.append({"xq": xq, "xscale": xs, "xsum": xsum, "wdev": load_weights(c["w"], dev),
+                            "n": n, "w_scale": c["w_scale"], "y": y, "acc": acc})
+            refs.append(oracle.forward_ref(c["x"], c["w"], c["w_scale"], "f64"))
+    qp, mp = bt.QuantPlan(items_q), bt.MatmulPlan(items_m)
+    for rep in range(2):
+        qp.launch()
+        mp.launch()
+        torch.cuda.synchronize()
+        for i, (it, ref) in enumerate(zip(items_m, refs)):
+            assert_exact(f"q[{i}]", it["xq"].cpu().numpy(), ref["q"])
+            assert_exact(f"acc[{i}]", it["acc"].cpu().numpy(), ref["acc"])
+            assert_rel(f"y[{i}]", it["y"].cpu().numpy(), ref["y"])

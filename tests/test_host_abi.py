@@ -1,0 +1,178 @@
+"""Host-side checks of libbt on a machine without a GPU.
+
+The library loads and exports every function include/bt.h declares; the C++
+canonical packing agrees byte for byte with the oracle; every error path
+returns its documented status before anything is launched (so no call here
+reaches the GPU).
+"""
+
+import ctypes as C
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle
+import ternary_weight_decoder_bt_amd as bt
+from ternary_weight_decoder_bt_amd import _lib
+from ternary_weight_decoder_bt_amd._lib import BtMatmulDesc, BtQuantDesc
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "bt.h")
+
+OK, NULL, SHAPE, VALUE, ALIGN, DEVICE, WORKSPACE = range(7)
+FAKE = 0x7F0000000000          # an aligned address that is never dereferenced on the host
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(bt_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_declares_the_boundary():
+    names = header_functions()
+    for must in ("bt_pack_ternary", "bt_quantize_act", "bt_ternary_matmul", "bt_repack_ternary"):
+        assert must in names
+
+
+def test_library_exports_every_declared_symbol():
+    L = C.CDLL(bt.LIB_PATH)
+    missing = [n for n in header_functions() if not hasattr(L, n)]
+    assert not missing, missing
+    assert set(header_functions()) == set(_lib.SIGNATURES)
+
+
+def test_struct_layouts_match_header_sizes():
+    # two int64 + pointer fields; no padding surprises between C and ctypes
+    assert C.sizeof(BtQuantDesc) == 6 * 8
+    assert C.sizeof(BtMatmulDesc) == 3 * 8 + 4 * 8 + 8 + 2 * 8
+
+
+def test_status_strings():
+    L = bt.lib()
+    for s in range(7):
+        assert L.bt_status_string(s)
+    assert b"unknown" in L.bt_status_string(99)
+
+
+@pytest.mark.parametrize("n,k", [(1, 128), (3, 256), (40, 384), (17, 1536), (2, 8960)])
+def test_pack_matches_oracle_bytes(n, k):
+    w = np.random.default_rng(n * 1000 + k).integers(-1, 2, (n, k), dtype=np.int8)
+    p = bt.pack_ternary(w)
+    assert p.shape == (n, k // 4)
+    assert np.array_equal(p, oracle.pack_ref(w))
+    assert np.array_equal(bt.unpack_ternary(p, k), w)
+    assert bt.packed_bytes(n, k) == oracle.packed_bytes(n, k) == p.nbytes
+
+
+def test_pack_skewed_distributions():
+    from synth import ternary_weights
+    rng = np.random.default_rng(3)
+    for p in [(0.3, 0.4, 0.3), (0.2, 0.6, 0.2), (1.0, 0.0, 0.0), (0.0, 0.0, 1.0)]:
+        w = ternary_weights(rng, 32, 512, p)
+        assert np.array_equal(bt.pack_ternary(w), oracle.pack_ref(w))
+
+
+def test_pack_rejects_and_leaves_output_untouched():
+    L = bt.lib()
+    w = np.zeros((2, 128), np.int8)
+    w[1, 77] = 2
+    out = np.full((2, 32), 0xEE, np.uint8)
+    assert L.bt_pack_ternary(w.ctypes.data, 2, 128, out.ctypes.data) == VALUE
+    assert (out == 0xEE).all()
+    assert L.bt_pack_ternary(None, 2, 128, out.ctypes.data) == NULL
+    assert L.bt_pack_ternary(w.ctypes.data, 2, 100, out.ctypes.data) == SHAPE
+    assert L.bt_pack_ternary(w.ctypes.data, 0, 128, out.ctypes.data) == SHAPE
+    with pytest.raises(bt.BtError):
+        bt.pack_ternary(w)
+
+
+def test_unpack_rejects_code_three():
+    p = np.full((1, 32), 0x55, np.uint8)
+    p[0, 9] = 0xD5           # top pair = 0b11
+    with pytest.raises(bt.BtError) as e:
+        bt.unpack_ternary(p, 128)
+    assert e.value.status == VALUE
+
+
+def test_sizes():
+    assert bt.packed_bytes(1536, 1536) == 589_824
+    assert bt.packed_bytes(10, 100) == 0 and bt.repacked_bytes(0, 128) == 0
+    assert bt.repacked_bytes(40, 384) == 48 * 384 // 4
+    # the decode step's packed weights: 28 layers of the four projections
+    total = 28 * sum(bt.packed_bytes(n, k) for k, n in
+                     [(1536, 2048), (1536, 1536), (1536, 17920), (8960, 1536)])
+    assert total == 327_548_928
+    assert bt.matmul_workspace_bytes(17, 1536, 1536) == 0    # GEMM path needs none
+    assert bt.matmul_workspace_bytes(1, 1536, 1536) > 0       # split K on a small matrix
+
+
+def test_device_entry_points_validate_before_launch():
+    L = bt.lib()
+    f = FAKE
+    # repack
+    assert L.bt_repack_ternary(None, 16, 128, f, None) == NULL
+    assert L.bt_repack_ternary(f, 16, 100, f, None) == SHAPE
+    assert L.bt_repack_ternary(f + 4, 16, 128, f, None) == ALIGN
+    # quantize
+    assert L.bt_quantize_act(None, 1, 128, f, f, f, None) == NULL
+    assert L.bt_quantize_act(f, 0, 128, f, f, f, None) == SHAPE
+    assert L.bt_quantize_act(f, 1, 0, f, f, f, None) == SHAPE
+    assert L.bt_quantize_act(f, 1, 128, f + 1, f, f, None) == ALIGN
+    # matmul
+    args = lambda **kw: [kw.get("M", 1), kw.get("N", 16), kw.get("K", 128), kw.get("xq", f),
+                         kw.get("xs", f), kw.get("xsum", f), kw.get("w", f),
+                         kw.get("scale", 0.5), kw.get("y", f), kw.get("acc", None),
+                         kw.get("ws", None), kw.get("wsb", 0), None]
+    assert L.bt_ternary_matmul(*args(xsum=None)) == NULL
+    assert L.bt_ternary_matmul(*args(y=None)) == NULL
+    assert L.bt_ternary_matmul(*args(K=130)) == SHAPE
+    assert L.bt_ternary_matmul(*args(M=0)) == SHAPE
+    assert L.bt_ternary_matmul(*args(w=f + 8)) == ALIGN
+    assert L.bt_ternary_matmul(*args(acc=f + 2)) == ALIGN
+    assert L.bt_ternary_matmul(*args(scale=float("inf"))) == VALUE
+    assert L.bt_ternary_matmul(*args(scale=float("nan"))) == VALUE
+    # a split-K GEMV without (enough) workspace
+    need = bt.matmul_workspace_bytes(1, 1536, 1536)
+    assert L.bt_ternary_matmul(*args(N=1536, K=1536)) == WORKSPACE
+    assert L.bt_ternary_matmul(*args(N=1536, K=1536, ws=f, wsb=need - 1)) == WORKSPACE
+    assert L.bt_ternary_matmul(*args(N=1536, K=1536, ws=f + 4, wsb=need)) == ALIGN
+
+
+def test_plan_building_on_host():
+    L = bt.lib()
+    f = FAKE
+    q = (BtQuantDesc * 2)(BtQuantDesc(f, f, f, f, 3, 1536), BtQuantDesc(f, f, f, f, 1, 8960))
+    nb = L.bt_quant_plan_bytes(2)
+    host = np.zeros(nb, np.uint8)
+    assert L.bt_quant_plan_build(q, 2, host.ctypes.data, nb) == OK
+    hdr = host[:16].view(np.int64)
+    assert hdr[1] == 4                                  # total rows = workgroups
+    assert L.bt_quant_plan_build(q, 2, host.ctypes.data, nb - 1) == WORKSPACE
+    q[1].xsum = None
+    assert L.bt_quant_plan_build(q, 2, host.ctypes.data, nb) == NULL
+
+    m = (BtMatmulDesc * 2)(BtMatmulDesc(1, 2048, 1536, f, f, f, f, 0.02, f, None),
+                           BtMatmulDesc(4, 1536, 8960, f, f, f, f, 0.03, f, f))
+    nb = L.bt_matmul_plan_bytes(2)
+    host = np.zeros(nb, np.uint8)
+    assert L.bt_matmul_plan_build(m, 2, host.ctypes.data, nb) == OK
+    assert host[:16].view(np.int64)[1] == 2048 // 64 + 1536 // 64
+    m[0].M = 17
+    assert L.bt_matmul_plan_build(m, 2, host.ctypes.data, nb) == SHAPE
+    m[0].M = 1
+    m[1].w_scale = float("nan")
+    assert L.bt_matmul_plan_build(m, 2, host.ctypes.data, nb) == VALUE
+    # a launch with a plan of the wrong kind is refused on the host
+    assert L.bt_quantize_act_grouped(host.ctypes.data, f, None) == VALUE
+
+
+def test_binding_has_no_cpu_fallback():
+    import inspect
+    import ternary_weight_decoder_bt_amd.ops as ops
+    src = inspect.getsource(ops)
+    assert "oracle" not in src and "import synth" not in src
+    for host_math in ("np.dot", "np.matmul", "torch.matmul", "torch.mm", "np.round", "torch.round"):
+        assert host_math not in src
