@@ -84,11 +84,12 @@ bt_status bt_unpack_ternary(const uint8_t* packed, int64_t N, int64_t K, int8_t*
  * Permutes the canonical bytes into the kernels' fragment order: 16-row tiles,
  * each 16-element run of one row in one 32-bit word, 256-element steps stored
  * so that one 128-bit load per lane feeds four matrix-core steps. Rows are
- * padded to a multiple of 16 with zero weights. The layout is private to the
- * library; only bt_ternary_matmul* read it.
+ * padded to a multiple of 16 and K to a multiple of 256 (padding holds zero
+ * weights). The layout is private to the library; only bt_ternary_matmul*
+ * read it.
  * ------------------------------------------------------------------------- */
 
-/* ceil(N/16)*16 * K/4, or 0 for invalid N, K. */
+/* ceil(N/16)*16 * ceil(K/256)*256 / 4, or 0 for invalid N, K. */
 size_t bt_repacked_bytes(int64_t N, int64_t K);
 
 /* packed_dev: device, bt_packed_bytes(N,K) canonical bytes.
@@ -175,10 +176,16 @@ bt_status bt_quantize_act_grouped(const void* plan_host, const void* plan_dev,
                                   hipStream_t stream);
 
 size_t bt_matmul_plan_bytes(int32_t count);
-bt_status bt_matmul_plan_build(const bt_matmul_desc* descs, int32_t count, void* plan_host,
-                               size_t plan_bytes);
-/* Grouped GEMV: every projection of the plan in one launch. A grouped plan never
- * splits K across workgroups, so it needs no workspace. */
+/* Workspace the grouped launch of these descriptors needs (0 if none): a
+ * projection whose M*K int8 activations do not fit one workgroup's LDS slice
+ * is split along K, and its partial sums meet in the workspace. */
+size_t bt_matmul_plan_workspace_bytes(const bt_matmul_desc* descs, int32_t count);
+/* workspace: device memory of at least bt_matmul_plan_workspace_bytes bytes
+ * (may be NULL when that is 0), zero-filled before its first use and left
+ * zero-filled by every completed launch; it belongs to the plan. */
+bt_status bt_matmul_plan_build(const bt_matmul_desc* descs, int32_t count, void* workspace,
+                               size_t workspace_bytes, void* plan_host, size_t plan_bytes);
+/* Every GEMV of the plan in one launch. */
 bt_status bt_ternary_matmul_grouped(const void* plan_host, const void* plan_dev,
                                     hipStream_t stream);
 

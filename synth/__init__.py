@@ -17,5 +17,7 @@ from .generators import (  # noqa: F401
     ternary_weights,
     projection_rng,
     small_problem,
+    device_student_t3,
+    CFG_LONG,
     REMAINDER_MS,
 )

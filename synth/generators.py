@@ -121,6 +121,26 @@ def long_prefill_problem(layer: int, proj: int, m: int = 4096, *, with_weights: 
     return out
 
 
+def device_student_t3(m: int, k: int, cfg: int, layer: int, proj: int, device):
+    """x ~ Student-t with 3 degrees of freedom, drawn on the GPU with torch.
+
+    t = z / sqrt(chi2_3 / 3) with chi2_3 the sum of three squared standard
+    normals. Used where drawing gigabytes of activations on the host would
+    dominate a benchmark's set-up time; the same seed always gives the same
+    tensor on the same device and torch version.
+    """
+    import torch
+    seed = int(np.random.SeedSequence([cfg, layer, proj, STREAM_X]).generate_state(1, np.uint64)[0]
+               & np.uint64(2 ** 63 - 1))
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    z = torch.randn((m, k), generator=g, device=device, dtype=torch.float32)
+    chi = torch.zeros((m, k), device=device, dtype=torch.float32)
+    for _ in range(3):
+        chi += torch.randn((m, k), generator=g, device=device, dtype=torch.float32).square()
+    return z / torch.sqrt(chi / 3)
+
+
 def small_problem(seed: int, m: int, n: int, k: int, dist: str = "normal",
                   p=None) -> dict:
     """Small seeded case for parity at sizes the oracle finishes in seconds."""

@@ -33,7 +33,8 @@ SIGNATURES = {
     "bt_quant_plan_build": (C.c_int, [_p, _i32, _p, _sz]),
     "bt_quantize_act_grouped": (C.c_int, [_p, _p, _p]),
     "bt_matmul_plan_bytes": (_sz, [_i32]),
-    "bt_matmul_plan_build": (C.c_int, [_p, _i32, _p, _sz]),
+    "bt_matmul_plan_workspace_bytes": (_sz, [_p, _i32]),
+    "bt_matmul_plan_build": (C.c_int, [_p, _i32, _p, _sz, _p, _sz]),
     "bt_ternary_matmul_grouped": (C.c_int, [_p, _p, _p]),
 }
 

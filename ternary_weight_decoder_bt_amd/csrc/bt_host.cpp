@@ -4,6 +4,8 @@
 
 #include <string.h>
 
+#include <algorithm>
+#include <cmath>
 #include <limits>
 
 #include "bt_internal.h"
@@ -28,7 +30,7 @@ static bool valid_nk(int64_t N, int64_t K) {
     // every byte count and int32 index the kernels form must fit
     if (N > (int64_t(1) << 30) || K > (int64_t(1) << 30)) return false;
     const int64_t padded = ceil_div(N, bt::kTileN) * bt::kTileN;
-    return padded <= std::numeric_limits<int64_t>::max() / K;
+    return padded <= std::numeric_limits<int64_t>::max() / (K + bt::kSuperK);
 }
 
 extern "C" size_t bt_packed_bytes(int64_t N, int64_t K) {
@@ -36,7 +38,9 @@ extern "C" size_t bt_packed_bytes(int64_t N, int64_t K) {
 }
 
 extern "C" size_t bt_repacked_bytes(int64_t N, int64_t K) {
-    return valid_nk(N, K) ? size_t(ceil_div(N, bt::kTileN) * bt::kTileN) * size_t(K) / 4 : 0;
+    if (!valid_nk(N, K)) return 0;
+    return size_t(ceil_div(N, bt::kTileN) * bt::kTileN) *
+           size_t(ceil_div(K, bt::kSuperK) * bt::kSuperK) / 4;
 }
 
 // Canonical layout (blog post "Paper 說支援 ARM，我大概是第一個真的去編譯的人",
@@ -89,40 +93,48 @@ extern "C" bt_status bt_unpack_ternary(const uint8_t* packed, int64_t N, int64_t
 
 namespace bt {
 
-// Split-K policy of the single-matrix GEMV. A small matrix (e.g. 1536 rows)
-// has too few 16-row tiles to keep 256 compute units streaming, so K is cut
-// into chunks of at least two 256-wide steps until about 1024 workgroups exist.
-void gemv_shape(int64_t M, int64_t N, int64_t K, GemvDesc* d) {
+// Work split of a GEMV. Each wave streams tiles_per_wave 16-row tiles over one
+// K chunk; a workgroup (4 waves) first stages its chunk of the M activation
+// rows (and a zero row) in LDS, so a chunk is at most
+// kGemvLdsBytes / (256 (M + 1)) steps. A single
+// call on a small matrix (e.g. 1536 rows) has too few tiles to keep 256
+// compute units streaming, so it also cuts K until about kTargetBlocks
+// workgroups exist (chunks of at least two steps). A grouped launch has
+// parallelism across problems and splits K only for the LDS slice.
+void gemv_shape(int64_t M, int64_t N, int64_t K, bool grouped, GemvDesc* d) {
     memset(d, 0, sizeof(*d));
     d->M = int32_t(M);
     d->N = int32_t(N);
     d->K = int32_t(K);
     d->tiles = int32_t(ceil_div(N, kTileN));
-    d->full_steps = int32_t(K / kSuperK);
-    d->half_step = int32_t((K % kSuperK) != 0);
-    const int64_t steps = d->full_steps + d->half_step;
-    const int64_t wg_per_chunk = ceil_div(d->tiles, kGemvWaves);
-    constexpr int64_t kTargetBlocks = 1024;
-    constexpr int64_t kMinStepsPerChunk = 2;
-    int64_t chunks = 1;
-    if (wg_per_chunk < kTargetBlocks) {
-        chunks = ceil_div(kTargetBlocks, wg_per_chunk);
-        const int64_t max_chunks = ceil_div(steps, kMinStepsPerChunk);
-        if (chunks > max_chunks) chunks = max_chunks;
-        if (chunks < 1) chunks = 1;
+    d->steps = int32_t(ceil_div(K, kSuperK));
+    d->tiles_per_wave = grouped ? kGemvGroupedTilesPerWave : 1;
+    d->groups = ceil_div(d->tiles, int64_t(kGemvWaves) * d->tiles_per_wave);
+    // M activation rows plus one zero row per chunk
+    const int64_t lds_steps = std::max<int64_t>(1, kGemvLdsBytes / ((M + 1) * kSuperK));
+    int64_t chunks = ceil_div(d->steps, lds_steps);
+    if (!grouped) {
+        constexpr int64_t kTargetBlocks = 1024;
+        constexpr int64_t kMinStepsPerChunk = 2;
+        const int64_t want = std::min(ceil_div(kTargetBlocks, d->groups),
+                                      ceil_div(d->steps, kMinStepsPerChunk));
+        chunks = std::max(chunks, want);
     }
-    int64_t spc = ceil_div(steps, chunks);
-    chunks = ceil_div(steps, spc);
+    const int64_t spc = ceil_div(d->steps, chunks);
+    chunks = ceil_div(d->steps, spc);
     d->chunks = int32_t(chunks);
     d->steps_per_chunk = int32_t(spc);
-    d->blocks = wg_per_chunk * chunks;
+    d->lds_row = int32_t(spc * kSuperK + 16);
+    d->blocks = d->groups * chunks;
+}
+
+size_t gemv_partial_bytes(const GemvDesc& d) {
+    return (size_t(d.M) * size_t(d.tiles) * kTileN * sizeof(int32_t) + 255) & ~size_t(255);
 }
 
 size_t gemv_workspace_bytes(const GemvDesc& d) {
     if (d.chunks <= 1) return 0;
-    const size_t partial = size_t(d.M) * size_t(d.tiles) * kTileN * sizeof(int32_t);
-    const size_t partial_aligned = (partial + 255) & ~size_t(255);
-    return partial_aligned + ((size_t(d.tiles) * sizeof(uint32_t) + 255) & ~size_t(255));
+    return gemv_partial_bytes(d) + ((size_t(d.tiles) * sizeof(uint32_t) + 255) & ~size_t(255));
 }
 
 }  // namespace bt
@@ -131,7 +143,7 @@ extern "C" size_t bt_matmul_workspace_bytes(int64_t M, int64_t N, int64_t K) {
     if (M < 1 || !valid_nk(N, K)) return 0;
     if (M > BT_GEMV_MAX_M) return 0;   // the GEMM path splits nothing
     bt::GemvDesc d;
-    bt::gemv_shape(M, N, K, &d);
+    bt::gemv_shape(M, N, K, false, &d);
     return bt::gemv_workspace_bytes(d);
 }
 
@@ -176,31 +188,52 @@ extern "C" size_t bt_matmul_plan_bytes(int32_t count) {
     return sizeof(bt::PlanHeader) + size_t(count) * sizeof(bt::GemvDesc);
 }
 
+static bt_status check_matmul_desc(const bt_matmul_desc& m) {
+    if (!m.xq || !m.xscale || !m.xsum || !m.wdev || !m.y) return BT_ERR_NULL;
+    if (m.M < 1 || m.M > BT_GEMV_MAX_M || !valid_nk(m.N, m.K)) return BT_ERR_SHAPE;
+    if (!bt::aligned16(m.xq) || !bt::aligned16(m.xscale) || !bt::aligned16(m.xsum) ||
+        !bt::aligned16(m.wdev) || !bt::aligned16(m.y) || (m.acc && !bt::aligned16(m.acc)))
+        return BT_ERR_ALIGN;
+    if (!std::isfinite(m.w_scale)) return BT_ERR_VALUE;
+    return BT_OK;
+}
+
+extern "C" size_t bt_matmul_plan_workspace_bytes(const bt_matmul_desc* descs, int32_t count) {
+    if (!descs || count < 1) return 0;
+    size_t total = 0;
+    for (int32_t i = 0; i < count; ++i) {
+        if (descs[i].M < 1 || descs[i].M > BT_GEMV_MAX_M || !valid_nk(descs[i].N, descs[i].K))
+            return 0;
+        bt::GemvDesc d;
+        bt::gemv_shape(descs[i].M, descs[i].N, descs[i].K, true, &d);
+        total += bt::gemv_workspace_bytes(d);
+    }
+    return total;
+}
+
 extern "C" bt_status bt_matmul_plan_build(const bt_matmul_desc* descs, int32_t count,
+                                          void* workspace, size_t workspace_bytes,
                                           void* plan_host, size_t plan_bytes) {
     if (!descs || !plan_host) return BT_ERR_NULL;
     if (count < 1) return BT_ERR_SHAPE;
     if (plan_bytes < bt_matmul_plan_bytes(count)) return BT_ERR_WORKSPACE;
     for (int32_t i = 0; i < count; ++i) {
-        const bt_matmul_desc& m = descs[i];
-        if (!m.xq || !m.xscale || !m.xsum || !m.wdev || !m.y) return BT_ERR_NULL;
-        if (m.M < 1 || m.M > BT_GEMV_MAX_M || !valid_nk(m.N, m.K)) return BT_ERR_SHAPE;
-        if (!bt::aligned16(m.xq) || !bt::aligned16(m.xscale) || !bt::aligned16(m.xsum) ||
-            !bt::aligned16(m.wdev) || !bt::aligned16(m.y) || (m.acc && !bt::aligned16(m.acc)))
-            return BT_ERR_ALIGN;
-        if (!(m.w_scale == m.w_scale) || m.w_scale - m.w_scale != 0.0f) return BT_ERR_VALUE;
+        const bt_status st = check_matmul_desc(descs[i]);
+        if (st != BT_OK) return st;
+    }
+    const size_t need = bt_matmul_plan_workspace_bytes(descs, count);
+    if (need) {
+        if (!workspace || workspace_bytes < need) return BT_ERR_WORKSPACE;
+        if (!bt::aligned16(workspace)) return BT_ERR_ALIGN;
     }
     auto* hdr = static_cast<bt::PlanHeader*>(plan_host);
     auto* out = reinterpret_cast<bt::GemvDesc*>(hdr + 1);
     int64_t blocks = 0;
+    char* ws = static_cast<char*>(workspace);
     for (int32_t i = 0; i < count; ++i) {
         const bt_matmul_desc& m = descs[i];
         bt::GemvDesc d;
-        bt::gemv_shape(m.M, m.N, m.K, &d);
-        // a grouped launch has parallelism across problems: never split K
-        d.chunks = 1;
-        d.steps_per_chunk = d.full_steps + d.half_step;
-        d.blocks = ceil_div(d.tiles, bt::kGemvWaves);
+        bt::gemv_shape(m.M, m.N, m.K, true, &d);
         d.xq = m.xq;
         d.xscale = m.xscale;
         d.xsum = m.xsum;
@@ -208,6 +241,11 @@ extern "C" bt_status bt_matmul_plan_build(const bt_matmul_desc* descs, int32_t c
         d.y = m.y;
         d.acc = m.acc;
         d.w_scale = m.w_scale;
+        if (d.chunks > 1) {
+            d.ws = reinterpret_cast<int32_t*>(ws);
+            d.cnt = reinterpret_cast<uint32_t*>(ws + bt::gemv_partial_bytes(d));
+            ws += bt::gemv_workspace_bytes(d);
+        }
         d.block_begin = blocks;
         blocks += d.blocks;
         out[i] = d;

@@ -20,6 +20,12 @@ constexpr uint32_t kPlanMagicGemv = 0x42544d47u;    // "GMTB"
 
 inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
+// GEMV tuning: weight steps (1 KB per wave) loaded per batch, and the LDS
+// slice that holds one workgroup's int8 activations (M rows x its K range).
+constexpr int kGemvBatch = 6;
+constexpr int kGemvLdsBytes = 40960;
+constexpr int kGemvGroupedTilesPerWave = 2;
+
 // One GEMV problem as the kernel sees it. The single-matrix call passes it by
 // value; a grouped plan stores an array of them in device memory.
 struct GemvDesc {
@@ -34,12 +40,15 @@ struct GemvDesc {
     float w_scale;
     int32_t M, N, K;
     int32_t tiles;          // ceil(N / 16)
+    int32_t steps;          // ceil(K / 256): 1 KB weight loads per tile
     int32_t chunks;         // K-splits per tile
-    int32_t steps_per_chunk;  // 256-wide K steps per chunk (the last chunk may be shorter)
-    int32_t full_steps;     // K / 256
-    int32_t half_step;      // 1 if K % 256 == 128 (one trailing 128-wide step)
+    int32_t steps_per_chunk;
+    int32_t tiles_per_wave;
+    int32_t lds_row;        // bytes per activation row in LDS (steps_per_chunk*256 + 16)
+    int32_t pad_;
+    int64_t groups;         // workgroups per chunk = ceil(tiles / (4 * tiles_per_wave))
     int64_t block_begin;    // first workgroup of this problem in a grouped launch
-    int64_t blocks;         // workgroups of this problem
+    int64_t blocks;         // workgroups of this problem = groups * chunks
 };
 
 struct QuantDesc {
@@ -57,9 +66,11 @@ struct PlanHeader {
     int64_t total_blocks;
 };
 
-// Split-K policy of a single GEMV call; also sizes its workspace.
-void gemv_shape(int64_t M, int64_t N, int64_t K, GemvDesc* d);
+// Work split of a GEMV (single call: split K for parallelism and for the LDS
+// slice; grouped: only for the LDS slice). Also sizes its workspace.
+void gemv_shape(int64_t M, int64_t N, int64_t K, bool grouped, GemvDesc* d);
 size_t gemv_workspace_bytes(const GemvDesc& d);
+size_t gemv_partial_bytes(const GemvDesc& d);
 
 inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 

@@ -14,13 +14,14 @@
 // AND per 4 weights, with no per-byte subtraction.
 //
 // Repacked weight layout (written by repack_kernel, read by both matmuls):
-//   tile t = 16 consecutive rows, 4*K bytes, stored contiguously;
+//   K is padded to Kp = ceil(K/256)*256 and N to a multiple of 16 (padding
+//   holds zero weights; the activation side is zero there too);
+//   tile t = 16 consecutive rows, 4*Kp bytes, stored contiguously;
 //   inside a tile, 256-wide K steps S of 1 KB: lane l (row 16t + l%16,
 //   K quarter l/16) owns bytes [16l, 16l+16) = four 32-bit words, word jj
 //   holding K = 256S + 64jj + 16(l/16) + e, e = 0..15, with element e in
-//   byte e%4 at bits 2*(e/4). A trailing 128-wide step (K % 256 == 128) is
-//   512 B with 8 bytes per lane. So one 128-bit load per lane yields the
-//   B fragments of four MFMA steps, and unpacking word jj is
+//   byte e%4 at bits 2*(e/4). So one 128-bit load per lane yields the B
+//   fragments of four MFMA steps, and unpacking word jj is
 //   (word >> 2s) & 0x03030303 for s = 0..3.
 
 #include <hip/hip_runtime.h>
@@ -58,6 +59,38 @@ __device__ __forceinline__ v4i mfma16x16x64(v4i a, v4i b, v4i c) {
     return __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, c, 0, 0, 0);
 }
 
+// Pointers held in descriptors are generic; these casts make the compiler
+// emit global_* / ds_* instructions instead of flat_* ones (flat accesses
+// also count against the LDS wait counter and serialize the two queues).
+#define BT_GLOBAL __attribute__((address_space(1)))
+#define BT_LDS __attribute__((address_space(3)))
+
+template <typename T>
+__device__ __forceinline__ T gld(const void* p) {
+    return *(const BT_GLOBAL T*)p;
+}
+
+// Streaming load for data read exactly once (the weights).
+template <typename T>
+__device__ __forceinline__ T gld_stream(const void* p) {
+    return __builtin_nontemporal_load((const BT_GLOBAL T*)p);
+}
+
+template <typename T>
+__device__ __forceinline__ void gst(void* p, T v) {
+    *(BT_GLOBAL T*)p = v;
+}
+
+template <typename T>
+__device__ __forceinline__ T lds_ld(const void* p) {
+    return *(const BT_LDS T*)p;
+}
+
+template <typename T>
+__device__ __forceinline__ void lds_st(void* p, T v) {
+    *(BT_LDS T*)p = v;
+}
+
 // ------------------------------------------------------------------ repack
 
 // One thread per output word. Word (tile t, step S, lane l, word jj) gathers
@@ -65,27 +98,19 @@ __device__ __forceinline__ v4i mfma16x16x64(v4i a, v4i b, v4i c) {
 // In the canonical layout those 16 elements share one bit pair (k0 % 128) / 32
 // of 16 consecutive bytes starting at byte 32*(k0/128) + k0 % 32 of the row.
 __global__ __launch_bounds__(256) void repack_kernel(const uint8_t* __restrict__ packed, int32_t N,
-                                                     int32_t K, int64_t total_words,
+                                                     int32_t K, int32_t Kp, int64_t total_words,
                                                      uint32_t* __restrict__ out) {
-    const int32_t full = K / bt::kSuperK;
     for (int64_t gid = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; gid < total_words;
          gid += int64_t(gridDim.x) * blockDim.x) {
-        const int64_t t = gid / K;
-        const int32_t d = int32_t(gid - t * K);
+        const int64_t t = gid / Kp;                 // a tile holds Kp words
+        const int32_t d = int32_t(gid - t * Kp);
         const int32_t S = d >> 8;
-        const int32_t rem = d & 255;
-        int32_t lane, jj;
-        if (S < full) {
-            lane = rem >> 2;
-            jj = rem & 3;
-        } else {
-            lane = rem >> 1;
-            jj = rem & 1;
-        }
+        const int32_t lane = (d & 255) >> 2;
+        const int32_t jj = d & 3;
         const int64_t n = t * bt::kTileN + (lane & 15);
         const int32_t k0 = bt::kSuperK * S + bt::kStepK * jj + 16 * (lane >> 4);
-        uint32_t word = 0x55555555u;   // padding rows: code 1 = weight 0
-        if (n < N) {
+        uint32_t word = 0x55555555u;   // padding: code 1 = weight 0
+        if (n < N && k0 < K) {
             const uint8_t* row = packed + n * (K / 4);
             const uint4 c = *reinterpret_cast<const uint4*>(row + 32 * (k0 >> 7) + (k0 & 31));
             const int sh = 2 * ((k0 & 127) >> 5);
@@ -238,72 +263,54 @@ __global__ __launch_bounds__(bt::kQuantThreads) void quantize_grouped_kernel(
 }
 
 // -------------------------------------------------------------------- GEMV
+//
+// A workgroup is 4 waves. It first copies its K chunk of the M activation rows
+// into LDS (zero beyond K), then each wave streams tiles_per_wave 16-row weight
+// tiles through the matrix cores. A wave's work is a sequence of items (tile,
+// batch of up to kB 1 KB steps); the loads of item i+1 are issued before item
+// i is consumed, so every wave keeps up to 2*kB KB of weights in flight.
+//
+// MFMA operands per 64-wide K step: lane l holds A = q[l%16][16(l/16)..+15]
+// (zero for tokens >= M) from LDS and B = the unpacked codes of tile row l%16
+// at the same K; the C fragment holds tokens 4(l/16)+i, output row l%16.
 
-constexpr int kGemvInFlight = 8;   // 1 KB weight loads in flight per wave
+constexpr int kB = bt::kGemvBatch;
 
-// One wave computes one 16-row tile over one K chunk. The A fragment of lane l
-// is q[l%16][64j + 16(l/16) .. +15] (zero for tokens >= M); the B fragment is
-// the unpacked word of that lane. The C fragment holds tokens 4(l/16)+i,
-// output row l%16 of the tile.
-__device__ __forceinline__ void gemv_wave(const GemvDesc& d, int64_t local_block) {
-    const int wave = threadIdx.x >> 6;
-    const int lane = threadIdx.x & 63;
-    const int64_t wg_per_chunk = (d.tiles + bt::kGemvWaves - 1) / bt::kGemvWaves;
-    const int chunk = int(local_block / wg_per_chunk);
-    const int tile = int(local_block - int64_t(chunk) * wg_per_chunk) * bt::kGemvWaves + wave;
-    if (tile >= d.tiles) return;
-    const int steps = d.full_steps + d.half_step;
-    const int s0 = chunk * d.steps_per_chunk;
-    const int s1 = min(s0 + d.steps_per_chunk, steps);
-    const int s1_full = min(s1, d.full_steps);
+struct GemvBatch {
+    v4u w[kB];
+};
 
-    const uint8_t* wt = d.w + int64_t(tile) * 4 * d.K;
-    const int am = lane & 15;
+// Loads steps sb .. sb+kB-1 of a tile, clamping the step to `last` (a repeated
+// step is a cache hit and is never consumed): no branches, so the compiler
+// can count the loads in flight exactly.
+__device__ __forceinline__ void gemv_issue(GemvBatch& b, const uint8_t* wt, int sb, int last,
+                                           int lane) {
+#pragma unroll
+    for (int u = 0; u < kB; ++u) {
+        const int st = min(sb + u, last);
+        b.w[u] = gld_stream<v4u>(wt + int64_t(st) * 1024 + lane * 16);
+    }
+}
+
+__device__ __forceinline__ v4i gemv_consume(const GemvBatch& b, int n, const int8_t* a, v4i c) {
+#pragma unroll
+    for (int u = 0; u < kB; ++u) {
+        if (u < n) {
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj)
+                c = mfma16x16x64(lds_ld<v4i>(a + u * 256 + 64 * jj), unpack16(b.w[u][jj]), c);
+        }
+    }
+    return c;
+}
+
+// Epilogue of one tile. With K split into chunks, partial sums meet in the
+// workspace (int32 addition is exact in any order) and the last chunk to
+// arrive reads the total, clears the workspace and finishes the tile.
+__device__ __forceinline__ void gemv_finish(const GemvDesc& d, int64_t tile, v4i c, int lane) {
     const int kq = lane >> 4;
-    const bool arow = am < d.M;
-    const int8_t* xrow = d.xq + int64_t(am) * d.K + 16 * kq;
-    v4i c = {0, 0, 0, 0};
-
-    int S = s0;
-    for (; S < s1_full; S += kGemvInFlight) {
-        v4u w[kGemvInFlight];
-#pragma unroll
-        for (int u = 0; u < kGemvInFlight; ++u)
-            if (S + u < s1_full)
-                w[u] = __builtin_nontemporal_load(
-                    reinterpret_cast<const v4u*>(wt + int64_t(S + u) * 1024 + lane * 16));
-#pragma unroll
-        for (int u = 0; u < kGemvInFlight; ++u) {
-            if (S + u < s1_full) {
-                const uint32_t ww[4] = {w[u][0], w[u][1], w[u][2], w[u][3]};
-#pragma unroll
-                for (int jj = 0; jj < 4; ++jj) {
-                    v4i a = {0, 0, 0, 0};
-                    if (arow)
-                        a = *reinterpret_cast<const v4i*>(xrow + int64_t(S + u) * 256 + 64 * jj);
-                    c = mfma16x16x64(a, unpack16(ww[jj]), c);
-                }
-            }
-        }
-    }
-    if (s1 > d.full_steps) {   // this chunk ends with the trailing 128-wide step
-        S = d.full_steps;
-        const v2u w = __builtin_nontemporal_load(
-            reinterpret_cast<const v2u*>(wt + int64_t(S) * 1024 + lane * 8));
-        const uint32_t ww[2] = {w[0], w[1]};
-#pragma unroll
-        for (int jj = 0; jj < 2; ++jj) {
-            v4i a = {0, 0, 0, 0};
-            if (arow) a = *reinterpret_cast<const v4i*>(xrow + int64_t(S) * 256 + 64 * jj);
-            c = mfma16x16x64(a, unpack16(ww[jj]), c);
-        }
-    }
-
-    const int n_local = lane & 15;
-    const int n = tile * bt::kTileN + n_local;
+    const int64_t n = tile * bt::kTileN + (lane & 15);
     if (d.chunks > 1) {
-        // Split K: add this chunk's partial sums (int32 addition is exact in
-        // any order), and let the last chunk to arrive finish the tile.
         const int64_t ldw = int64_t(d.tiles) * bt::kTileN;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -328,21 +335,90 @@ __device__ __forceinline__ void gemv_wave(const GemvDesc& d, int64_t local_block
         for (int i = 0; i < 4; ++i) {
             const int mm = 4 * kq + i;
             if (mm < d.M) {
-                const int32_t acc = c[i] - d.xsum[mm];
-                const float rs = d.xscale[mm] * d.w_scale;
-                d.y[int64_t(mm) * d.N + n] = float(acc) * rs;
-                if (d.acc) d.acc[int64_t(mm) * d.N + n] = acc;
+                const int32_t acc = c[i] - gld<int32_t>(d.xsum + mm);
+                const float rs = gld<float>(d.xscale + mm) * d.w_scale;
+                gst<float>(d.y + int64_t(mm) * d.N + n, float(acc) * rs);
+                if (d.acc) gst<int32_t>(d.acc + int64_t(mm) * d.N + n, acc);
             }
         }
     }
 }
 
+__device__ __forceinline__ void gemv_block(const GemvDesc& d, int64_t local_block, int8_t* lds) {
+    const int tid = threadIdx.x;
+    const int wave = tid >> 6;
+    const int lane = tid & 63;
+    const int chunk = int(local_block / d.groups);
+    const int64_t g = local_block - int64_t(chunk) * d.groups;
+    const int s0 = chunk * d.steps_per_chunk;
+    const int s1 = min(s0 + d.steps_per_chunk, d.steps);
+    const int nsteps = s1 - s0;
+
+    // Stage q[0:M][256*s0 : 256*s1] in LDS rows 0..M-1 (zero past K) and a
+    // zero row M, which the lanes of tokens >= M read instead.
+    const int64_t kbeg = int64_t(s0) * bt::kSuperK;
+    const int pieces = nsteps * (bt::kSuperK / 16);
+    for (int i = tid; i < (d.M + 1) * pieces; i += 64 * bt::kGemvWaves) {
+        const int m = i / pieces;
+        const int col = (i - m * pieces) * 16;
+        v4i v = {0, 0, 0, 0};
+        if (m < d.M && kbeg + col < d.K) v = gld<v4i>(d.xq + int64_t(m) * d.K + kbeg + col);
+        lds_st<v4i>(lds + m * d.lds_row + col, v);
+    }
+    __syncthreads();
+
+    const int am = min(lane & 15, d.M);
+    const int8_t* abase = lds + am * d.lds_row + 16 * (lane >> 4);
+    const int nb = (nsteps + kB - 1) / kB;
+    const int total = d.tiles_per_wave * nb;
+    const int64_t tile0 = g * (int64_t(bt::kGemvWaves) * d.tiles_per_wave) + wave;
+    const int64_t tile_bytes = int64_t(d.steps) * 1024;
+
+    // Items are (tile, batch of kB steps). Two items are loaded back to back
+    // (2*kB KB in flight per wave), then consumed. Loads are unconditional:
+    // a tile past N or a step past the chunk is clamped to a valid address and
+    // its data is never consumed.
+    v4i cur = {0, 0, 0, 0};
+    auto issue = [&](GemvBatch& b, int idx) {
+        const int r = idx / nb;
+        const int bb = idx - r * nb;
+        const int64_t t = min(tile0 + int64_t(bt::kGemvWaves) * r, int64_t(d.tiles) - 1);
+        gemv_issue(b, d.w + t * tile_bytes, s0 + bb * kB, s1 - 1, lane);
+    };
+    auto consume = [&](const GemvBatch& b, int idx) {
+        const int r = idx / nb;
+        const int bb = idx - r * nb;
+        const int64_t t = tile0 + int64_t(bt::kGemvWaves) * r;
+        if (t >= d.tiles) return;
+        cur = gemv_consume(b, min(kB, nsteps - bb * kB), abase + bb * kB * 256, cur);
+        if (bb == nb - 1) {
+            gemv_finish(d, t, cur, lane);
+            cur = v4i{0, 0, 0, 0};
+        }
+    };
+
+    // The scheduling barriers keep the unpacking of batch 1 below the use of
+    // batch 0, so the wait before batch 0 leaves batch 1's loads in flight.
+    GemvBatch b0, b1;
+    for (int idx = 0; idx < total; idx += 2) {
+        issue(b0, idx);
+        __builtin_amdgcn_sched_barrier(0);
+        issue(b1, min(idx + 1, total - 1));
+        __builtin_amdgcn_sched_barrier(0);
+        consume(b0, idx);
+        __builtin_amdgcn_sched_barrier(0);
+        if (idx + 1 < total) consume(b1, idx + 1);
+    }
+}
+
 __global__ __launch_bounds__(64 * bt::kGemvWaves) void gemv_kernel(GemvDesc d) {
-    gemv_wave(d, blockIdx.x);
+    extern __shared__ __attribute__((aligned(16))) int8_t gemv_lds[];
+    gemv_block(d, blockIdx.x, gemv_lds);
 }
 
 __global__ __launch_bounds__(64 * bt::kGemvWaves) void gemv_grouped_kernel(
     const GemvDesc* __restrict__ descs, int32_t count) {
+    extern __shared__ __attribute__((aligned(16))) int8_t gemv_lds[];
     const int64_t b = blockIdx.x;
     int lo = 0, hi = count - 1;
     while (lo < hi) {
@@ -350,8 +426,10 @@ __global__ __launch_bounds__(64 * bt::kGemvWaves) void gemv_grouped_kernel(
         if (descs[mid].block_begin <= b) lo = mid; else hi = mid - 1;
     }
     const GemvDesc d = descs[lo];
-    gemv_wave(d, b - d.block_begin);
+    gemv_block(d, b - d.block_begin, gemv_lds);
 }
+
+size_t gemv_lds_bytes(const GemvDesc& d) { return size_t(d.M + 1) * size_t(d.lds_row); }
 
 // -------------------------------------------------------------------- GEMM
 
@@ -367,13 +445,14 @@ struct GemmArgs {
     float* y;
     int32_t* acc;
     float w_scale;
-    int32_t M, N, K, tiles, full_steps, half_step;
+    int32_t M, N, K, tiles, steps;
 };
 
 // 128 x 128 output tile per workgroup, 4 waves as 2 x 2, each wave 64 x 64 =
-// 4 x 4 MFMA blocks. Per 256-wide K step the activation tile (128 x 256 int8)
-// is staged in LDS and each wave loads the packed words of its four 16-row
-// weight tiles straight from global memory (one 128-bit load per tile).
+// 4 x 4 MFMA blocks. Per 256-wide K step the activation tile (128 x 256 int8,
+// zero past M and K) is staged in LDS and each wave loads the packed words of
+// its four 16-row weight tiles straight from global memory (one 128-bit load
+// per tile), unpacking them in registers.
 __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g) {
     __shared__ __attribute__((aligned(16))) int8_t As[kBM * kALds];
     const int tid = threadIdx.x;
@@ -384,6 +463,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g) {
     const int64_t m0 = int64_t(blockIdx.y) * kBM;
     const int n0 = blockIdx.x * kBN;
     const int t0 = n0 / bt::kTileN + wn * 4;
+    const int64_t tile_bytes = int64_t(g.steps) * 1024;
 
     v4i acc[4][4];
 #pragma unroll
@@ -391,49 +471,33 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) acc[i][j] = v4i{0, 0, 0, 0};
 
-    const int steps = g.full_steps + g.half_step;
-    for (int S = 0; S < steps; ++S) {
-        const bool half = S >= g.full_steps;
-        uint4 wb[4];
+    for (int S = 0; S < g.steps; ++S) {
+        v4u wb[4];
 #pragma unroll
         for (int tn = 0; tn < 4; ++tn) {
-            const int t = t0 + tn;
-            wb[tn] = uint4{0, 0, 0, 0};
-            if (t < g.tiles) {
-                const uint8_t* base = g.w + int64_t(t) * 4 * g.K + int64_t(S) * 1024;
-                if (!half) {
-                    wb[tn] = *reinterpret_cast<const uint4*>(base + lane * 16);
-                } else {
-                    const uint2 h = *reinterpret_cast<const uint2*>(base + lane * 8);
-                    wb[tn].x = h.x;
-                    wb[tn].y = h.y;
-                }
-            }
+            const int t = min(t0 + tn, g.tiles - 1);   // past-N tiles are never stored
+            wb[tn] = gld<v4u>(g.w + int64_t(t) * tile_bytes + int64_t(S) * 1024 + lane * 16);
         }
-        const int kw = half ? 128 : 256;
-        const int cpr = kw / 16;   // 16-byte chunks per row
         __syncthreads();
+        constexpr int cpr = bt::kSuperK / 16;   // 16-byte chunks per row
         for (int ch = tid; ch < kBM * cpr; ch += 256) {
             const int r = ch / cpr;
             const int col = (ch - r * cpr) * 16;
             const int64_t gm = m0 + r;
-            int4 v = {0, 0, 0, 0};
-            if (gm < g.M)
-                v = *reinterpret_cast<const int4*>(g.xq + gm * g.K + int64_t(S) * 256 + col);
-            *reinterpret_cast<int4*>(As + r * kALds + col) = v;
+            const int64_t k = int64_t(S) * bt::kSuperK + col;
+            v4i v = {0, 0, 0, 0};
+            if (gm < g.M && k < g.K) v = gld<v4i>(g.xq + gm * g.K + k);
+            lds_st<v4i>(As + r * kALds + col, v);
         }
         __syncthreads();
-        const int nj = half ? 2 : 4;
-        for (int jj = 0; jj < nj; ++jj) {
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
             v4i bf[4];
 #pragma unroll
-            for (int tn = 0; tn < 4; ++tn) {
-                const uint32_t word = jj == 0 ? wb[tn].x : jj == 1 ? wb[tn].y : jj == 2 ? wb[tn].z : wb[tn].w;
-                bf[tn] = unpack16(word);
-            }
+            for (int tn = 0; tn < 4; ++tn) bf[tn] = unpack16(wb[tn][jj]);
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const v4i af = *reinterpret_cast<const v4i*>(
+                const v4i af = lds_ld<v4i>(
                     As + (wm * 64 + 16 * i + (lane & 15)) * kALds + 64 * jj + 16 * (lane >> 4));
 #pragma unroll
                 for (int tn = 0; tn < 4; ++tn) acc[i][tn] = mfma16x16x64(af, bf[tn], acc[i][tn]);
@@ -447,15 +511,15 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g) {
         for (int r = 0; r < 4; ++r) {
             const int64_t mm = m0 + wm * 64 + 16 * i + 4 * (lane >> 4) + r;
             if (mm >= g.M) continue;
-            const int32_t qs = g.xsum[mm];
-            const float rs = g.xscale[mm] * g.w_scale;
+            const int32_t qs = gld<int32_t>(g.xsum + mm);
+            const float rs = gld<float>(g.xscale + mm) * g.w_scale;
 #pragma unroll
             for (int tn = 0; tn < 4; ++tn) {
                 const int n = n0 + wn * 64 + 16 * tn + (lane & 15);
                 if (n < g.N) {
                     const int32_t a = acc[i][tn][r] - qs;
-                    g.y[mm * g.N + n] = float(a) * rs;
-                    if (g.acc) g.acc[mm * g.N + n] = a;
+                    gst<float>(g.y + mm * g.N + n, float(a) * rs);
+                    if (g.acc) gst<int32_t>(g.acc + mm * g.N + n, a);
                 }
             }
         }
@@ -477,12 +541,12 @@ extern "C" bt_status bt_repack_ternary(const uint8_t* packed_dev, int64_t N, int
     if (!packed_dev || !wdev) return BT_ERR_NULL;
     if (!nk_ok(N, K)) return BT_ERR_SHAPE;
     if (!bt::aligned16(packed_dev) || !bt::aligned16(wdev)) return BT_ERR_ALIGN;
-    const int64_t tiles = bt::ceil_div(N, bt::kTileN);
-    const int64_t words = tiles * K;
+    const int64_t Kp = bt::ceil_div(K, bt::kSuperK) * bt::kSuperK;
+    const int64_t words = bt::ceil_div(N, bt::kTileN) * Kp;   // 16 rows * Kp/4 bytes / 4
     const int64_t blocks = std::min<int64_t>(bt::ceil_div(words, 256), int64_t(1) << 20);
     (void)hipGetLastError();
     hipLaunchKernelGGL(repack_kernel, dim3(unsigned(blocks)), dim3(256), 0, stream, packed_dev,
-                       int32_t(N), int32_t(K), words, static_cast<uint32_t*>(wdev));
+                       int32_t(N), int32_t(K), int32_t(Kp), words, static_cast<uint32_t*>(wdev));
     return launched();
 }
 
@@ -512,15 +576,14 @@ extern "C" bt_status bt_ternary_matmul(int64_t M, int64_t N, int64_t K, const in
     if (!isfinite(w_scale)) return BT_ERR_VALUE;
     if (M <= BT_GEMV_MAX_M) {
         GemvDesc d;
-        bt::gemv_shape(M, N, K, &d);
+        bt::gemv_shape(M, N, K, false, &d);
         const size_t need = bt::gemv_workspace_bytes(d);
         if (need) {
             if (!workspace || workspace_bytes < need) return BT_ERR_WORKSPACE;
             if (!bt::aligned16(workspace)) return BT_ERR_ALIGN;
-            const size_t partial =
-                (size_t(d.M) * size_t(d.tiles) * bt::kTileN * sizeof(int32_t) + 255) & ~size_t(255);
             d.ws = static_cast<int32_t*>(workspace);
-            d.cnt = reinterpret_cast<uint32_t*>(static_cast<char*>(workspace) + partial);
+            d.cnt = reinterpret_cast<uint32_t*>(static_cast<char*>(workspace) +
+                                                bt::gemv_partial_bytes(d));
         }
         d.xq = xq;
         d.xscale = xscale;
@@ -530,8 +593,8 @@ extern "C" bt_status bt_ternary_matmul(int64_t M, int64_t N, int64_t K, const in
         d.acc = acc;
         d.w_scale = w_scale;
         (void)hipGetLastError();
-        hipLaunchKernelGGL(gemv_kernel, dim3(unsigned(d.blocks)), dim3(64 * bt::kGemvWaves), 0,
-                           stream, d);
+        hipLaunchKernelGGL(gemv_kernel, dim3(unsigned(d.blocks)), dim3(64 * bt::kGemvWaves),
+                           gemv_lds_bytes(d), stream, d);
         return launched();
     }
     GemmArgs g;
@@ -546,8 +609,7 @@ extern "C" bt_status bt_ternary_matmul(int64_t M, int64_t N, int64_t K, const in
     g.N = int32_t(N);
     g.K = int32_t(K);
     g.tiles = int32_t(bt::ceil_div(N, bt::kTileN));
-    g.full_steps = int32_t(K / bt::kSuperK);
-    g.half_step = int32_t((K % bt::kSuperK) != 0);
+    g.steps = int32_t(bt::ceil_div(K, bt::kSuperK));
     const int64_t gy = bt::ceil_div(M, kBM);
     if (gy > 65535) return BT_ERR_SHAPE;
     (void)hipGetLastError();
@@ -576,10 +638,13 @@ extern "C" bt_status bt_ternary_matmul_grouped(const void* plan_host, const void
     const auto* hdr = static_cast<const bt::PlanHeader*>(plan_host);
     if (hdr->magic != bt::kPlanMagicGemv || hdr->count < 1) return BT_ERR_VALUE;
     if (!bt::aligned16(plan_dev)) return BT_ERR_ALIGN;
+    const auto* host_descs = reinterpret_cast<const GemvDesc*>(hdr + 1);
+    size_t lds = 0;
+    for (int32_t i = 0; i < hdr->count; ++i) lds = std::max(lds, gemv_lds_bytes(host_descs[i]));
     const auto* descs = reinterpret_cast<const GemvDesc*>(static_cast<const char*>(plan_dev) +
                                                           sizeof(bt::PlanHeader));
     (void)hipGetLastError();
     hipLaunchKernelGGL(gemv_grouped_kernel, dim3(unsigned(hdr->total_blocks)),
-                       dim3(64 * bt::kGemvWaves), 0, stream, descs, hdr->count);
+                       dim3(64 * bt::kGemvWaves), lds, stream, descs, hdr->count);
     return launched();
 }

@@ -209,11 +209,15 @@ class MatmulPlan(_Plan):
             descs[i] = BtMatmulDesc(m, it["n"], k, _ptr(it["xq"]), _ptr(it["xscale"]),
                                     _ptr(it["xsum"]), _ptr(it["wdev"]), float(it["w_scale"]),
                                     _ptr(it["y"]), _ptr(it.get("acc")))
+        torch = _torch()
+        dev = items[0]["xq"].device
+        ws_bytes = int(lib().bt_matmul_plan_workspace_bytes(descs, len(items)))
+        self.workspace = torch.zeros(ws_bytes, dtype=torch.uint8, device=dev) if ws_bytes else None
         nbytes = int(lib().bt_matmul_plan_bytes(len(items)))
         host = np.zeros(nbytes, np.uint8)
-        check(lib().bt_matmul_plan_build(descs, len(items), _np_ptr(host), nbytes),
-              "bt_matmul_plan_build")
-        super().__init__(host, items[0]["xq"].device)
+        check(lib().bt_matmul_plan_build(descs, len(items), _ptr(self.workspace), ws_bytes,
+                                         _np_ptr(host), nbytes), "bt_matmul_plan_build")
+        super().__init__(host, dev)
 
     def launch(self, stream=None):
         h, d = self._ptrs()

@@ -100,7 +100,8 @@ def test_unpack_rejects_code_three():
 def test_sizes():
     assert bt.packed_bytes(1536, 1536) == 589_824
     assert bt.packed_bytes(10, 100) == 0 and bt.repacked_bytes(0, 128) == 0
-    assert bt.repacked_bytes(40, 384) == 48 * 384 // 4
+    assert bt.repacked_bytes(40, 384) == 48 * 512 // 4     # rows to 16, K to 256
+    assert bt.repacked_bytes(1536, 8960) == 1536 * 8960 // 4
     # the decode step's packed weights: 28 layers of the four projections
     total = 28 * sum(bt.packed_bytes(n, k) for k, n in
                      [(1536, 2048), (1536, 1536), (1536, 17920), (8960, 1536)])
@@ -155,16 +156,24 @@ def test_plan_building_on_host():
     assert L.bt_quant_plan_build(q, 2, host.ctypes.data, nb) == NULL
 
     m = (BtMatmulDesc * 2)(BtMatmulDesc(1, 2048, 1536, f, f, f, f, 0.02, f, None),
-                           BtMatmulDesc(4, 1536, 8960, f, f, f, f, 0.03, f, f))
+                           BtMatmulDesc(3, 1536, 8960, f, f, f, f, 0.03, f, f))
     nb = L.bt_matmul_plan_bytes(2)
     host = np.zeros(nb, np.uint8)
-    assert L.bt_matmul_plan_build(m, 2, host.ctypes.data, nb) == OK
-    assert host[:16].view(np.int64)[1] == 2048 // 64 + 1536 // 64
+    assert L.bt_matmul_plan_workspace_bytes(m, 2) == 0      # both fit one LDS slice
+    assert L.bt_matmul_plan_build(m, 2, None, 0, host.ctypes.data, nb) == OK
+    # two tiles per wave, four waves per workgroup: 64 output rows per workgroup
+    assert host[:16].view(np.int64)[1] == 2048 // 128 + 1536 // 128
     m[0].M = 17
-    assert L.bt_matmul_plan_build(m, 2, host.ctypes.data, nb) == SHAPE
+    assert L.bt_matmul_plan_build(m, 2, None, 0, host.ctypes.data, nb) == SHAPE
     m[0].M = 1
     m[1].w_scale = float("nan")
-    assert L.bt_matmul_plan_build(m, 2, host.ctypes.data, nb) == VALUE
+    assert L.bt_matmul_plan_build(m, 2, None, 0, host.ctypes.data, nb) == VALUE
+    m[1].w_scale = 0.5
+    m[1].M = 16                     # 17 rows of 8960 int8 exceed the LDS slice: K is split
+    need = L.bt_matmul_plan_workspace_bytes(m, 2)
+    assert need > 0
+    assert L.bt_matmul_plan_build(m, 2, None, 0, host.ctypes.data, nb) == WORKSPACE
+    assert L.bt_matmul_plan_build(m, 2, f, need, host.ctypes.data, nb) == OK
     # a launch with a plan of the wrong kind is refused on the host
     assert L.bt_quantize_act_grouped(host.ctypes.data, f, None) == VALUE
 
