@@ -254,6 +254,9 @@ def main():
     ap.add_argument("--prefill-steps", type=int, default=5)
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 1 GiB device-to-device copy (5 times), to scale the "
+                         "FETCH_SIZE / WRITE_SIZE counters of a profiler run")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -261,6 +264,17 @@ def main():
               "(each GPU would serve its own decode streams with replicated weights).",
               file=sys.stderr)
         sys.exit(2)
+
+    if args.copy_calibration:
+        import torch
+        src = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_read_per_launch": src.numel() * 4,
+                          "copy_bytes_written_per_launch": dst.numel() * 4, "launches": 5}))
+        return
 
     packed_prefill = None
     if not args.no_prefill:
