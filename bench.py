@@ -3,9 +3,11 @@
 Headline workload: one decode step of the 28-layer, 1.5B-shaped decoder at M=1
 (per layer QKV 1536->2048, O 1536->1536, gate+up 1536->17920, down 8960->1536;
 327,548,928 bytes of 2-bit weights). A step quantizes the 112 activation
-vectors (one grouped launch) and runs the 112 ternary GEMVs (one grouped
-launch). Two copies of the weights alternate between steps so the 256 MB
-on-package cache cannot hold them. value = packed weight bytes / step time.
+vectors and runs the 112 ternary GEMVs in one launch (quantization fused into
+the grouped GEMV); the same step as two launches (grouped quantize, grouped
+GEMV) is reported beside it. Two copies of the weights alternate between steps
+so the 256 MB on-package cache cannot hold them. value = packed weight bytes /
+step time.
 
 Secondary workload (--prefill, on by default): long prefill, M=4096 tokens
 through all 112 projections (per projection: quantize, then the MFMA GEMM),
@@ -35,7 +37,7 @@ import synth  # noqa: E402
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 I8_PEAK_TOPS = 5000.0          # MI355X dense int8 MFMA, TOPS
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemv_grouped_decode_step_traffic.json")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemv_decode_step_traffic.json")
 KERNEL_SRC = os.path.join(ROOT, "ternary_weight_decoder_bt_amd", "csrc", "bt_kernels.hip")
 
 METRIC = "ternary GEMV HBM GB/s (% of peak) + decode-step tokens/s; prefill int8 TOPS"
@@ -50,9 +52,9 @@ def kernel_source_hash() -> str:
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
-def measured_traffic(per_launch_bytes: float):
-    """HBM bytes per launch from the committed counter summary, or None when
-    the kernels changed since the counters were taken."""
+def measured_traffic(kernel: str):
+    """HBM bytes per launch of `kernel` from the committed counter summary, or
+    None when the kernels changed since the counters were taken."""
     try:
         with open(TRAFFIC_FILE) as f:
             t = json.load(f)
@@ -60,17 +62,26 @@ def measured_traffic(per_launch_bytes: float):
         return None
     if t.get("kernel_source_sha256_16") != kernel_source_hash():
         return None
-    return t.get("hbm_bytes_per_launch")
+    return t.get("kernels", {}).get(kernel, {}).get("hbm_bytes_per_launch")
 
 
 # --------------------------------------------------------------- decode step
 
 class DecodeStep:
+    """The 112 projections of one decode step, resident on the GPU.
+
+    Headline path: one fused launch per step (bt_ternary_matmul_grouped with a
+    plan whose descriptors carry the fp32 activations: quantization runs
+    inside the GEMV). Context path: the same work as two launches (grouped
+    quantize, then grouped GEMV on the quantized activations).
+    """
+
     def __init__(self, torch, bt, dev, layers: int):
         self.torch, self.bt = torch, bt
-        self.items_q, self.items = [], []
+        self.items_q, self.items, self.fitems = [], [], []
         self.w_bytes = 0
-        self.alg_bytes = 0            # weights + q + y + scales per GEMV launch
+        self.alg_bytes = 0            # bytes the fused launch must move at least
+        self.alg_bytes_gemv = 0       # bytes the unfused GEMV launch must move at least
         self.shapes = []
         wsets = ([], [])
         t0 = time.time()
@@ -89,13 +100,21 @@ class DecodeStep:
                 xsum = torch.empty(m, dtype=torch.int32, device=dev)
                 y = torch.empty((m, n), dtype=torch.float32, device=dev)
                 self.items_q.append((x, xq, xs, xsum))
-                self.items.append({"xq": xq, "xscale": xs, "xsum": xsum, "n": n,
-                                   "w_scale": c["w_scale"], "y": y})
+                base = {"xq": xq, "xscale": xs, "xsum": xsum, "n": n, "w_scale": c["w_scale"],
+                        "y": y}
+                self.items.append(base)
+                self.fitems.append(dict(base, x=x))
                 self.shapes.append((layer, proj, m, n, k))
-                self.w_bytes += bt.packed_bytes(n, k)
-                self.alg_bytes += bt.packed_bytes(n, k) + m * k + 4 * m * n + 8 * m
+                wb = bt.packed_bytes(n, k)
+                self.w_bytes += wb
+                # fused: read x, write q once, write y, write d and the row sum
+                self.alg_bytes += wb + 4 * m * k + m * k + 4 * m * n + 8 * m
+                # unfused GEMV: read q, d and the row sum, write y
+                self.alg_bytes_gemv += wb + m * k + 4 * m * n + 8 * m
         self.qplan = bt.QuantPlan(self.items_q)
         self.mplans = [bt.MatmulPlan([dict(it, wdev=w) for it, w in zip(self.items, ws)])
+                       for ws in wsets]
+        self.fplans = [bt.MatmulPlan([dict(it, wdev=w) for it, w in zip(self.fitems, ws)])
                        for ws in wsets]
         self.wsets = wsets
         torch.cuda.synchronize()
@@ -103,12 +122,25 @@ class DecodeStep:
             f"setup {time.time() - t0:.1f}s")
 
     def step(self, i, ev=None):
+        """One decode step as one fused launch (events, if given, bracket it)."""
+        if ev is not None:
+            ev[0].record()
+        self.fplans[i & 1].launch()
+        if ev is not None:
+            ev[1].record()
+
+    def step_two_launch(self, i, ev=None):
         self.qplan.launch()
         if ev is not None:
             ev[0].record()
         self.mplans[i & 1].launch()
         if ev is not None:
             ev[1].record()
+
+    def clear_outputs(self):
+        for it in self.items:
+            it["y"].fill_(float("nan"))
+            it["xq"].fill_(99)
 
     def parity(self, idx_list):
         """Full oracle comparison of a few projections, untimed."""
@@ -122,6 +154,7 @@ class DecodeStep:
             y = it["y"].cpu().numpy()
             ok &= np.array_equal(it["xq"].cpu().numpy(), ref["q"])
             ok &= np.array_equal(it["xscale"].cpu().numpy(), ref["d"])
+            ok &= np.array_equal(it["xsum"].cpu().numpy(), ref["qsum"])
             nz = ref["y"] != 0
             ok &= bool((y[~nz] == 0).all())
             ok &= bool((np.abs(y[nz] - ref["y"][nz]) <= 1e-6 * np.abs(ref["y"][nz])).all())
@@ -293,33 +326,72 @@ def main():
 
     # ---- decode step (headline)
     ds = DecodeStep(torch, bt, dev, args.layers)
+    check_idx = [0, 1, 2, 3, len(ds.items) - 1]
+    ds.clear_outputs()
+    ds.step_two_launch(0)
+    torch.cuda.synchronize()
+    two_launch_ok = ds.parity(check_idx)
+    ds.clear_outputs()
     ds.step(0)
     torch.cuda.synchronize()
-    decode_ok = ds.parity([0, 1, 2, 3, len(ds.items) - 1])
-    log(f"decode parity on sampled projections: {decode_ok}")
+    decode_ok = ds.parity(check_idx) and two_launch_ok
+    log(f"decode parity on sampled projections: fused {decode_ok}, two-launch {two_launch_ok}")
+
+    def time_steps(step_fn, steps):
+        """Step time: `steps` steps between two events, nothing recorded in between."""
+        start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        start.record()
+        for i in range(steps):
+            step_fn(i)
+        stop.record()
+        torch.cuda.synchronize()
+        return start.elapsed_time(stop) / steps
+
+    def time_kernel(step_fn, steps):
+        """Duration of the step's GEMV launch: an event pair on the launch stream
+        around it in every step (a separate pass, since each recorded event
+        adds a few microseconds of queue time between launches)."""
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(steps)]
+        torch.cuda.synchronize()
+        for i in range(steps):
+            step_fn(i, evs[i])
+        torch.cuda.synchronize()
+        return [a.elapsed_time(b) for a, b in evs]
+
     for i in range(args.warmup):
         ds.step(i)
-    torch.cuda.synchronize()
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(args.steps)]
-    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        ds.step_two_launch(i)
     torch.cuda.synchronize()
     t_wall = time.perf_counter()
-    start.record()
-    for i in range(args.steps):
-        ds.step(i, evs[i])
-    stop.record()
-    torch.cuda.synchronize()
+    ms_fused = time_steps(ds.step, args.steps)
+    ms_two = time_steps(ds.step_two_launch, args.steps)
     t_wall = time.perf_counter() - t_wall
-    ms_step = start.elapsed_time(stop) / args.steps
-    gemv_ms = [a.elapsed_time(b) for a, b in evs]
-    gemv_avg_ms = float(np.mean(gemv_ms))
+    k_fused = time_kernel(ds.step, args.steps)
+    k_two = time_kernel(ds.step_two_launch, args.steps)
+    paths = {
+        "fused": {"ms_per_step": ms_fused, "kernel_ms": k_fused, "alg": ds.alg_bytes,
+                  "kernel": "gemv_grouped_kernel<true>",
+                  "workload": "one launch per step: quantization fused into the grouped GEMV"},
+        "two_launch": {"ms_per_step": ms_two, "kernel_ms": k_two, "alg": ds.alg_bytes_gemv,
+                       "kernel": "gemv_grouped_kernel<false>",
+                       "workload": "two launches per step: grouped quantize, then grouped GEMV"},
+    }
+    head_name = min(paths, key=lambda k: paths[k]["ms_per_step"])
+    head = paths[head_name]
+    other = paths["two_launch" if head_name == "fused" else "fused"]
+    ms_step = head["ms_per_step"]
+    kern_avg_ms = float(np.mean(head["kernel_ms"]))
     value = ds.w_bytes / (ms_step * 1e-3) / 1e9
-    achieved = ds.alg_bytes / (gemv_avg_ms * 1e-3) / 1e9
-    traffic = measured_traffic(ds.alg_bytes)
-    log(f"decode: {ms_step * 1e3:.1f} us/step, GEMV {gemv_avg_ms * 1e3:.1f} us "
-        f"(p10 {np.percentile(gemv_ms, 10) * 1e3:.1f}, p90 {np.percentile(gemv_ms, 90) * 1e3:.1f}), "
-        f"{value:.0f} GB/s, wall {t_wall:.2f}s")
+    achieved = head["alg"] / (kern_avg_ms * 1e-3) / 1e9
+    traffic = measured_traffic(head["kernel"])
+    for name, p in paths.items():
+        km = np.array(p["kernel_ms"]) * 1e3
+        log(f"decode [{name}]: {p['ms_per_step'] * 1e3:.1f} us/step, GEMV kernel "
+            f"{km.mean():.1f} us (p10 {np.percentile(km, 10):.1f}, p90 {np.percentile(km, 90):.1f}), "
+            f"{ds.w_bytes / p['ms_per_step'] / 1e6:.0f} GB/s over weights")
+    log(f"headline path: {head_name}; timed region wall {t_wall:.2f}s")
 
     out = {
         "metric": METRIC,
@@ -336,17 +408,26 @@ def main():
         "data": "synthetic (seeded; ternary weights uniform over {-1,0,1}, x ~ N(0,1) with 0.1% x20; random-init, no checkpoint)",
         "config": {"workload": "decode step, 28-layer 1.5B-shaped decoder, M=1: per layer "
                                "qkv 1536->2048, o 1536->1536, gate_up 1536->17920, "
-                               "down 8960->1536 (grouped quantize + grouped GEMV launch)",
+                               "down 8960->1536 (" + head["workload"] + ")",
                    "layers": args.layers, "M": 1, "weight_bytes_per_step": ds.w_bytes,
-                   "weight_sets_alternating": 2},
+                   "weight_sets_alternating": 2, "path": head_name},
         "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
         "tokens_per_s": round(1e3 / ms_step, 1),
         "parity_ok": decode_ok,
-        "roofline": {"bound": "hbm", "kernel": "gemv_grouped_kernel",
+        "roofline": {"bound": "hbm", "kernel": head["kernel"],
                      "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
-                     "algorithmic_bytes_per_launch": ds.alg_bytes,
-                     "avg_launch_ms": round(gemv_avg_ms, 5)},
+                     "algorithmic_bytes_per_launch": head["alg"],
+                     "avg_launch_ms": round(kern_avg_ms, 5)},
+        "decode_other_path": {
+            "path": "two_launch" if head_name == "fused" else "fused",
+            "workload": other["workload"],
+            "ms_per_step": round(other["ms_per_step"], 5),
+            "gb_per_s_over_weights": round(ds.w_bytes / (other["ms_per_step"] * 1e-3) / 1e9, 2),
+            "kernel": other["kernel"],
+            "kernel_avg_ms": round(float(np.mean(other["kernel_ms"])), 5),
+            "kernel_achieved_gb_per_s": round(
+                other["alg"] / (np.mean(other["kernel_ms"]) * 1e-3) / 1e9, 2)},
     }
     del ds
     torch.cuda.empty_cache()
@@ -358,16 +439,20 @@ def main():
         lp.step()
         torch.cuda.synchronize()
         pf_ok = lp.parity()
-        gev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-                for _ in lp.probs] for _ in range(args.prefill_steps)]
         s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
         s0.record()
         for i in range(args.prefill_steps):
-            lp.step(gev[i])
+            lp.step()
         s1.record()
         torch.cuda.synchronize()
         ms = s0.elapsed_time(s1) / args.prefill_steps
+        # GEMM durations: event pairs around each GEMM, in a separate pass
+        gev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                for _ in lp.probs] for _ in range(args.prefill_steps)]
+        for i in range(args.prefill_steps):
+            lp.step(gev[i])
+        torch.cuda.synchronize()
         gemm_ms = float(np.mean([sum(a.elapsed_time(b) for a, b in g) for g in gev]))
         tops = lp.ops / (ms * 1e-3) / 1e12
         gemm_tops = lp.ops / (gemm_ms * 1e-3) / 1e12

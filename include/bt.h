@@ -130,6 +130,18 @@ bt_status bt_quantize_act(const float* x, int64_t M, int64_t K, int8_t* xq, floa
  * ------------------------------------------------------------------------- */
 size_t bt_matmul_workspace_bytes(int64_t M, int64_t N, int64_t K);
 
+/* Quantization fused into the GEMV (M <= BT_GEMV_MAX_M): the same result as
+ * bt_quantize_act followed by bt_ternary_matmul, in one launch. Every
+ * workgroup quantizes the whole of each token row (the row sums and scales
+ * need all of it) and keeps its own K range, so it pays off for small M (the
+ * decode step). x: device fp32 M x K. xq, xscale, xsum: optional outputs
+ * (NULL to skip), written with exactly bt_quantize_act's values. Workspace as
+ * for bt_ternary_matmul with the same M, N, K. */
+bt_status bt_ternary_matmul_fused(int64_t M, int64_t N, int64_t K, const float* x,
+                                  const void* wdev, float w_scale, float* y, int32_t* acc,
+                                  int8_t* xq, float* xscale, int32_t* xsum, void* workspace,
+                                  size_t workspace_bytes, hipStream_t stream);
+
 bt_status bt_ternary_matmul(int64_t M, int64_t N, int64_t K, const int8_t* xq,
                             const float* xscale, const int32_t* xsum, const void* wdev,
                             float w_scale, float* y, int32_t* acc, void* workspace,
@@ -160,13 +172,15 @@ typedef struct bt_quant_desc {
 
 typedef struct bt_matmul_desc {
     int64_t M, N, K;        /* M <= BT_GEMV_MAX_M in a grouped plan */
-    const int8_t* xq;
-    const float* xscale;
-    const int32_t* xsum;
+    const int8_t* xq;       /* x == NULL: input from bt_quantize_act. x != NULL: optional output */
+    const float* xscale;    /* same */
+    const int32_t* xsum;    /* same */
     const void* wdev;
     float w_scale;
     float* y;
     int32_t* acc;           /* may be NULL */
+    const float* x;         /* NULL, or fp32 M x K activations to quantize inside the launch
+                               (then every descriptor of the plan must give x) */
 } bt_matmul_desc;
 
 size_t bt_quant_plan_bytes(int32_t count);

@@ -23,5 +23,6 @@ from .ops import (  # noqa: F401
     repack_ternary,
     repacked_bytes,
     ternary_matmul,
+    ternary_matmul_fused,
     unpack_ternary,
 )

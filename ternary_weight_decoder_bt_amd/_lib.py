@@ -29,6 +29,8 @@ SIGNATURES = {
     "bt_quantize_act": (C.c_int, [_p, _i64, _i64, _p, _p, _p, _p]),
     "bt_matmul_workspace_bytes": (_sz, [_i64, _i64, _i64]),
     "bt_ternary_matmul": (C.c_int, [_i64, _i64, _i64, _p, _p, _p, _p, _f, _p, _p, _p, _sz, _p]),
+    "bt_ternary_matmul_fused": (C.c_int, [_i64, _i64, _i64, _p, _p, _f, _p, _p, _p, _p, _p, _p,
+                                          _sz, _p]),
     "bt_quant_plan_bytes": (_sz, [_i32]),
     "bt_quant_plan_build": (C.c_int, [_p, _i32, _p, _sz]),
     "bt_quantize_act_grouped": (C.c_int, [_p, _p, _p]),
@@ -45,7 +47,7 @@ class BtQuantDesc(C.Structure):
 
 class BtMatmulDesc(C.Structure):
     _fields_ = [("M", _i64), ("N", _i64), ("K", _i64), ("xq", _p), ("xscale", _p),
-                ("xsum", _p), ("wdev", _p), ("w_scale", _f), ("y", _p), ("acc", _p)]
+                ("xsum", _p), ("wdev", _p), ("w_scale", _f), ("y", _p), ("acc", _p), ("x", _p)]
 
 
 class BtError(RuntimeError):

@@ -188,10 +188,12 @@ extern "C" size_t bt_matmul_plan_bytes(int32_t count) {
     return sizeof(bt::PlanHeader) + size_t(count) * sizeof(bt::GemvDesc);
 }
 
-static bt_status check_matmul_desc(const bt_matmul_desc& m) {
-    if (!m.xq || !m.xscale || !m.xsum || !m.wdev || !m.y) return BT_ERR_NULL;
+static bt_status check_matmul_desc(const bt_matmul_desc& m, bool fused) {
+    if (!m.wdev || !m.y) return BT_ERR_NULL;
+    if (fused ? !m.x : (!m.xq || !m.xscale || !m.xsum)) return BT_ERR_NULL;
     if (m.M < 1 || m.M > BT_GEMV_MAX_M || !valid_nk(m.N, m.K)) return BT_ERR_SHAPE;
-    if (!bt::aligned16(m.xq) || !bt::aligned16(m.xscale) || !bt::aligned16(m.xsum) ||
+    if ((m.xq && !bt::aligned16(m.xq)) || (m.xscale && !bt::aligned16(m.xscale)) ||
+        (m.xsum && !bt::aligned16(m.xsum)) || (m.x && !bt::aligned16(m.x)) ||
         !bt::aligned16(m.wdev) || !bt::aligned16(m.y) || (m.acc && !bt::aligned16(m.acc)))
         return BT_ERR_ALIGN;
     if (!std::isfinite(m.w_scale)) return BT_ERR_VALUE;
@@ -217,8 +219,10 @@ extern "C" bt_status bt_matmul_plan_build(const bt_matmul_desc* descs, int32_t c
     if (!descs || !plan_host) return BT_ERR_NULL;
     if (count < 1) return BT_ERR_SHAPE;
     if (plan_bytes < bt_matmul_plan_bytes(count)) return BT_ERR_WORKSPACE;
+    const bool fused = descs[0].x != nullptr;
     for (int32_t i = 0; i < count; ++i) {
-        const bt_status st = check_matmul_desc(descs[i]);
+        if ((descs[i].x != nullptr) != fused) return BT_ERR_VALUE;   // all fused or none
+        const bt_status st = check_matmul_desc(descs[i], fused);
         if (st != BT_OK) return st;
     }
     const size_t need = bt_matmul_plan_workspace_bytes(descs, count);
@@ -228,15 +232,15 @@ extern "C" bt_status bt_matmul_plan_build(const bt_matmul_desc* descs, int32_t c
     }
     auto* hdr = static_cast<bt::PlanHeader*>(plan_host);
     auto* out = reinterpret_cast<bt::GemvDesc*>(hdr + 1);
-    int64_t blocks = 0;
     char* ws = static_cast<char*>(workspace);
     for (int32_t i = 0; i < count; ++i) {
         const bt_matmul_desc& m = descs[i];
         bt::GemvDesc d;
         bt::gemv_shape(m.M, m.N, m.K, true, &d);
-        d.xq = m.xq;
-        d.xscale = m.xscale;
-        d.xsum = m.xsum;
+        d.x = m.x;
+        d.xq = const_cast<int8_t*>(m.xq);
+        d.xscale = const_cast<float*>(m.xscale);
+        d.xsum = const_cast<int32_t*>(m.xsum);
         d.w = static_cast<const uint8_t*>(m.wdev);
         d.y = m.y;
         d.acc = m.acc;
@@ -246,12 +250,21 @@ extern "C" bt_status bt_matmul_plan_build(const bt_matmul_desc* descs, int32_t c
             d.cnt = reinterpret_cast<uint32_t*>(ws + bt::gemv_partial_bytes(d));
             ws += bt::gemv_workspace_bytes(d);
         }
-        d.block_begin = blocks;
-        blocks += d.blocks;
         out[i] = d;
     }
+    // Longest workgroups first: the grid drains in dispatch order, so the
+    // long-K projections (e.g. down, 8960 wide) must not be the tail.
+    std::stable_sort(out, out + count, [](const bt::GemvDesc& a, const bt::GemvDesc& b) {
+        return int64_t(a.steps_per_chunk) * a.tiles_per_wave >
+               int64_t(b.steps_per_chunk) * b.tiles_per_wave;
+    });
+    int64_t blocks = 0;
+    for (int32_t i = 0; i < count; ++i) {
+        out[i].block_begin = blocks;
+        blocks += out[i].blocks;
+    }
     if (blocks > int64_t(1) << 31) return BT_ERR_SHAPE;
-    hdr->magic = bt::kPlanMagicGemv;
+    hdr->magic = fused ? bt::kPlanMagicGemvFused : bt::kPlanMagicGemv;
     hdr->count = count;
     hdr->total_blocks = blocks;
     return BT_OK;

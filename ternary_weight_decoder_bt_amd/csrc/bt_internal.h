@@ -17,21 +17,32 @@ constexpr int kQuantThreads = 256;  // threads per quantized row
 
 constexpr uint32_t kPlanMagicQuant = 0x42545141u;   // "AQTB"
 constexpr uint32_t kPlanMagicGemv = 0x42544d47u;    // "GMTB"
+constexpr uint32_t kPlanMagicGemvFused = 0x42544646u;   // "FFTB"
 
 inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 // GEMV tuning: weight steps (1 KB per wave) loaded per batch, and the LDS
 // slice that holds one workgroup's int8 activations (M rows x its K range).
-constexpr int kGemvBatch = 6;
+#ifndef BT_GEMV_BATCH
+#define BT_GEMV_BATCH 6
+#endif
+#ifndef BT_GEMV_NONTEMPORAL
+#define BT_GEMV_NONTEMPORAL 1
+#endif
+#ifndef BT_GEMV_TILES_PER_WAVE
+#define BT_GEMV_TILES_PER_WAVE 2
+#endif
+constexpr int kGemvBatch = BT_GEMV_BATCH;
 constexpr int kGemvLdsBytes = 40960;
-constexpr int kGemvGroupedTilesPerWave = 2;
+constexpr int kGemvGroupedTilesPerWave = BT_GEMV_TILES_PER_WAVE;
 
 // One GEMV problem as the kernel sees it. The single-matrix call passes it by
 // value; a grouped plan stores an array of them in device memory.
 struct GemvDesc {
-    const int8_t* xq;
-    const float* xscale;
-    const int32_t* xsum;
+    const float* x;         // fused quantization: fp32 activations (else null)
+    int8_t* xq;             // unfused: input. fused: optional output (written once)
+    float* xscale;          // same
+    int32_t* xsum;          // same
     const uint8_t* w;       // repacked tiles
     float* y;
     int32_t* acc;           // may be null

@@ -43,6 +43,7 @@ using bt::QuantDesc;
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef unsigned int v4u __attribute__((ext_vector_type(4)));
 typedef unsigned int v2u __attribute__((ext_vector_type(2)));
+typedef float v4f __attribute__((ext_vector_type(4)));
 
 constexpr uint32_t kLow2 = 0x03030303u;
 
@@ -288,7 +289,11 @@ __device__ __forceinline__ void gemv_issue(GemvBatch& b, const uint8_t* wt, int 
 #pragma unroll
     for (int u = 0; u < kB; ++u) {
         const int st = min(sb + u, last);
+#if BT_GEMV_NONTEMPORAL
         b.w[u] = gld_stream<v4u>(wt + int64_t(st) * 1024 + lane * 16);
+#else
+        b.w[u] = gld<v4u>(wt + int64_t(st) * 1024 + lane * 16);
+#endif
     }
 }
 
@@ -304,10 +309,18 @@ __device__ __forceinline__ v4i gemv_consume(const GemvBatch& b, int n, const int
     return c;
 }
 
+struct GemvShared {
+    QuantShared red;
+    float d[BT_GEMV_MAX_M];      // fused quantization: per-token scale
+    int32_t qs[BT_GEMV_MAX_M];   // fused quantization: per-token sum of q
+};
+
 // Epilogue of one tile. With K split into chunks, partial sums meet in the
 // workspace (int32 addition is exact in any order) and the last chunk to
 // arrive reads the total, clears the workspace and finishes the tile.
-__device__ __forceinline__ void gemv_finish(const GemvDesc& d, int64_t tile, v4i c, int lane) {
+template <bool kFused>
+__device__ __forceinline__ void gemv_finish(const GemvDesc& d, int64_t tile, v4i c, int lane,
+                                            const GemvShared& sh) {
     const int kq = lane >> 4;
     const int64_t n = tile * bt::kTileN + (lane & 15);
     if (d.chunks > 1) {
@@ -335,8 +348,10 @@ __device__ __forceinline__ void gemv_finish(const GemvDesc& d, int64_t tile, v4i
         for (int i = 0; i < 4; ++i) {
             const int mm = 4 * kq + i;
             if (mm < d.M) {
-                const int32_t acc = c[i] - gld<int32_t>(d.xsum + mm);
-                const float rs = gld<float>(d.xscale + mm) * d.w_scale;
+                const int32_t qsum = kFused ? sh.qs[mm] : gld<int32_t>(d.xsum + mm);
+                const float dm = kFused ? sh.d[mm] : gld<float>(d.xscale + mm);
+                const int32_t acc = c[i] - qsum;
+                const float rs = dm * d.w_scale;
                 gst<float>(d.y + int64_t(mm) * d.N + n, float(acc) * rs);
                 if (d.acc) gst<int32_t>(d.acc + int64_t(mm) * d.N + n, acc);
             }
@@ -344,7 +359,81 @@ __device__ __forceinline__ void gemv_finish(const GemvDesc& d, int64_t tile, v4i
     }
 }
 
-__device__ __forceinline__ void gemv_block(const GemvDesc& d, int64_t local_block, int8_t* lds) {
+// Fused quantization prologue: each workgroup quantizes the whole of every
+// token row (the row sum of q and the scale need all of it), keeps its own K
+// chunk in LDS, and the first workgroup of the problem also writes q, d and
+// the row sums out when asked to. The arithmetic is quantize_row's exactly.
+// Rows up to kFusedRegs*1024 elements are read once and held in registers
+// between the absmax and the quantize pass; longer rows are read twice.
+constexpr int kFusedRegs = 2;   // float4 per thread: K <= 2048 in one read
+
+__device__ __forceinline__ int gemv_quant_store(v4f v, float inv, int64_t k, int m, bool writer,
+                                                const GemvDesc& d, int64_t kbeg, int64_t kend,
+                                                int8_t* lds) {
+    const int a = quant1(v.x * inv), b = quant1(v.y * inv);
+    const int c = quant1(v.z * inv), e = quant1(v.w * inv);
+    const int packed = pack4(a, b, c, e);
+    if (k >= kbeg && k < kend) lds_st<int>(lds + m * d.lds_row + (k - kbeg), packed);
+    if (writer && d.xq) gst<int>(d.xq + int64_t(m) * d.K + k, packed);
+    return a + b + c + e;
+}
+
+__device__ __forceinline__ void gemv_quantize_rows(const GemvDesc& d, bool writer, int64_t kbeg,
+                                                   int64_t kend, int8_t* lds, GemvShared& sh) {
+    const int tid = threadIdx.x;
+    constexpr int T = 64 * bt::kGemvWaves;
+    const int64_t K4 = d.K >> 2;   // K % 128 == 0
+    const bool in_regs = K4 <= int64_t(kFusedRegs) * T;
+    for (int m = 0; m < d.M; ++m) {
+        const float* xr = d.x + int64_t(m) * d.K;
+        float amax = 0.0f;
+        int s = 0;
+        if (in_regs) {
+            v4f v[kFusedRegs];
+#pragma unroll
+            for (int j = 0; j < kFusedRegs; ++j) {
+                const int64_t i = tid + int64_t(j) * T;
+                v[j] = i < K4 ? gld<v4f>(xr + 4 * i) : v4f{0.0f, 0.0f, 0.0f, 0.0f};
+            }
+#pragma unroll
+            for (int j = 0; j < kFusedRegs; ++j)
+                amax = fmaxf(amax, fmaxf(fmaxf(fabsf(v[j].x), fabsf(v[j].y)),
+                                         fmaxf(fabsf(v[j].z), fabsf(v[j].w))));
+            amax = block_max(amax, sh.red);
+            float inv = 127.0f / amax;
+            if (!(inv <= FLT_MAX)) inv = 0.0f;
+#pragma unroll
+            for (int j = 0; j < kFusedRegs; ++j) {
+                const int64_t i = tid + int64_t(j) * T;
+                if (i < K4) s += gemv_quant_store(v[j], inv, 4 * i, m, writer, d, kbeg, kend, lds);
+            }
+        } else {
+            for (int64_t i = tid; i < K4; i += T) {
+                const v4f v = gld<v4f>(xr + 4 * i);
+                amax = fmaxf(amax, fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w))));
+            }
+            amax = block_max(amax, sh.red);
+            float inv = 127.0f / amax;
+            if (!(inv <= FLT_MAX)) inv = 0.0f;
+            for (int64_t i = tid; i < K4; i += T)
+                s += gemv_quant_store(gld<v4f>(xr + 4 * i), inv, 4 * i, m, writer, d, kbeg, kend, lds);
+        }
+        s = block_sum(s, sh.red);
+        if (tid == 0) {
+            const bool dead = !(127.0f / amax <= FLT_MAX);
+            const float dm = dead ? 0.0f : amax / 127.0f;
+            sh.d[m] = dm;
+            sh.qs[m] = s;
+            if (writer && d.xscale) gst<float>(d.xscale + m, dm);
+            if (writer && d.xsum) gst<int32_t>(d.xsum + m, s);
+        }
+        __syncthreads();   // the reduction slots are reused by the next row
+    }
+}
+
+template <bool kFused>
+__device__ __forceinline__ void gemv_block(const GemvDesc& d, int64_t local_block, int8_t* lds,
+                                           GemvShared& sh) {
     const int tid = threadIdx.x;
     const int wave = tid >> 6;
     const int lane = tid & 63;
@@ -353,22 +442,6 @@ __device__ __forceinline__ void gemv_block(const GemvDesc& d, int64_t local_bloc
     const int s0 = chunk * d.steps_per_chunk;
     const int s1 = min(s0 + d.steps_per_chunk, d.steps);
     const int nsteps = s1 - s0;
-
-    // Stage q[0:M][256*s0 : 256*s1] in LDS rows 0..M-1 (zero past K) and a
-    // zero row M, which the lanes of tokens >= M read instead.
-    const int64_t kbeg = int64_t(s0) * bt::kSuperK;
-    const int pieces = nsteps * (bt::kSuperK / 16);
-    for (int i = tid; i < (d.M + 1) * pieces; i += 64 * bt::kGemvWaves) {
-        const int m = i / pieces;
-        const int col = (i - m * pieces) * 16;
-        v4i v = {0, 0, 0, 0};
-        if (m < d.M && kbeg + col < d.K) v = gld<v4i>(d.xq + int64_t(m) * d.K + kbeg + col);
-        lds_st<v4i>(lds + m * d.lds_row + col, v);
-    }
-    __syncthreads();
-
-    const int am = min(lane & 15, d.M);
-    const int8_t* abase = lds + am * d.lds_row + 16 * (lane >> 4);
     const int nb = (nsteps + kB - 1) / kB;
     const int total = d.tiles_per_wave * nb;
     const int64_t tile0 = g * (int64_t(bt::kGemvWaves) * d.tiles_per_wave) + wave;
@@ -378,13 +451,45 @@ __device__ __forceinline__ void gemv_block(const GemvDesc& d, int64_t local_bloc
     // (2*kB KB in flight per wave), then consumed. Loads are unconditional:
     // a tile past N or a step past the chunk is clamped to a valid address and
     // its data is never consumed.
-    v4i cur = {0, 0, 0, 0};
     auto issue = [&](GemvBatch& b, int idx) {
         const int r = idx / nb;
         const int bb = idx - r * nb;
         const int64_t t = min(tile0 + int64_t(bt::kGemvWaves) * r, int64_t(d.tiles) - 1);
         gemv_issue(b, d.w + t * tile_bytes, s0 + bb * kB, s1 - 1, lane);
     };
+
+    // The first two batches go out before the activations are staged, so the
+    // weight latency overlaps the staging.
+    GemvBatch b0, b1;
+    issue(b0, 0);
+    issue(b1, min(1, total - 1));
+
+    // Stage this chunk of the M token rows in LDS rows 0..M-1 (zero past K)
+    // and a zero row M, which the lanes of tokens >= M read instead.
+    const int64_t kbeg = int64_t(s0) * bt::kSuperK;
+    const int64_t kend = int64_t(s1) * bt::kSuperK;
+    const int pieces = nsteps * (bt::kSuperK / 16);
+    if (kFused) {
+        for (int i = tid; i < (d.M + 1) * pieces; i += 64 * bt::kGemvWaves) {
+            const int m = i / pieces;
+            const int col = (i - m * pieces) * 16;
+            if (m == d.M || kbeg + col >= d.K) lds_st<v4i>(lds + m * d.lds_row + col, v4i{0, 0, 0, 0});
+        }
+        gemv_quantize_rows(d, chunk == 0 && g == 0, kbeg, kend, lds, sh);
+    } else {
+        for (int i = tid; i < (d.M + 1) * pieces; i += 64 * bt::kGemvWaves) {
+            const int m = i / pieces;
+            const int col = (i - m * pieces) * 16;
+            v4i v = {0, 0, 0, 0};
+            if (m < d.M && kbeg + col < d.K) v = gld<v4i>(d.xq + int64_t(m) * d.K + kbeg + col);
+            lds_st<v4i>(lds + m * d.lds_row + col, v);
+        }
+        __syncthreads();
+    }
+
+    const int am = min(lane & 15, d.M);
+    const int8_t* abase = lds + am * d.lds_row + 16 * (lane >> 4);
+    v4i cur = {0, 0, 0, 0};
     auto consume = [&](const GemvBatch& b, int idx) {
         const int r = idx / nb;
         const int bb = idx - r * nb;
@@ -392,18 +497,19 @@ __device__ __forceinline__ void gemv_block(const GemvDesc& d, int64_t local_bloc
         if (t >= d.tiles) return;
         cur = gemv_consume(b, min(kB, nsteps - bb * kB), abase + bb * kB * 256, cur);
         if (bb == nb - 1) {
-            gemv_finish(d, t, cur, lane);
+            gemv_finish<kFused>(d, t, cur, lane, sh);
             cur = v4i{0, 0, 0, 0};
         }
     };
 
     // The scheduling barriers keep the unpacking of batch 1 below the use of
-    // batch 0, so the wait before batch 0 leaves batch 1's loads in flight.
-    GemvBatch b0, b1;
+    // batch 0.
     for (int idx = 0; idx < total; idx += 2) {
-        issue(b0, idx);
-        __builtin_amdgcn_sched_barrier(0);
-        issue(b1, min(idx + 1, total - 1));
+        if (idx > 0) {
+            issue(b0, idx);
+            __builtin_amdgcn_sched_barrier(0);
+            issue(b1, min(idx + 1, total - 1));
+        }
         __builtin_amdgcn_sched_barrier(0);
         consume(b0, idx);
         __builtin_amdgcn_sched_barrier(0);
@@ -411,14 +517,18 @@ __device__ __forceinline__ void gemv_block(const GemvDesc& d, int64_t local_bloc
     }
 }
 
+template <bool kFused>
 __global__ __launch_bounds__(64 * bt::kGemvWaves) void gemv_kernel(GemvDesc d) {
     extern __shared__ __attribute__((aligned(16))) int8_t gemv_lds[];
-    gemv_block(d, blockIdx.x, gemv_lds);
+    __shared__ GemvShared sh;
+    gemv_block<kFused>(d, blockIdx.x, gemv_lds, sh);
 }
 
+template <bool kFused>
 __global__ __launch_bounds__(64 * bt::kGemvWaves) void gemv_grouped_kernel(
     const GemvDesc* __restrict__ descs, int32_t count) {
     extern __shared__ __attribute__((aligned(16))) int8_t gemv_lds[];
+    __shared__ GemvShared sh;
     const int64_t b = blockIdx.x;
     int lo = 0, hi = count - 1;
     while (lo < hi) {
@@ -426,7 +536,7 @@ __global__ __launch_bounds__(64 * bt::kGemvWaves) void gemv_grouped_kernel(
         if (descs[mid].block_begin <= b) lo = mid; else hi = mid - 1;
     }
     const GemvDesc d = descs[lo];
-    gemv_block(d, b - d.block_begin, gemv_lds);
+    gemv_block<kFused>(d, b - d.block_begin, gemv_lds, sh);
 }
 
 size_t gemv_lds_bytes(const GemvDesc& d) { return size_t(d.M + 1) * size_t(d.lds_row); }
@@ -564,6 +674,47 @@ extern "C" bt_status bt_quantize_act(const float* x, int64_t M, int64_t K, int8_
     return launched();
 }
 
+// Fills the split-K workspace pointers of a single-call GEMV.
+static bt_status gemv_bind_workspace(GemvDesc& d, void* workspace, size_t workspace_bytes) {
+    const size_t need = bt::gemv_workspace_bytes(d);
+    if (!need) return BT_OK;
+    if (!workspace || workspace_bytes < need) return BT_ERR_WORKSPACE;
+    if (!bt::aligned16(workspace)) return BT_ERR_ALIGN;
+    d.ws = static_cast<int32_t*>(workspace);
+    d.cnt = reinterpret_cast<uint32_t*>(static_cast<char*>(workspace) + bt::gemv_partial_bytes(d));
+    return BT_OK;
+}
+
+extern "C" bt_status bt_ternary_matmul_fused(int64_t M, int64_t N, int64_t K, const float* x,
+                                             const void* wdev, float w_scale, float* y,
+                                             int32_t* acc, int8_t* xq, float* xscale,
+                                             int32_t* xsum, void* workspace,
+                                             size_t workspace_bytes, hipStream_t stream) {
+    if (!x || !wdev || !y) return BT_ERR_NULL;
+    if (M < 1 || M > BT_GEMV_MAX_M || !nk_ok(N, K)) return BT_ERR_SHAPE;
+    if (!bt::aligned16(x) || !bt::aligned16(wdev) || !bt::aligned16(y) ||
+        (acc && !bt::aligned16(acc)) || (xq && !bt::aligned16(xq)) ||
+        (xscale && !bt::aligned16(xscale)) || (xsum && !bt::aligned16(xsum)))
+        return BT_ERR_ALIGN;
+    if (!isfinite(w_scale)) return BT_ERR_VALUE;
+    GemvDesc d;
+    bt::gemv_shape(M, N, K, false, &d);
+    const bt_status st = gemv_bind_workspace(d, workspace, workspace_bytes);
+    if (st != BT_OK) return st;
+    d.x = x;
+    d.xq = xq;
+    d.xscale = xscale;
+    d.xsum = xsum;
+    d.w = static_cast<const uint8_t*>(wdev);
+    d.y = y;
+    d.acc = acc;
+    d.w_scale = w_scale;
+    (void)hipGetLastError();
+    hipLaunchKernelGGL(gemv_kernel<true>, dim3(unsigned(d.blocks)), dim3(64 * bt::kGemvWaves),
+                       gemv_lds_bytes(d), stream, d);
+    return launched();
+}
+
 extern "C" bt_status bt_ternary_matmul(int64_t M, int64_t N, int64_t K, const int8_t* xq,
                                        const float* xscale, const int32_t* xsum, const void* wdev,
                                        float w_scale, float* y, int32_t* acc, void* workspace,
@@ -577,23 +728,17 @@ extern "C" bt_status bt_ternary_matmul(int64_t M, int64_t N, int64_t K, const in
     if (M <= BT_GEMV_MAX_M) {
         GemvDesc d;
         bt::gemv_shape(M, N, K, false, &d);
-        const size_t need = bt::gemv_workspace_bytes(d);
-        if (need) {
-            if (!workspace || workspace_bytes < need) return BT_ERR_WORKSPACE;
-            if (!bt::aligned16(workspace)) return BT_ERR_ALIGN;
-            d.ws = static_cast<int32_t*>(workspace);
-            d.cnt = reinterpret_cast<uint32_t*>(static_cast<char*>(workspace) +
-                                                bt::gemv_partial_bytes(d));
-        }
-        d.xq = xq;
-        d.xscale = xscale;
-        d.xsum = xsum;
+        const bt_status st = gemv_bind_workspace(d, workspace, workspace_bytes);
+        if (st != BT_OK) return st;
+        d.xq = const_cast<int8_t*>(xq);
+        d.xscale = const_cast<float*>(xscale);
+        d.xsum = const_cast<int32_t*>(xsum);
         d.w = static_cast<const uint8_t*>(wdev);
         d.y = y;
         d.acc = acc;
         d.w_scale = w_scale;
         (void)hipGetLastError();
-        hipLaunchKernelGGL(gemv_kernel, dim3(unsigned(d.blocks)), dim3(64 * bt::kGemvWaves),
+        hipLaunchKernelGGL(gemv_kernel<false>, dim3(unsigned(d.blocks)), dim3(64 * bt::kGemvWaves),
                            gemv_lds_bytes(d), stream, d);
         return launched();
     }
@@ -636,7 +781,8 @@ extern "C" bt_status bt_ternary_matmul_grouped(const void* plan_host, const void
                                                hipStream_t stream) {
     if (!plan_host || !plan_dev) return BT_ERR_NULL;
     const auto* hdr = static_cast<const bt::PlanHeader*>(plan_host);
-    if (hdr->magic != bt::kPlanMagicGemv || hdr->count < 1) return BT_ERR_VALUE;
+    const bool fused = hdr->magic == bt::kPlanMagicGemvFused;
+    if ((!fused && hdr->magic != bt::kPlanMagicGemv) || hdr->count < 1) return BT_ERR_VALUE;
     if (!bt::aligned16(plan_dev)) return BT_ERR_ALIGN;
     const auto* host_descs = reinterpret_cast<const GemvDesc*>(hdr + 1);
     size_t lds = 0;
@@ -644,7 +790,11 @@ extern "C" bt_status bt_ternary_matmul_grouped(const void* plan_host, const void
     const auto* descs = reinterpret_cast<const GemvDesc*>(static_cast<const char*>(plan_dev) +
                                                           sizeof(bt::PlanHeader));
     (void)hipGetLastError();
-    hipLaunchKernelGGL(gemv_grouped_kernel, dim3(unsigned(hdr->total_blocks)),
-                       dim3(64 * bt::kGemvWaves), lds, stream, descs, hdr->count);
+    if (fused)
+        hipLaunchKernelGGL(gemv_grouped_kernel<true>, dim3(unsigned(hdr->total_blocks)),
+                           dim3(64 * bt::kGemvWaves), lds, stream, descs, hdr->count);
+    else
+        hipLaunchKernelGGL(gemv_grouped_kernel<false>, dim3(unsigned(hdr->total_blocks)),
+                           dim3(64 * bt::kGemvWaves), lds, stream, descs, hdr->count);
     return launched();
 }

@@ -158,6 +158,37 @@ def ternary_matmul(xq, xscale, xsum, wdev, n: int, w_scale: float, y=None, acc=N
     return (y, acc) if (want_acc or acc is not None) else y
 
 
+def ternary_matmul_fused(x, wdev, n: int, w_scale: float, y=None, acc=None, xq=None,
+                         xscale=None, xsum=None, workspace=None, want_acc=False, stream=None):
+    """Quantize x and multiply in one launch (bt_ternary_matmul_fused, M <= 16).
+
+    xq, xscale, xsum are optional outputs (same values as quantize_act).
+    """
+    torch = _torch()
+    _dev(x, torch.float32, None, "x")
+    m, k = x.shape
+    _dev(wdev, torch.uint8, (repacked_bytes(n, k),), "wdev")
+    if y is None:
+        y = torch.empty((m, n), dtype=torch.float32, device=x.device)
+    _dev(y, torch.float32, (m, n), "y")
+    if acc is None and want_acc:
+        acc = torch.empty((m, n), dtype=torch.int32, device=x.device)
+    for t, dt, shp, name in ((acc, torch.int32, (m, n), "acc"), (xq, torch.int8, (m, k), "xq"),
+                             (xscale, torch.float32, (m,), "xscale"),
+                             (xsum, torch.int32, (m,), "xsum")):
+        if t is not None:
+            _dev(t, dt, shp, name)
+    need = matmul_workspace_bytes(m, n, k)
+    if need and workspace is None:
+        workspace = new_workspace(m, n, k, x.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    check(lib().bt_ternary_matmul_fused(m, n, k, _ptr(x), _ptr(wdev), float(w_scale), _ptr(y),
+                                        _ptr(acc), _ptr(xq), _ptr(xscale), _ptr(xsum),
+                                        _ptr(workspace), ws_bytes, _stream(stream)),
+          "bt_ternary_matmul_fused")
+    return (y, acc) if (want_acc or acc is not None) else y
+
+
 # ------------------------------------------------------------------ grouped
 
 class _Plan:
@@ -197,20 +228,22 @@ class QuantPlan(_Plan):
 class MatmulPlan(_Plan):
     """Many independent GEMVs (M <= 16) in one launch (bt_ternary_matmul_grouped).
 
-    items: sequence of dicts with keys xq, xscale, xsum, wdev, n, w_scale, y,
-    and optionally acc.
+    items: sequence of dicts with keys wdev, n, w_scale, y, optionally acc, and
+    either xq, xscale, xsum (quantized inputs) or x (fp32 activations quantized
+    inside the launch; xq, xscale, xsum then optional outputs).
     """
 
     def __init__(self, items):
         descs = (BtMatmulDesc * len(items))()
         self._keep = list(items)
         for i, it in enumerate(items):
-            m, k = it["xq"].shape
-            descs[i] = BtMatmulDesc(m, it["n"], k, _ptr(it["xq"]), _ptr(it["xscale"]),
-                                    _ptr(it["xsum"]), _ptr(it["wdev"]), float(it["w_scale"]),
-                                    _ptr(it["y"]), _ptr(it.get("acc")))
+            src = it.get("x")
+            m, k = (src if src is not None else it["xq"]).shape
+            descs[i] = BtMatmulDesc(m, it["n"], k, _ptr(it.get("xq")), _ptr(it.get("xscale")),
+                                    _ptr(it.get("xsum")), _ptr(it["wdev"]), float(it["w_scale"]),
+                                    _ptr(it["y"]), _ptr(it.get("acc")), _ptr(src))
         torch = _torch()
-        dev = items[0]["xq"].device
+        dev = items[0]["y"].device
         ws_bytes = int(lib().bt_matmul_plan_workspace_bytes(descs, len(items)))
         self.workspace = torch.zeros(ws_bytes, dtype=torch.uint8, device=dev) if ws_bytes else None
         nbytes = int(lib().bt_matmul_plan_bytes(len(items)))
@@ -227,5 +260,6 @@ class MatmulPlan(_Plan):
 __all__ = [
     "BtError", "GROUP_K", "GEMV_MAX_M", "packed_bytes", "repacked_bytes",
     "matmul_workspace_bytes", "pack_ternary", "unpack_ternary", "repack_ternary",
-    "quantize_act", "new_workspace", "ternary_matmul", "QuantPlan", "MatmulPlan",
+    "quantize_act", "new_workspace", "ternary_matmul", "ternary_matmul_fused", "QuantPlan",
+    "MatmulPlan",
 ]

@@ -303,3 +303,105 @@ def test_grouped_decode_layers(dev):
             assert_exact(f"q[{i}]", it["xq"].cpu().numpy(), ref["q"])
             assert_exact(f"acc[{i}]", it["acc"].cpu().numpy(), ref["acc"])
             assert_rel(f"y[{i}]", it["y"].cpu().numpy(), ref["y"])
+
+
+# ------------------------------------------------------- fused quantization
+
+def run_fused(c, dev, with_outputs=True, wdev=None):
+    x, w, s = c["x"], c["w"], c["w_scale"]
+    m, k = x.shape
+    n = w.shape[0]
+    if wdev is None:
+        wdev = load_weights(w, dev)
+    y = torch.full((m, n), float("nan"), dtype=torch.float32, device=dev)
+    acc = torch.full((m, n), POISON_I32, dtype=torch.int32, device=dev)
+    outs = (None, None, None)
+    if with_outputs:
+        outs = (torch.full((m, k), 99, dtype=torch.int8, device=dev),
+                torch.full((m,), float("nan"), dtype=torch.float32, device=dev),
+                torch.full((m,), POISON_I32, dtype=torch.int32, device=dev))
+    bt.ternary_matmul_fused(to_dev(x, dev), wdev, n, s, y=y, acc=acc, xq=outs[0], xscale=outs[1],
+                            xsum=outs[2])
+    torch.cuda.synchronize()
+    return y, acc, outs
+
+
+@pytest.mark.parametrize("m,n,k", [(1, 1536, 1536), (1, 40, 384), (3, 17920, 1536),
+                                   (4, 1536, 8960), (16, 200, 640), (2, 1, 128), (7, 2048, 8960)])
+def test_fused_quantize_gemv(dev, m, n, k):
+    c = synth.small_problem(7, m, n, k, "outlier")
+    ref = oracle.forward_ref(c["x"], c["w"], c["w_scale"], "f64")
+    y, acc, (xq, xs, xsum) = run_fused(c, dev)
+    assert_exact("q", xq.cpu().numpy(), ref["q"])
+    assert_exact("d", xs.cpu().numpy(), ref["d"])
+    assert_exact("qsum", xsum.cpu().numpy(), ref["qsum"])
+    assert_exact("acc", acc.cpu().numpy(), ref["acc"])
+    assert_rel("y", y.cpu().numpy(), ref["y"])
+
+
+def test_fused_without_optional_outputs_and_zero_rows(dev):
+    c = synth.small_problem(8, 5, 300, 1536, "t3")
+    c["x"][2] = 0
+    ref = oracle.forward_ref(c["x"], c["w"], c["w_scale"], "f64")
+    y, acc, _ = run_fused(c, dev, with_outputs=False)
+    assert_exact("acc", acc.cpu().numpy(), ref["acc"])
+    assert_rel("y", y.cpu().numpy(), ref["y"])
+    assert (y.cpu().numpy()[2] == 0).all()
+
+
+def _grouped_items(cases, dev, fused):
+    items, refs = [], []
+    for c in cases:
+        m, k = c["x"].shape
+        n = c["w"].shape[0]
+        it = {"wdev": load_weights(c["w"], dev), "n": n, "w_scale": c["w_scale"],
+              "y": torch.full((m, n), float("nan"), dtype=torch.float32, device=dev),
+              "acc": torch.full((m, n), POISON_I32, dtype=torch.int32, device=dev),
+              "xq": torch.full((m, k), 99, dtype=torch.int8, device=dev),
+              "xscale": torch.full((m,), float("nan"), dtype=torch.float32, device=dev),
+              "xsum": torch.full((m,), POISON_I32, dtype=torch.int32, device=dev)}
+        if fused:
+            it["x"] = to_dev(c["x"], dev)
+        else:
+            bt.quantize_act(to_dev(c["x"], dev), it["xq"], it["xscale"], it["xsum"])
+        items.append(it)
+        refs.append(oracle.forward_ref(c["x"], c["w"], c["w_scale"], "f64"))
+    return items, refs
+
+
+def _check_grouped(items, refs):
+    for i, (it, ref) in enumerate(zip(items, refs)):
+        assert_exact(f"q[{i}]", it["xq"].cpu().numpy(), ref["q"])
+        assert_exact(f"d[{i}]", it["xscale"].cpu().numpy(), ref["d"])
+        assert_exact(f"qsum[{i}]", it["xsum"].cpu().numpy(), ref["qsum"])
+        assert_exact(f"acc[{i}]", it["acc"].cpu().numpy(), ref["acc"])
+        assert_rel(f"y[{i}]", it["y"].cpu().numpy(), ref["y"])
+
+
+@pytest.mark.parametrize("fused", [False, True])
+def test_grouped_fused_decode_layers(dev, fused):
+    cases = [synth.decode_problem(layer, proj) for layer in (0, 13) for proj in range(4)]
+    items, refs = _grouped_items(cases, dev, fused)
+    plan = bt.MatmulPlan(items)
+    for _ in range(2):
+        plan.launch()
+        torch.cuda.synchronize()
+        _check_grouped(items, refs)
+
+
+@pytest.mark.parametrize("fused", [False, True])
+def test_grouped_mixed_m_with_lds_split(dev, fused):
+    # M = 16 rows of K = 8960 do not fit one LDS slice, so that projection is
+    # split along K inside the grouped launch and uses the plan's workspace
+    cases = [synth.small_problem(9, 16, 1536, 8960), synth.small_problem(9, 1, 2048, 1536),
+             synth.small_problem(9, 3, 40, 384, "t3"), synth.small_problem(9, 5, 17920, 1536)]
+    items, refs = _grouped_items(cases, dev, fused)
+    plan = bt.MatmulPlan(items)
+    assert plan.workspace is not None
+    for _ in range(3):
+        for it in items:
+            it["y"].fill_(float("nan"))
+        plan.launch()
+        torch.cuda.synchronize()
+        _check_grouped(items, refs)
+    assert int(plan.workspace.count_nonzero()) == 0

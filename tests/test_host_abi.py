@@ -47,7 +47,7 @@ def test_library_exports_every_declared_symbol():
 def test_struct_layouts_match_header_sizes():
     # two int64 + pointer fields; no padding surprises between C and ctypes
     assert C.sizeof(BtQuantDesc) == 6 * 8
-    assert C.sizeof(BtMatmulDesc) == 3 * 8 + 4 * 8 + 8 + 2 * 8
+    assert C.sizeof(BtMatmulDesc) == 3 * 8 + 4 * 8 + 8 + 3 * 8
 
 
 def test_status_strings():
@@ -140,6 +140,15 @@ def test_device_entry_points_validate_before_launch():
     assert L.bt_ternary_matmul(*args(N=1536, K=1536)) == WORKSPACE
     assert L.bt_ternary_matmul(*args(N=1536, K=1536, ws=f, wsb=need - 1)) == WORKSPACE
     assert L.bt_ternary_matmul(*args(N=1536, K=1536, ws=f + 4, wsb=need)) == ALIGN
+    # fused quantize + GEMV: x, wdev, y required; q outputs optional; M <= 16
+    fa = lambda **kw: [kw.get("M", 1), kw.get("N", 16), kw.get("K", 128), kw.get("x", f),
+                       kw.get("w", f), kw.get("scale", 0.5), kw.get("y", f), None,
+                       kw.get("xq", None), None, None, kw.get("ws", None), kw.get("wsb", 0), None]
+    assert L.bt_ternary_matmul_fused(*fa(x=None)) == NULL
+    assert L.bt_ternary_matmul_fused(*fa(M=17)) == SHAPE
+    assert L.bt_ternary_matmul_fused(*fa(xq=f + 1)) == ALIGN
+    assert L.bt_ternary_matmul_fused(*fa(scale=float("inf"))) == VALUE
+    assert L.bt_ternary_matmul_fused(*fa(N=1536, K=1536)) == WORKSPACE
 
 
 def test_plan_building_on_host():
@@ -174,6 +183,17 @@ def test_plan_building_on_host():
     assert need > 0
     assert L.bt_matmul_plan_build(m, 2, None, 0, host.ctypes.data, nb) == WORKSPACE
     assert L.bt_matmul_plan_build(m, 2, f, need, host.ctypes.data, nb) == OK
+    # a plan fuses quantization for all its projections or for none
+    m[0].x = f
+    assert L.bt_matmul_plan_build(m, 2, f, need, host.ctypes.data, nb) == VALUE
+    m[1].x = f
+    m[0].xq = m[0].xscale = m[0].xsum = None        # optional outputs when fused
+    assert L.bt_matmul_plan_build(m, 2, f, need, host.ctypes.data, nb) == OK
+    # the longest workgroups (K = 8960) are placed first in the grid
+    assert host[:4].view(np.uint32)[0] == 0x42544646      # a fused plan
+    # GemvDesc: 9 pointers, w_scale, then M, N, K as int32 (K at byte 84)
+    first_k = host[16 + 84:16 + 88].view(np.int32)[0]
+    assert first_k == 8960
     # a launch with a plan of the wrong kind is refused on the host
     assert L.bt_quantize_act_grouped(host.ctypes.data, f, None) == VALUE
 
