@@ -29,6 +29,8 @@
 #include <float.h>
 #include <math.h>
 
+#include <string.h>
+
 #include <algorithm>
 
 #include "bt_internal.h"
@@ -80,6 +82,18 @@ __device__ __forceinline__ T gld_stream(const void* p) {
 template <typename T>
 __device__ __forceinline__ void gst(void* p, T v) {
     *(BT_GLOBAL T*)p = v;
+}
+
+// Buffer resources (base and size in SGPRs): a load takes a per-lane VGPR
+// offset plus a scalar offset, and any byte past the size reads as zero.
+constexpr int kBufferFlags = 0x00020000;   // gfx9 buffer resource word 3
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, int(bytes), kBufferFlags);
+}
+
+__device__ __forceinline__ v4u buf_ld16u(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+    return __builtin_bit_cast(v4u, __builtin_amdgcn_raw_buffer_load_b128(r, int(voff), int(soff), 0));
 }
 
 template <typename T>
@@ -311,14 +325,13 @@ __device__ __forceinline__ v4i gemv_consume(const GemvBatch& b, int n, const int
 
 struct GemvShared {
     QuantShared red;
-    float d[BT_GEMV_MAX_M];      // fused quantization: per-token scale
-    int32_t qs[BT_GEMV_MAX_M];   // fused quantization: per-token sum of q
+    float d[BT_GEMV_MAX_M];      // per-token scale d_m
+    int32_t qs[BT_GEMV_MAX_M];   // per-token sum of q
 };
 
 // Epilogue of one tile. With K split into chunks, partial sums meet in the
 // workspace (int32 addition is exact in any order) and the last chunk to
 // arrive reads the total, clears the workspace and finishes the tile.
-template <bool kFused>
 __device__ __forceinline__ void gemv_finish(const GemvDesc& d, int64_t tile, v4i c, int lane,
                                             const GemvShared& sh) {
     const int kq = lane >> 4;
@@ -348,8 +361,8 @@ __device__ __forceinline__ void gemv_finish(const GemvDesc& d, int64_t tile, v4i
         for (int i = 0; i < 4; ++i) {
             const int mm = 4 * kq + i;
             if (mm < d.M) {
-                const int32_t qsum = kFused ? sh.qs[mm] : gld<int32_t>(d.xsum + mm);
-                const float dm = kFused ? sh.d[mm] : gld<float>(d.xscale + mm);
+                const int32_t qsum = sh.qs[mm];
+                const float dm = sh.d[mm];
                 const int32_t acc = c[i] - qsum;
                 const float rs = dm * d.w_scale;
                 gst<float>(d.y + int64_t(mm) * d.N + n, float(acc) * rs);
@@ -484,6 +497,11 @@ __device__ __forceinline__ void gemv_block(const GemvDesc& d, int64_t local_bloc
             if (m < d.M && kbeg + col < d.K) v = gld<v4i>(d.xq + int64_t(m) * d.K + kbeg + col);
             lds_st<v4i>(lds + m * d.lds_row + col, v);
         }
+        // the epilogue's per-token scale and row sum, read once
+        if (tid < d.M) {
+            sh.d[tid] = gld<float>(d.xscale + tid);
+            sh.qs[tid] = gld<int32_t>(d.xsum + tid);
+        }
         __syncthreads();
     }
 
@@ -497,13 +515,13 @@ __device__ __forceinline__ void gemv_block(const GemvDesc& d, int64_t local_bloc
         if (t >= d.tiles) return;
         cur = gemv_consume(b, min(kB, nsteps - bb * kB), abase + bb * kB * 256, cur);
         if (bb == nb - 1) {
-            gemv_finish<kFused>(d, t, cur, lane, sh);
+            gemv_finish(d, t, cur, lane, sh);
             cur = v4i{0, 0, 0, 0};
         }
     };
 
-    // The scheduling barriers keep the unpacking of batch 1 below the use of
-    // batch 0.
+    // Two items are in flight, then consumed. The scheduling barriers keep the
+    // unpacking of batch 1 below the use of batch 0.
     for (int idx = 0; idx < total; idx += 2) {
         if (idx > 0) {
             issue(b0, idx);
@@ -542,10 +560,25 @@ __global__ __launch_bounds__(64 * bt::kGemvWaves) void gemv_grouped_kernel(
 size_t gemv_lds_bytes(const GemvDesc& d) { return size_t(d.M + 1) * size_t(d.lds_row); }
 
 // -------------------------------------------------------------------- GEMM
-
-constexpr int kBM = 128;
-constexpr int kBN = 128;
-constexpr int kALds = bt::kSuperK + 16;   // padded LDS row: 16 lanes hit distinct banks
+//
+// Prefill GEMM for M > 16. A workgroup of WGM x WGN waves computes a
+// (WA*WGM) x (WW*WGN) tile of y (token rows x weight rows); each wave owns a
+// WA x WW sub-tile held as (WA/16) x (WW/16) MFMA accumulators.
+//
+// K advances in 256-wide stages. The workgroup's activation rows for a stage
+// (BM x 256 int8) are copied from global memory straight into one of two LDS
+// buffers (buffer_load ... lds: no staging registers), while the other
+// buffer feeds the matrix cores. Rows past M, and columns past K, read as
+// zero through the buffer bounds. In LDS a row's sixteen 16-byte chunks are
+// stored XOR-swizzled (chunk c of row r at slot c ^ (r % 16)), so the 16 rows
+// an MFMA fragment read touches fall in 16 different bank groups. Each wave
+// keeps its WW/16 weight tiles' packed words for the next stage in registers
+// (one 128-bit load per tile and lane) and unpacks each 16-element word right
+// before the WA/16 MFMAs that use it.
+//
+// Workgroup order: consecutive workgroup ids go to different XCDs, so ids are
+// remapped to give each XCD a contiguous band of output tiles (whole rows of
+// tiles along N): the activation rows of a band stay in that XCD's L2.
 
 struct GemmArgs {
     const int8_t* xq;
@@ -555,85 +588,208 @@ struct GemmArgs {
     float* y;
     int32_t* acc;
     float w_scale;
-    int32_t M, N, K, tiles, steps;
+    int32_t M, N, K, tiles, steps;   // steps: 256-wide stages (Kp / 256)
+    int32_t m_tiles, n_tiles, per_xcd;
 };
 
-// 128 x 128 output tile per workgroup, 4 waves as 2 x 2, each wave 64 x 64 =
-// 4 x 4 MFMA blocks. Per 256-wide K step the activation tile (128 x 256 int8,
-// zero past M and K) is staged in LDS and each wave loads the packed words of
-// its four 16-row weight tiles straight from global memory (one 128-bit load
-// per tile), unpacking them in registers.
-__global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g) {
-    __shared__ __attribute__((aligned(16))) int8_t As[kBM * kALds];
+constexpr int kXcds = 8;
+
+__device__ __forceinline__ void lds_dma16(__amdgpu_buffer_rsrc_t r, int8_t* lds_wave_base,
+                                          uint32_t voff, uint32_t soff) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (BT_LDS void*)lds_wave_base, 16, int(voff),
+                                              int(soff), 0, 0);
+}
+
+template <int WA, int WW, int WGM, int WGN>
+__global__ __launch_bounds__(64 * WGM * WGN) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void gemm_kernel(GemmArgs g) {
+    constexpr int BM = WA * WGM;
+    constexpr int BN = WW * WGN;
+    constexpr int NW = WGM * WGN;
+    constexpr int TA = WA / 16;   // MFMA blocks along tokens per wave
+    constexpr int TW = WW / 16;   // MFMA blocks (16-row weight tiles) per wave
+    constexpr int kStage = BM * 256;                 // LDS bytes per activation stage
+    constexpr int kDmaPerWave = BM * 16 / 64 / NW;   // 1 KB copies per wave per stage
+    static_assert(kDmaPerWave * 64 * NW == BM * 16, "A stage must split evenly over waves");
+    __shared__ __attribute__((aligned(16))) int8_t As[2 * kStage];
+
+    const int xcd = blockIdx.x % kXcds;
+    const int tile_id = xcd * g.per_xcd + blockIdx.x / kXcds;
+    if (tile_id >= g.m_tiles * g.n_tiles) return;
+    const int mt = tile_id / g.n_tiles;
+    const int nt = tile_id - mt * g.n_tiles;
+
     const int tid = threadIdx.x;
-    const int wave = tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lane = tid & 63;
-    const int wm = wave >> 1;
-    const int wn = wave & 1;
-    const int64_t m0 = int64_t(blockIdx.y) * kBM;
-    const int n0 = blockIdx.x * kBN;
-    const int t0 = n0 / bt::kTileN + wn * 4;
-    const int64_t tile_bytes = int64_t(g.steps) * 1024;
+    const int wm = wave / WGN;
+    const int wn = wave - wm * WGN;
+    const int64_t m0 = int64_t(mt) * BM;
+    const int n0 = nt * BN;
+    const int t0 = min(n0 / bt::kTileN + wn * TW, g.tiles - 1);
+    const uint32_t tile_bytes = uint32_t(g.steps) * 1024u;
+    const int nst = g.steps;
 
-    v4i acc[4][4];
+    // This wave's weight tiles as one buffer; tiles past N read as zero.
+    const __amdgpu_buffer_rsrc_t wrsrc =
+        make_rsrc(g.w + int64_t(t0) * tile_bytes, uint32_t(min(TW, g.tiles - t0)) * tile_bytes);
+    auto load_b = [&](v4u (&b)[TW], int s) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = v4i{0, 0, 0, 0};
+        for (int t = 0; t < TW; ++t)
+            b[t] = buf_ld16u(wrsrc, uint32_t(lane) * 16u, uint32_t(t) * tile_bytes + uint32_t(s) * 1024u);
+    };
 
-    for (int S = 0; S < g.steps; ++S) {
-        v4u wb[4];
+    // The workgroup's activation rows as one buffer; rows past M read as zero.
+    const uint32_t arows = uint32_t(min(int64_t(BM), int64_t(g.M) - m0));
+    const __amdgpu_buffer_rsrc_t arsrc = make_rsrc(g.xq + m0 * g.K, arows * uint32_t(g.K));
+    // Copy j of this wave fills LDS slots p = (wave*kDmaPerWave + j)*64 + lane:
+    // row r = p / 16 = r0 + 4j, swizzled chunk p % 16 = lane % 16, logical
+    // chunk c = (lane % 16) ^ (r % 16), which depends on j only through j % 4.
+    // So four per-lane offsets serve every copy; the 4jK row step is scalar.
+    const int r0 = wave * kDmaPerWave * 4 + (lane >> 4);
+    uint32_t avoff[4];
+    bool ahigh[4];   // logical chunk in the upper half of the stage (past K on a 128-wide tail)
 #pragma unroll
-        for (int tn = 0; tn < 4; ++tn) {
-            const int t = min(t0 + tn, g.tiles - 1);   // past-N tiles are never stored
-            wb[tn] = gld<v4u>(g.w + int64_t(t) * tile_bytes + int64_t(S) * 1024 + lane * 16);
+    for (int q = 0; q < 4; ++q) {
+        const int c = (lane & 15) ^ ((r0 + 4 * q) & 15);
+        avoff[q] = uint32_t(r0) * uint32_t(g.K) + uint32_t(c) * 16u;
+        ahigh[q] = c >= 8;
+    }
+    const bool tail128 = (g.K & 255) != 0;
+    auto load_a = [&](int buf, int s) {
+        const uint32_t kcol = uint32_t(s) * 256u;
+        const bool last_tail = tail128 && s == nst - 1;
+#pragma unroll
+        for (int j = 0; j < kDmaPerWave; ++j) {
+            // a chunk past K must read zero, not the next row: push it out of bounds
+            const uint32_t voff = (last_tail && ahigh[j & 3]) ? 0xfffffff0u : avoff[j & 3];
+            lds_dma16(arsrc, As + buf * kStage + (wave * kDmaPerWave + j) * 1024, voff,
+                      kcol + uint32_t(4 * j) * uint32_t(g.K));
         }
-        __syncthreads();
-        constexpr int cpr = bt::kSuperK / 16;   // 16-byte chunks per row
-        for (int ch = tid; ch < kBM * cpr; ch += 256) {
-            const int r = ch / cpr;
-            const int col = (ch - r * cpr) * 16;
-            const int64_t gm = m0 + r;
-            const int64_t k = int64_t(S) * bt::kSuperK + col;
-            v4i v = {0, 0, 0, 0};
-            if (gm < g.M && k < g.K) v = gld<v4i>(g.xq + gm * g.K + k);
-            lds_st<v4i>(As + r * kALds + col, v);
+    };
+
+    // The MFMA runs transposed: A = weight fragment, B = activation fragment,
+    // so C[n][m] and a lane holds 4 consecutive weight rows (outputs n) of one
+    // token m, which the epilogue writes as one 16-byte store.
+    v4i acc[TA][TW];
+#pragma unroll
+    for (int i = 0; i < TA; ++i)
+#pragma unroll
+        for (int t = 0; t < TW; ++t) acc[i][t] = v4i{0, 0, 0, 0};
+
+    // fragment reads: row (wm*WA + 16i + lane%16), logical chunk 4jj + lane/16,
+    // swizzled with (row % 16) = lane % 16
+    const int8_t* afrag = As + (wm * WA + (lane & 15)) * 256;
+    int aslot[4];
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) aslot[jj] = ((4 * jj + (lane >> 4)) ^ (lane & 15)) * 16;
+
+    auto stage = [&](int s, const v4u (&bc)[TW], v4u (&bn)[TW]) {
+        const int cur = s & 1;
+        const bool more = s + 1 < nst;
+        if (more) {
+            load_a(cur ^ 1, s + 1);
+            load_b(bn, s + 1);
         }
-        __syncthreads();
+        asm volatile("" ::: "memory");
+        const int8_t* abuf = afrag + cur * kStage;
 #pragma unroll
         for (int jj = 0; jj < 4; ++jj) {
-            v4i bf[4];
+            v4i af[TA];
 #pragma unroll
-            for (int tn = 0; tn < 4; ++tn) bf[tn] = unpack16(wb[tn][jj]);
+            for (int i = 0; i < TA; ++i) af[i] = lds_ld<v4i>(abuf + i * 16 * 256 + aslot[jj]);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const v4i af = lds_ld<v4i>(
-                    As + (wm * 64 + 16 * i + (lane & 15)) * kALds + 64 * jj + 16 * (lane >> 4));
+            for (int t = 0; t < TW; ++t) {
+                const v4i bf = unpack16(bc[t][jj]);
 #pragma unroll
-                for (int tn = 0; tn < 4; ++tn) acc[i][tn] = mfma16x16x64(af, bf[tn], acc[i][tn]);
+                for (int i = 0; i < TA; ++i) acc[i][t] = mfma16x16x64(bf, af[i], acc[i][t]);
             }
         }
+        // the next stage's LDS copies and weight words must have landed
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+    };
+
+    v4u b0[TW], b1[TW];
+    load_a(0, 0);
+    load_b(b0, 0);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    for (int s = 0; s < nst; s += 2) {
+        stage(s, b0, b1);
+        if (s + 1 < nst) stage(s + 1, b1, b0);
     }
 
+    // epilogue: acc[i][t][r] = C[n = n0 + wn*WW + 16t + 4(l/16) + r][m = m0 + wm*WA + 16i + l%16]
+    const int nq = n0 + wn * WW + 4 * (lane >> 4);
+    const bool full = m0 + BM <= g.M && n0 + BN <= g.N && (g.N & 3) == 0;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < TA; ++i) {
+        const int64_t mm = m0 + wm * WA + 16 * i + (lane & 15);
+        if (!full && mm >= g.M) continue;
+        const int32_t qs = gld<int32_t>(g.xsum + mm);
+        const float rs = gld<float>(g.xscale + mm) * g.w_scale;
+        float* yrow = g.y + mm * g.N;
+        int32_t* arow = g.acc ? g.acc + mm * g.N : nullptr;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int64_t mm = m0 + wm * 64 + 16 * i + 4 * (lane >> 4) + r;
-            if (mm >= g.M) continue;
-            const int32_t qs = gld<int32_t>(g.xsum + mm);
-            const float rs = gld<float>(g.xscale + mm) * g.w_scale;
+        for (int t = 0; t < TW; ++t) {
+            const int n = nq + 16 * t;
+            const v4i a = acc[i][t] - qs;
+            const v4f yv = {float(a.x) * rs, float(a.y) * rs, float(a.z) * rs, float(a.w) * rs};
+            if (full) {
+                __builtin_nontemporal_store(yv, (BT_GLOBAL v4f*)(yrow + n));
+                if (arow) __builtin_nontemporal_store(a, (BT_GLOBAL v4i*)(arow + n));
+            } else {
 #pragma unroll
-            for (int tn = 0; tn < 4; ++tn) {
-                const int n = n0 + wn * 64 + 16 * tn + (lane & 15);
-                if (n < g.N) {
-                    const int32_t a = acc[i][tn][r] - qs;
-                    gst<float>(g.y + mm * g.N + n, float(a) * rs);
-                    if (g.acc) gst<int32_t>(g.acc + mm * g.N + n, a);
+                for (int r = 0; r < 4; ++r) {
+                    if (n + r < g.N) {
+                        gst<float>(yrow + n + r, yv[r]);
+                        if (arow) gst<int32_t>(arow + n + r, a[r]);
+                    }
                 }
             }
         }
     }
+}
+
+#ifndef BT_GEMM_WA
+#define BT_GEMM_WA 64
+#endif
+#ifndef BT_GEMM_WW
+#define BT_GEMM_WW 128
+#endif
+#ifndef BT_GEMM_WGM
+#define BT_GEMM_WGM 2
+#endif
+#ifndef BT_GEMM_WGN
+#define BT_GEMM_WGN 2
+#endif
+
+// Shape dispatch of the GEMM: the default tile, or a 128 x 128 tile (waves of
+// 64 x 64) when the default leaves fewer than two workgroups per compute unit
+// (e.g. 4096 x 1536 outputs).
+template <int WA, int WW, int WGM, int WGN>
+bt_status launch_gemm(GemmArgs g, hipStream_t stream) {
+    constexpr int BM = WA * WGM;
+    constexpr int BN = WW * WGN;
+    g.m_tiles = int32_t(bt::ceil_div(g.M, BM));
+    g.n_tiles = int32_t(bt::ceil_div(g.N, BN));
+    const int64_t total = int64_t(g.m_tiles) * g.n_tiles;
+    g.per_xcd = int32_t(bt::ceil_div(total, kXcds));
+    const int64_t grid = int64_t(g.per_xcd) * kXcds;
+    if (grid > (int64_t(1) << 31) - 1) return BT_ERR_SHAPE;
+    (void)hipGetLastError();
+    hipLaunchKernelGGL((gemm_kernel<WA, WW, WGM, WGN>), dim3(unsigned(grid)),
+                       dim3(64 * WGM * WGN), 0, stream, g);
+    return hipGetLastError() == hipSuccess ? BT_OK : BT_ERR_DEVICE;
+}
+
+bt_status dispatch_gemm(const GemmArgs& g, hipStream_t stream) {
+    constexpr int BM = BT_GEMM_WA * BT_GEMM_WGM;
+    constexpr int BN = BT_GEMM_WW * BT_GEMM_WGN;
+    const int64_t blocks = bt::ceil_div(g.M, BM) * bt::ceil_div(g.N, BN);
+    if (blocks < 512) return launch_gemm<64, 64, 2, 2>(g, stream);
+    return launch_gemm<BT_GEMM_WA, BT_GEMM_WW, BT_GEMM_WGM, BT_GEMM_WGN>(g, stream);
 }
 
 bt_status launched() {
@@ -743,6 +899,7 @@ extern "C" bt_status bt_ternary_matmul(int64_t M, int64_t N, int64_t K, const in
         return launched();
     }
     GemmArgs g;
+    memset(&g, 0, sizeof(g));
     g.xq = xq;
     g.xscale = xscale;
     g.xsum = xsum;
@@ -755,12 +912,7 @@ extern "C" bt_status bt_ternary_matmul(int64_t M, int64_t N, int64_t K, const in
     g.K = int32_t(K);
     g.tiles = int32_t(bt::ceil_div(N, bt::kTileN));
     g.steps = int32_t(bt::ceil_div(K, bt::kSuperK));
-    const int64_t gy = bt::ceil_div(M, kBM);
-    if (gy > 65535) return BT_ERR_SHAPE;
-    (void)hipGetLastError();
-    hipLaunchKernelGGL(gemm_kernel, dim3(unsigned(bt::ceil_div(N, kBN)), unsigned(gy)), dim3(256), 0,
-                       stream, g);
-    return launched();
+    return dispatch_gemm(g, stream);
 }
 
 extern "C" bt_status bt_quantize_act_grouped(const void* plan_host, const void* plan_dev,
