@@ -65,6 +65,22 @@ def measured_traffic(kernel: str):
     return t.get("kernels", {}).get(kernel, {}).get("hbm_bytes_per_launch")
 
 
+def capture_graph(torch, fn):
+    """HIP graph of fn's launches (all on the capture stream). Warm-up runs on
+    a side stream first, as graph capture requires."""
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        fn()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fn()
+    torch.cuda.synchronize()
+    return g
+
+
 # --------------------------------------------------------------- decode step
 
 class DecodeStep:
@@ -209,15 +225,16 @@ class LongPrefill:
         log(f"long prefill ready: {len(self.probs)} projections, M={m}, "
             f"setup {time.time() - t0:.1f}s")
 
-    def step(self, gemm_events=None):
+    def step(self):
         bt = self.bt
-        for j, p in enumerate(self.probs):
+        for p in self.probs:
             bt.quantize_act(p["x"], p["xq"], p["xs"], p["xsum"])
-            if gemm_events is not None:
-                gemm_events[j][0].record()
             bt.ternary_matmul(p["xq"], p["xs"], p["xsum"], p["wdev"], p["n"], p["s"], y=p["y"])
-            if gemm_events is not None:
-                gemm_events[j][1].record()
+
+    def gemms(self):
+        bt = self.bt
+        for p in self.probs:
+            bt.ternary_matmul(p["xq"], p["xs"], p["xsum"], p["wdev"], p["n"], p["s"], y=p["y"])
 
     def parity(self):
         """Sampled oracle comparison (rows and columns) on the first and last projection."""
@@ -282,6 +299,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--trials", type=int, default=5)
     ap.add_argument("--layers", type=int, default=synth.N_LAYERS)
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--prefill-steps", type=int, default=5)
@@ -348,49 +366,66 @@ def main():
         torch.cuda.synchronize()
         return start.elapsed_time(stop) / steps
 
-    def time_kernel(step_fn, steps):
-        """Duration of the step's GEMV launch: an event pair on the launch stream
-        around it in every step (a separate pass, since each recorded event
-        adds a few microseconds of queue time between launches)."""
-        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-               for _ in range(steps)]
-        torch.cuda.synchronize()
-        for i in range(steps):
-            step_fn(i, evs[i])
-        torch.cuda.synchronize()
-        return [a.elapsed_time(b) for a, b in evs]
-
     for i in range(args.warmup):
         ds.step(i)
         ds.step_two_launch(i)
     torch.cuda.synchronize()
-    t_wall = time.perf_counter()
-    ms_fused = time_steps(ds.step, args.steps)
-    ms_two = time_steps(ds.step_two_launch, args.steps)
-    t_wall = time.perf_counter() - t_wall
-    k_fused = time_kernel(ds.step, args.steps)
-    k_two = time_kernel(ds.step_two_launch, args.steps)
-    paths = {
-        "fused": {"ms_per_step": ms_fused, "kernel_ms": k_fused, "alg": ds.alg_bytes,
-                  "kernel": "gemv_grouped_kernel<true>",
-                  "workload": "one launch per step: quantization fused into the grouped GEMV"},
-        "two_launch": {"ms_per_step": ms_two, "kernel_ms": k_two, "alg": ds.alg_bytes_gemv,
-                       "kernel": "gemv_grouped_kernel<false>",
-                       "workload": "two launches per step: grouped quantize, then grouped GEMV"},
+    # HIP graphs of two consecutive steps (one per weight set): a replay runs
+    # them with no host launch cost in between.
+    g_fused = capture_graph(torch, lambda: (ds.step(0), ds.step(1)))
+    g_two = capture_graph(torch, lambda: (ds.step_two_launch(0), ds.step_two_launch(1)))
+    ds.clear_outputs()
+    g_fused.replay()
+    torch.cuda.synchronize()
+    graph_ok = ds.parity(check_idx)
+    ds.clear_outputs()
+    g_two.replay()
+    torch.cuda.synchronize()
+    graph_ok = graph_ok and ds.parity(check_idx)
+    decode_ok = decode_ok and graph_ok
+    log(f"decode parity after graph replays: {graph_ok}")
+    # Timed trials: every variant in turn, repeated; the median of each is kept
+    # (interleaving spreads clock and thermal drift over all variants alike).
+    runs = {
+        "fused_eager": (lambda i: ds.step(i), 1),
+        "two_launch_eager": (lambda i: ds.step_two_launch(i), 1),
+        "fused_graph": (lambda i: g_fused.replay(), 2),
+        "two_launch_graph": (lambda i: g_two.replay(), 2),
+        "gemv_fused_b2b": (lambda i: ds.fplans[i & 1].launch(), 1),
+        "gemv_two_launch_b2b": (lambda i: ds.mplans[i & 1].launch(), 1),
     }
+    for _ in range(args.warmup):
+        for fn, _per in runs.values():
+            fn(0)
+    samples = {k: [] for k in runs}
+    t_wall = time.perf_counter()
+    for _ in range(args.trials):
+        for k, (fn, per) in runs.items():
+            samples[k].append(time_steps(fn, max(1, args.steps // per)) / per)
+    t_wall = time.perf_counter() - t_wall
+    med = {k: float(np.median(v)) for k, v in samples.items()}
+    paths = {}
+    for name, alg, kern, work in (
+            ("fused", ds.alg_bytes, "gemv_grouped_kernel<true>",
+             "one launch per step: quantization fused into the grouped GEMV"),
+            ("two_launch", ds.alg_bytes_gemv, "gemv_grouped_kernel<false>",
+             "two launches per step: grouped quantize, then grouped GEMV")):
+        for mode in ("eager", "graph"):
+            paths[f"{name}_{mode}"] = {
+                "ms_per_step": med[f"{name}_{mode}"], "kernel_ms": [med[f"gemv_{name}_b2b"]],
+                "alg": alg, "kernel": kern,
+                "workload": work + ("; steps replayed from a HIP graph" if mode == "graph"
+                                    else "; launched eagerly")}
+    for k, v in med.items():
+        log(f"decode [{k}]: {v * 1e3:.1f} us (median of {args.trials}; all: "
+            f"{', '.join(f'{x * 1e3:.1f}' for x in samples[k])})")
     head_name = min(paths, key=lambda k: paths[k]["ms_per_step"])
     head = paths[head_name]
-    other = paths["two_launch" if head_name == "fused" else "fused"]
     ms_step = head["ms_per_step"]
     kern_avg_ms = float(np.mean(head["kernel_ms"]))
     value = ds.w_bytes / (ms_step * 1e-3) / 1e9
     achieved = head["alg"] / (kern_avg_ms * 1e-3) / 1e9
     traffic = measured_traffic(head["kernel"])
-    for name, p in paths.items():
-        km = np.array(p["kernel_ms"]) * 1e3
-        log(f"decode [{name}]: {p['ms_per_step'] * 1e3:.1f} us/step, GEMV kernel "
-            f"{km.mean():.1f} us (p10 {np.percentile(km, 10):.1f}, p90 {np.percentile(km, 90):.1f}), "
-            f"{ds.w_bytes / p['ms_per_step'] / 1e6:.0f} GB/s over weights")
     log(f"headline path: {head_name}; timed region wall {t_wall:.2f}s")
 
     out = {
@@ -419,15 +454,11 @@ def main():
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
                      "algorithmic_bytes_per_launch": head["alg"],
                      "avg_launch_ms": round(kern_avg_ms, 5)},
-        "decode_other_path": {
-            "path": "two_launch" if head_name == "fused" else "fused",
-            "workload": other["workload"],
-            "ms_per_step": round(other["ms_per_step"], 5),
-            "gb_per_s_over_weights": round(ds.w_bytes / (other["ms_per_step"] * 1e-3) / 1e9, 2),
-            "kernel": other["kernel"],
-            "kernel_avg_ms": round(float(np.mean(other["kernel_ms"])), 5),
-            "kernel_achieved_gb_per_s": round(
-                other["alg"] / (np.mean(other["kernel_ms"]) * 1e-3) / 1e9, 2)},
+        "decode_paths_ms_per_step": {k: round(v["ms_per_step"], 5) for k, v in paths.items()},
+        "gemv_kernel_ms_back_to_back": {"gemv_grouped_kernel<true>": round(med["gemv_fused_b2b"], 5),
+                                        "gemv_grouped_kernel<false>":
+                                            round(med["gemv_two_launch_b2b"], 5)},
+        "timing": f"median of {args.trials} interleaved trials of {args.steps} steps per variant",
     }
     del ds
     torch.cuda.empty_cache()
@@ -439,26 +470,37 @@ def main():
         lp.step()
         torch.cuda.synchronize()
         pf_ok = lp.parity()
+        # the whole stack (112 quantize + 112 GEMM launches) as one HIP graph
+        g_stack = capture_graph(torch, lp.step)
+        g_gemms = capture_graph(torch, lp.gemms)
+        for p in lp.probs:
+            p["y"].fill_(float("nan"))
+        g_stack.replay()
+        torch.cuda.synchronize()
+        pf_ok = pf_ok and lp.parity()
         s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
         s0.record()
         for i in range(args.prefill_steps):
-            lp.step()
+            g_stack.replay()
         s1.record()
         torch.cuda.synchronize()
         ms = s0.elapsed_time(s1) / args.prefill_steps
-        # GEMM durations: event pairs around each GEMM, in a separate pass
-        gev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-                for _ in lp.probs] for _ in range(args.prefill_steps)]
-        for i in range(args.prefill_steps):
-            lp.step(gev[i])
+        # GEMM-only time: the stack's GEMMs back to back (no quantize between)
+        g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
-        gemm_ms = float(np.mean([sum(a.elapsed_time(b) for a, b in g) for g in gev]))
+        g0.record()
+        for i in range(args.prefill_steps):
+            g_gemms.replay()
+        g1.record()
+        torch.cuda.synchronize()
+        gemm_ms = g0.elapsed_time(g1) / args.prefill_steps
         tops = lp.ops / (ms * 1e-3) / 1e12
         gemm_tops = lp.ops / (gemm_ms * 1e-3) / 1e12
         log(f"prefill: {ms:.3f} ms/stack ({tops:.0f} TOPS), GEMMs {gemm_ms:.3f} ms ({gemm_tops:.0f} TOPS)")
         out["prefill"] = {
-            "workload": "long prefill, M=4096 tokens x 28 layers x 4 projections (quantize + GEMM each)",
+            "workload": "long prefill, M=4096 tokens x 28 layers x 4 projections (quantize + GEMM "
+                        "each), replayed from a HIP graph",
             "int8_ops_per_stack": lp.ops, "ms_per_stack": round(ms, 4),
             "tops": round(tops, 2), "gemm_only_tops": round(gemm_tops, 2),
             "pct_of_int8_peak": round(100 * tops / I8_PEAK_TOPS, 2),

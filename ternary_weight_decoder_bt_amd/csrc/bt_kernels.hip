@@ -32,6 +32,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <type_traits>
 
 #include "bt_internal.h"
 
@@ -164,7 +165,7 @@ __device__ __forceinline__ int pack4(int a, int b, int c, int d) {
     return (a & 0xff) | ((b & 0xff) << 8) | ((c & 0xff) << 16) | (int(uint32_t(d) << 24));
 }
 
-constexpr int kQuantRegs = 16;   // float4 per thread kept in registers: K <= 16384
+constexpr int kQuantRegs = 9;    // float4 per thread kept in registers: K <= 9216
 
 struct QuantShared {
     float fmax[bt::kQuantThreads / 64];
@@ -194,7 +195,7 @@ __device__ __forceinline__ int block_sum(int v, QuantShared& sh) {
 }
 
 // One workgroup quantizes one row: absmax, then scale, round and clamp, then
-// the row sum of q. With K % 4 == 0 and K <= 16384 the row stays in registers
+// the row sum of q. With K % 4 == 0 and K <= 9216 the row stays in registers
 // between the two passes; otherwise the second pass re-reads it.
 __device__ void quantize_row(const float* __restrict__ x, int64_t K, int8_t* __restrict__ q,
                              float* xscale, int32_t* xsum, QuantShared& sh) {
@@ -263,6 +264,51 @@ __global__ __launch_bounds__(bt::kQuantThreads) void quantize_kernel(const float
     quantize_row(x + m * K, K, xq + m * K, xscale + m, xsum ? xsum + m : nullptr, sh);
 }
 
+// Short rows (K <= 2048, K % 4 == 0): one wave per row, four rows per
+// workgroup, the row held in registers and reduced with cross-lane shuffles
+// only (no LDS, no barrier). Same arithmetic as quantize_row.
+constexpr int kWaveRowRegs = 8;   // float4 per lane: K <= 64 * 8 * 4 = 2048
+
+__global__ __launch_bounds__(bt::kQuantThreads) void quantize_wave_rows_kernel(
+    const float* __restrict__ x, int64_t M, int64_t K, int8_t* __restrict__ xq,
+    float* __restrict__ xscale, int32_t* __restrict__ xsum) {
+    const int lane = threadIdx.x & 63;
+    const int64_t m = int64_t(blockIdx.x) * (bt::kQuantThreads / 64) + (threadIdx.x >> 6);
+    if (m >= M) return;
+    const int64_t K4 = K >> 2;
+    const float* xr = x + m * K;
+    v4f v[kWaveRowRegs];
+    float amax = 0.0f;
+#pragma unroll
+    for (int j = 0; j < kWaveRowRegs; ++j) {
+        const int64_t i = lane + 64 * j;
+        v[j] = i < K4 ? gld<v4f>(xr + 4 * i) : v4f{0.0f, 0.0f, 0.0f, 0.0f};
+        amax = fmaxf(amax, fmaxf(fmaxf(fabsf(v[j].x), fabsf(v[j].y)),
+                                 fmaxf(fabsf(v[j].z), fabsf(v[j].w))));
+    }
+    amax = wave_max(amax);
+    float inv = 127.0f / amax;
+    const bool dead = !(inv <= FLT_MAX);
+    if (dead) inv = 0.0f;
+    int s = 0;
+    int* qr = reinterpret_cast<int*>(xq + m * K);
+#pragma unroll
+    for (int j = 0; j < kWaveRowRegs; ++j) {
+        const int64_t i = lane + 64 * j;
+        if (i < K4) {
+            const int a = quant1(v[j].x * inv), b = quant1(v[j].y * inv);
+            const int c = quant1(v[j].z * inv), d = quant1(v[j].w * inv);
+            gst<int>(qr + i, pack4(a, b, c, d));
+            s += a + b + c + d;
+        }
+    }
+    s = wave_sum(s);
+    if (lane == 0) {
+        gst<float>(xscale + m, dead ? 0.0f : amax / 127.0f);
+        if (xsum) gst<int32_t>(xsum + m, s);
+    }
+}
+
 __global__ __launch_bounds__(bt::kQuantThreads) void quantize_grouped_kernel(
     const QuantDesc* __restrict__ descs, int32_t count) {
     __shared__ QuantShared sh;
@@ -325,9 +371,17 @@ __device__ __forceinline__ v4i gemv_consume(const GemvBatch& b, int n, const int
 
 struct GemvShared {
     QuantShared red;
-    float d[BT_GEMV_MAX_M];      // per-token scale d_m
-    int32_t qs[BT_GEMV_MAX_M];   // per-token sum of q
+    float wmax[BT_GEMV_MAX_M][bt::kGemvWaves];   // fused prologue: per-wave |x| maxima
+    float d[BT_GEMV_MAX_M];                       // per-token scale d_m
+    int32_t qs[bt::kGemvWaves][BT_GEMV_MAX_M];    // per-token sum of q, as per-wave parts
 };
+
+__device__ __forceinline__ int32_t gemv_row_sum(const GemvShared& sh, int m) {
+    int32_t s = sh.qs[0][m];
+#pragma unroll
+    for (int w = 1; w < bt::kGemvWaves; ++w) s += sh.qs[w][m];
+    return s;
+}
 
 // Epilogue of one tile. With K split into chunks, partial sums meet in the
 // workspace (int32 addition is exact in any order) and the last chunk to
@@ -361,7 +415,7 @@ __device__ __forceinline__ void gemv_finish(const GemvDesc& d, int64_t tile, v4i
         for (int i = 0; i < 4; ++i) {
             const int mm = 4 * kq + i;
             if (mm < d.M) {
-                const int32_t qsum = sh.qs[mm];
+                const int32_t qsum = gemv_row_sum(sh, mm);
                 const float dm = sh.d[mm];
                 const int32_t acc = c[i] - qsum;
                 const float rs = dm * d.w_scale;
@@ -376,9 +430,27 @@ __device__ __forceinline__ void gemv_finish(const GemvDesc& d, int64_t tile, v4i
 // token row (the row sum of q and the scale need all of it), keeps its own K
 // chunk in LDS, and the first workgroup of the problem also writes q, d and
 // the row sums out when asked to. The arithmetic is quantize_row's exactly.
-// Rows up to kFusedRegs*1024 elements are read once and held in registers
-// between the absmax and the quantize pass; longer rows are read twice.
+// Rows up to kFusedRegs*1024 elements are read once into registers; token 0
+// is read before the first weight loads go out, so its data is not queued
+// behind them. Longer rows are read twice (absmax, then quantize).
 constexpr int kFusedRegs = 2;   // float4 per thread: K <= 2048 in one read
+constexpr int kGemvThreads = 64 * bt::kGemvWaves;
+
+struct FusedRow {
+    v4f v[kFusedRegs];
+};
+
+__device__ __forceinline__ void gemv_load_row(FusedRow& r, const GemvDesc& d, int m) {
+    const int64_t K4 = d.K >> 2;
+    const float* xr = d.x + int64_t(m) * d.K;
+#pragma unroll
+    for (int j = 0; j < kFusedRegs; ++j) {
+        // clamped, branch-free: lanes past the row re-read its last float4
+        // and their values are never used
+        const int64_t i = min(int64_t(threadIdx.x) + int64_t(j) * kGemvThreads, K4 - 1);
+        r.v[j] = gld<v4f>(xr + 4 * i);
+    }
+}
 
 __device__ __forceinline__ int gemv_quant_store(v4f v, float inv, int64_t k, int m, bool writer,
                                                 const GemvDesc& d, int64_t kbeg, int64_t kend,
@@ -391,57 +463,89 @@ __device__ __forceinline__ int gemv_quant_store(v4f v, float inv, int64_t k, int
     return a + b + c + e;
 }
 
-__device__ __forceinline__ void gemv_quantize_rows(const GemvDesc& d, bool writer, int64_t kbeg,
-                                                   int64_t kend, int8_t* lds, GemvShared& sh) {
+// One short row held in registers: a barrier joins the four wave maxima; the
+// row sum is left as four wave parts that the caller's barrier publishes.
+__device__ __forceinline__ void gemv_quant_short_row(const FusedRow& r, int m, const GemvDesc& d,
+                                                     bool writer, int64_t kbeg, int64_t kend,
+                                                     int8_t* lds, GemvShared& sh) {
     const int tid = threadIdx.x;
-    constexpr int T = 64 * bt::kGemvWaves;
+    const int wave = tid >> 6;
+    const int64_t K4 = d.K >> 2;
+    float amax = 0.0f;
+#pragma unroll
+    for (int j = 0; j < kFusedRegs; ++j) {
+        const int64_t i = tid + int64_t(j) * kGemvThreads;
+        if (i < K4)
+            amax = fmaxf(amax, fmaxf(fmaxf(fabsf(r.v[j].x), fabsf(r.v[j].y)),
+                                     fmaxf(fabsf(r.v[j].z), fabsf(r.v[j].w))));
+    }
+    amax = wave_max(amax);
+    if ((tid & 63) == 0) sh.wmax[m][wave] = amax;
+    __syncthreads();
+    amax = sh.wmax[m][0];
+#pragma unroll
+    for (int w = 1; w < bt::kGemvWaves; ++w) amax = fmaxf(amax, sh.wmax[m][w]);
+    float inv = 127.0f / amax;
+    const bool dead = !(inv <= FLT_MAX);
+    if (dead) inv = 0.0f;
+    int s = 0;
+#pragma unroll
+    for (int j = 0; j < kFusedRegs; ++j) {
+        const int64_t i = tid + int64_t(j) * kGemvThreads;
+        if (i < K4) s += gemv_quant_store(r.v[j], inv, 4 * i, m, writer, d, kbeg, kend, lds);
+    }
+    s = wave_sum(s);
+    if ((tid & 63) == 0) sh.qs[wave][m] = s;
+    if (tid == 0) {
+        const float dm = dead ? 0.0f : amax / 127.0f;
+        sh.d[m] = dm;
+        if (writer && d.xscale) gst<float>(d.xscale + m, dm);
+    }
+}
+
+// All token rows. `r0` holds token 0 when the rows are short. Ends with the
+// barrier that publishes q, d and the row-sum parts; the writer then stores
+// the row sums.
+__device__ __forceinline__ void gemv_quantize_rows(const GemvDesc& d, const FusedRow& r0,
+                                                   bool writer, int64_t kbeg, int64_t kend,
+                                                   int8_t* lds, GemvShared& sh) {
+    const int tid = threadIdx.x;
+    constexpr int T = kGemvThreads;
     const int64_t K4 = d.K >> 2;   // K % 128 == 0
-    const bool in_regs = K4 <= int64_t(kFusedRegs) * T;
-    for (int m = 0; m < d.M; ++m) {
-        const float* xr = d.x + int64_t(m) * d.K;
-        float amax = 0.0f;
-        int s = 0;
-        if (in_regs) {
-            v4f v[kFusedRegs];
-#pragma unroll
-            for (int j = 0; j < kFusedRegs; ++j) {
-                const int64_t i = tid + int64_t(j) * T;
-                v[j] = i < K4 ? gld<v4f>(xr + 4 * i) : v4f{0.0f, 0.0f, 0.0f, 0.0f};
-            }
-#pragma unroll
-            for (int j = 0; j < kFusedRegs; ++j)
-                amax = fmaxf(amax, fmaxf(fmaxf(fabsf(v[j].x), fabsf(v[j].y)),
-                                         fmaxf(fabsf(v[j].z), fabsf(v[j].w))));
-            amax = block_max(amax, sh.red);
-            float inv = 127.0f / amax;
-            if (!(inv <= FLT_MAX)) inv = 0.0f;
-#pragma unroll
-            for (int j = 0; j < kFusedRegs; ++j) {
-                const int64_t i = tid + int64_t(j) * T;
-                if (i < K4) s += gemv_quant_store(v[j], inv, 4 * i, m, writer, d, kbeg, kend, lds);
-            }
-        } else {
+    if (K4 <= int64_t(kFusedRegs) * T) {
+        gemv_quant_short_row(r0, 0, d, writer, kbeg, kend, lds, sh);
+        for (int m = 1; m < d.M; ++m) {
+            FusedRow r;
+            gemv_load_row(r, d, m);
+            gemv_quant_short_row(r, m, d, writer, kbeg, kend, lds, sh);
+        }
+    } else {
+        for (int m = 0; m < d.M; ++m) {
+            const float* xr = d.x + int64_t(m) * d.K;
+            float amax = 0.0f;
             for (int64_t i = tid; i < K4; i += T) {
                 const v4f v = gld<v4f>(xr + 4 * i);
                 amax = fmaxf(amax, fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w))));
             }
             amax = block_max(amax, sh.red);
             float inv = 127.0f / amax;
-            if (!(inv <= FLT_MAX)) inv = 0.0f;
+            const bool dead = !(inv <= FLT_MAX);
+            if (dead) inv = 0.0f;
+            int s = 0;
             for (int64_t i = tid; i < K4; i += T)
                 s += gemv_quant_store(gld<v4f>(xr + 4 * i), inv, 4 * i, m, writer, d, kbeg, kend, lds);
+            s = block_sum(s, sh.red);
+            if (tid < bt::kGemvWaves) sh.qs[tid][m] = tid == 0 ? s : 0;
+            if (tid == 0) {
+                const float dm = dead ? 0.0f : amax / 127.0f;
+                sh.d[m] = dm;
+                if (writer && d.xscale) gst<float>(d.xscale + m, dm);
+            }
+            __syncthreads();   // the reduction slots are reused by the next row
         }
-        s = block_sum(s, sh.red);
-        if (tid == 0) {
-            const bool dead = !(127.0f / amax <= FLT_MAX);
-            const float dm = dead ? 0.0f : amax / 127.0f;
-            sh.d[m] = dm;
-            sh.qs[m] = s;
-            if (writer && d.xscale) gst<float>(d.xscale + m, dm);
-            if (writer && d.xsum) gst<int32_t>(d.xsum + m, s);
-        }
-        __syncthreads();   // the reduction slots are reused by the next row
     }
+    __syncthreads();
+    if (writer && d.xsum && tid < d.M) gst<int32_t>(d.xsum + tid, gemv_row_sum(sh, tid));
 }
 
 template <bool kFused>
@@ -471,11 +575,15 @@ __device__ __forceinline__ void gemv_block(const GemvDesc& d, int64_t local_bloc
         gemv_issue(b, d.w + t * tile_bytes, s0 + bb * kB, s1 - 1, lane);
     };
 
-    // The first two batches go out before the activations are staged, so the
-    // weight latency overlaps the staging.
+    // The first weight batches go out before the activations are staged, so
+    // their latency overlaps the staging. Fused: token 0's activations go out
+    // first, and the second batch waits until the rows are quantized (the
+    // registers it needs hold the activations until then).
+    FusedRow r0;
+    if (kFused) gemv_load_row(r0, d, 0);
     GemvBatch b0, b1;
     issue(b0, 0);
-    issue(b1, min(1, total - 1));
+    if (!kFused) issue(b1, min(1, total - 1));
 
     // Stage this chunk of the M token rows in LDS rows 0..M-1 (zero past K)
     // and a zero row M, which the lanes of tokens >= M read instead.
@@ -488,7 +596,8 @@ __device__ __forceinline__ void gemv_block(const GemvDesc& d, int64_t local_bloc
             const int col = (i - m * pieces) * 16;
             if (m == d.M || kbeg + col >= d.K) lds_st<v4i>(lds + m * d.lds_row + col, v4i{0, 0, 0, 0});
         }
-        gemv_quantize_rows(d, chunk == 0 && g == 0, kbeg, kend, lds, sh);
+        gemv_quantize_rows(d, r0, chunk == 0 && g == 0, kbeg, kend, lds, sh);
+        issue(b1, min(1, total - 1));
     } else {
         for (int i = tid; i < (d.M + 1) * pieces; i += 64 * bt::kGemvWaves) {
             const int m = i / pieces;
@@ -500,7 +609,9 @@ __device__ __forceinline__ void gemv_block(const GemvDesc& d, int64_t local_bloc
         // the epilogue's per-token scale and row sum, read once
         if (tid < d.M) {
             sh.d[tid] = gld<float>(d.xscale + tid);
-            sh.qs[tid] = gld<int32_t>(d.xsum + tid);
+            sh.qs[0][tid] = gld<int32_t>(d.xsum + tid);
+#pragma unroll
+            for (int w = 1; w < bt::kGemvWaves; ++w) sh.qs[w][tid] = 0;
         }
         __syncthreads();
     }
@@ -536,14 +647,14 @@ __device__ __forceinline__ void gemv_block(const GemvDesc& d, int64_t local_bloc
 }
 
 template <bool kFused>
-__global__ __launch_bounds__(64 * bt::kGemvWaves) void gemv_kernel(GemvDesc d) {
+__global__ __launch_bounds__(64 * bt::kGemvWaves) __attribute__((amdgpu_waves_per_eu(5))) void gemv_kernel(GemvDesc d) {
     extern __shared__ __attribute__((aligned(16))) int8_t gemv_lds[];
     __shared__ GemvShared sh;
     gemv_block<kFused>(d, blockIdx.x, gemv_lds, sh);
 }
 
 template <bool kFused>
-__global__ __launch_bounds__(64 * bt::kGemvWaves) void gemv_grouped_kernel(
+__global__ __launch_bounds__(64 * bt::kGemvWaves) __attribute__((amdgpu_waves_per_eu(5))) void gemv_grouped_kernel(
     const GemvDesc* __restrict__ descs, int32_t count) {
     extern __shared__ __attribute__((aligned(16))) int8_t gemv_lds[];
     __shared__ GemvShared sh;
@@ -580,6 +691,10 @@ size_t gemv_lds_bytes(const GemvDesc& d) { return size_t(d.M + 1) * size_t(d.lds
 // remapped to give each XCD a contiguous band of output tiles (whole rows of
 // tiles along N): the activation rows of a band stay in that XCD's L2.
 
+#ifndef BT_GEMM_SCHED
+#define BT_GEMM_SCHED 0
+#endif
+
 struct GemmArgs {
     const int8_t* xq;
     const float* xscale;
@@ -600,18 +715,27 @@ __device__ __forceinline__ void lds_dma16(__amdgpu_buffer_rsrc_t r, int8_t* lds_
                                               int(soff), 0, 0);
 }
 
-template <int WA, int WW, int WGM, int WGN>
+template <int WA, int WW, int WGM, int WGN, int KS>
 __global__ __launch_bounds__(64 * WGM * WGN) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void gemm_kernel(GemmArgs g) {
     constexpr int BM = WA * WGM;
     constexpr int BN = WW * WGN;
     constexpr int NW = WGM * WGN;
-    constexpr int TA = WA / 16;   // MFMA blocks along tokens per wave
-    constexpr int TW = WW / 16;   // MFMA blocks (16-row weight tiles) per wave
-    constexpr int kStage = BM * 256;                 // LDS bytes per activation stage
-    constexpr int kDmaPerWave = BM * 16 / 64 / NW;   // 1 KB copies per wave per stage
-    static_assert(kDmaPerWave * 64 * NW == BM * 16, "A stage must split evenly over waves");
+    constexpr int TA = WA / 16;    // MFMA blocks along tokens per wave
+    constexpr int TW = WW / 16;    // MFMA blocks (16-row weight tiles) per wave
+    constexpr int CPR = KS / 16;   // 16-byte chunks per activation row per stage
+    constexpr int SPW = KS / 64;   // 64-wide MFMA steps per stage
+    constexpr int kStage = BM * KS;                   // LDS bytes per activation stage
+    constexpr int kDmaPerWave = BM * CPR / 64 / NW;   // 1 KB copies per wave per stage
+    static_assert(KS == 128 || KS == 256, "stage width");
+    static_assert(kDmaPerWave * 64 * NW == BM * CPR, "A stage must split evenly over waves");
     __shared__ __attribute__((aligned(16))) int8_t As[2 * kStage];
+
+    // Swizzled LDS slot of logical chunk c of row r: the 16 rows an MFMA
+    // fragment read touches land in 16 distinct 4-bank groups.
+    auto slot_of = [](int r, int c) {
+        return KS == 256 ? (c ^ (r & 15)) : (c ^ ((r >> 1) & 7));
+    };
 
     const int xcd = blockIdx.x % kXcds;
     const int tile_id = xcd * g.per_xcd + blockIdx.x / kXcds;
@@ -628,43 +752,55 @@ void gemm_kernel(GemmArgs g) {
     const int n0 = nt * BN;
     const int t0 = min(n0 / bt::kTileN + wn * TW, g.tiles - 1);
     const uint32_t tile_bytes = uint32_t(g.steps) * 1024u;
-    const int nst = g.steps;
+    const int nst = (g.K + KS - 1) / KS;
 
     // This wave's weight tiles as one buffer; tiles past N read as zero.
+    // Per stage a lane needs KS/64 words of each tile: 16 bytes (KS = 256) or
+    // the matching 8-byte half (KS = 128) of its 16 bytes in the 256-wide step.
     const __amdgpu_buffer_rsrc_t wrsrc =
         make_rsrc(g.w + int64_t(t0) * tile_bytes, uint32_t(min(TW, g.tiles - t0)) * tile_bytes);
-    auto load_b = [&](v4u (&b)[TW], int s) {
+    using BVec = typename std::conditional<KS == 256, v4u, v2u>::type;
+    auto load_b = [&](BVec (&b)[TW], int s) {
+        const uint32_t soff = KS == 256 ? uint32_t(s) * 1024u
+                                        : uint32_t(s >> 1) * 1024u + uint32_t(s & 1) * 8u;
 #pragma unroll
-        for (int t = 0; t < TW; ++t)
-            b[t] = buf_ld16u(wrsrc, uint32_t(lane) * 16u, uint32_t(t) * tile_bytes + uint32_t(s) * 1024u);
+        for (int t = 0; t < TW; ++t) {
+            if constexpr (KS == 256)
+                b[t] = buf_ld16u(wrsrc, uint32_t(lane) * 16u, uint32_t(t) * tile_bytes + soff);
+            else
+                b[t] = __builtin_bit_cast(v2u, __builtin_amdgcn_raw_buffer_load_b64(
+                    wrsrc, int(uint32_t(lane) * 16u), int(uint32_t(t) * tile_bytes + soff), 0));
+        }
     };
 
     // The workgroup's activation rows as one buffer; rows past M read as zero.
     const uint32_t arows = uint32_t(min(int64_t(BM), int64_t(g.M) - m0));
     const __amdgpu_buffer_rsrc_t arsrc = make_rsrc(g.xq + m0 * g.K, arows * uint32_t(g.K));
     // Copy j of this wave fills LDS slots p = (wave*kDmaPerWave + j)*64 + lane:
-    // row r = p / 16 = r0 + 4j, swizzled chunk p % 16 = lane % 16, logical
-    // chunk c = (lane % 16) ^ (r % 16), which depends on j only through j % 4.
-    // So four per-lane offsets serve every copy; the 4jK row step is scalar.
-    const int r0 = wave * kDmaPerWave * 4 + (lane >> 4);
+    // row r = p / CPR, slot p % CPR, logical chunk c = slot_of^-1 (an XOR, its
+    // own inverse). The row advances by 64/CPR per copy; the swizzle repeats
+    // every 4 copies, so four per-lane offsets serve all copies.
+    constexpr int RPC = 64 / CPR;   // rows per copy
+    const int r0 = wave * kDmaPerWave * RPC + lane / CPR;
     uint32_t avoff[4];
-    bool ahigh[4];   // logical chunk in the upper half of the stage (past K on a 128-wide tail)
+    bool ahigh[4];   // chunk in the upper 128 bytes of a 256-wide stage
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-        const int c = (lane & 15) ^ ((r0 + 4 * q) & 15);
+        const int r = r0 + RPC * q;
+        const int c = slot_of(r, lane % CPR);
         avoff[q] = uint32_t(r0) * uint32_t(g.K) + uint32_t(c) * 16u;
         ahigh[q] = c >= 8;
     }
-    const bool tail128 = (g.K & 255) != 0;
+    const bool tail128 = KS == 256 && (g.K & 255) != 0;
     auto load_a = [&](int buf, int s) {
-        const uint32_t kcol = uint32_t(s) * 256u;
+        const uint32_t kcol = uint32_t(s) * KS;
         const bool last_tail = tail128 && s == nst - 1;
 #pragma unroll
         for (int j = 0; j < kDmaPerWave; ++j) {
             // a chunk past K must read zero, not the next row: push it out of bounds
             const uint32_t voff = (last_tail && ahigh[j & 3]) ? 0xfffffff0u : avoff[j & 3];
             lds_dma16(arsrc, As + buf * kStage + (wave * kDmaPerWave + j) * 1024, voff,
-                      kcol + uint32_t(4 * j) * uint32_t(g.K));
+                      kcol + uint32_t(RPC * j) * uint32_t(g.K));
         }
     };
 
@@ -677,14 +813,13 @@ void gemm_kernel(GemmArgs g) {
 #pragma unroll
         for (int t = 0; t < TW; ++t) acc[i][t] = v4i{0, 0, 0, 0};
 
-    // fragment reads: row (wm*WA + 16i + lane%16), logical chunk 4jj + lane/16,
-    // swizzled with (row % 16) = lane % 16
-    const int8_t* afrag = As + (wm * WA + (lane & 15)) * 256;
-    int aslot[4];
+    // fragment reads: row (wm*WA + 16i + lane%16), logical chunk 4jj + lane/16
+    const int8_t* afrag = As + (wm * WA + (lane & 15)) * KS;
+    int aslot[SPW];
 #pragma unroll
-    for (int jj = 0; jj < 4; ++jj) aslot[jj] = ((4 * jj + (lane >> 4)) ^ (lane & 15)) * 16;
+    for (int jj = 0; jj < SPW; ++jj) aslot[jj] = slot_of(lane & 15, 4 * jj + (lane >> 4)) * 16;
 
-    auto stage = [&](int s, const v4u (&bc)[TW], v4u (&bn)[TW]) {
+    auto stage = [&](int s, const BVec (&bc)[TW], BVec (&bn)[TW]) {
         const int cur = s & 1;
         const bool more = s + 1 < nst;
         if (more) {
@@ -694,10 +829,10 @@ void gemm_kernel(GemmArgs g) {
         asm volatile("" ::: "memory");
         const int8_t* abuf = afrag + cur * kStage;
 #pragma unroll
-        for (int jj = 0; jj < 4; ++jj) {
+        for (int jj = 0; jj < SPW; ++jj) {
             v4i af[TA];
 #pragma unroll
-            for (int i = 0; i < TA; ++i) af[i] = lds_ld<v4i>(abuf + i * 16 * 256 + aslot[jj]);
+            for (int i = 0; i < TA; ++i) af[i] = lds_ld<v4i>(abuf + i * 16 * KS + aslot[jj]);
 #pragma unroll
             for (int t = 0; t < TW; ++t) {
                 const v4i bf = unpack16(bc[t][jj]);
@@ -705,12 +840,31 @@ void gemm_kernel(GemmArgs g) {
                 for (int i = 0; i < TA; ++i) acc[i][t] = mfma16x16x64(bf, af[i], acc[i][t]);
             }
         }
+#if BT_GEMM_SCHED
+        // Optional fixed interleave (off by default: measured slower than the
+        // compiler's own order on the 64 x 64 tile): each MFMA followed by up
+        // to two VALU slots, fragment reads spread over the first MFMAs.
+#pragma unroll
+        for (int jj = 0; jj < SPW; ++jj) {
+#pragma unroll
+            for (int k = 0; k < TA; ++k) {
+                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // DS read
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
+                __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);   // VALU
+            }
+#pragma unroll
+            for (int k = 0; k < TA * TW - TA; ++k) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
+                __builtin_amdgcn_sched_group_barrier(0x002, 1, 0);   // VALU
+            }
+        }
+#endif
         // the next stage's LDS copies and weight words must have landed
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
     };
 
-    v4u b0[TW], b1[TW];
+    BVec b0[TW], b1[TW];
     load_a(0, 0);
     load_b(b0, 0);
     __builtin_amdgcn_s_waitcnt(0);
@@ -753,10 +907,10 @@ void gemm_kernel(GemmArgs g) {
 }
 
 #ifndef BT_GEMM_WA
-#define BT_GEMM_WA 64
+#define BT_GEMM_WA 128
 #endif
 #ifndef BT_GEMM_WW
-#define BT_GEMM_WW 128
+#define BT_GEMM_WW 64
 #endif
 #ifndef BT_GEMM_WGM
 #define BT_GEMM_WGM 2
@@ -764,11 +918,14 @@ void gemm_kernel(GemmArgs g) {
 #ifndef BT_GEMM_WGN
 #define BT_GEMM_WGN 2
 #endif
+#ifndef BT_GEMM_KS
+#define BT_GEMM_KS 128
+#endif
 
 // Shape dispatch of the GEMM: the default tile, or a 128 x 128 tile (waves of
 // 64 x 64) when the default leaves fewer than two workgroups per compute unit
 // (e.g. 4096 x 1536 outputs).
-template <int WA, int WW, int WGM, int WGN>
+template <int WA, int WW, int WGM, int WGN, int KS>
 bt_status launch_gemm(GemmArgs g, hipStream_t stream) {
     constexpr int BM = WA * WGM;
     constexpr int BN = WW * WGN;
@@ -779,7 +936,7 @@ bt_status launch_gemm(GemmArgs g, hipStream_t stream) {
     const int64_t grid = int64_t(g.per_xcd) * kXcds;
     if (grid > (int64_t(1) << 31) - 1) return BT_ERR_SHAPE;
     (void)hipGetLastError();
-    hipLaunchKernelGGL((gemm_kernel<WA, WW, WGM, WGN>), dim3(unsigned(grid)),
+    hipLaunchKernelGGL((gemm_kernel<WA, WW, WGM, WGN, KS>), dim3(unsigned(grid)),
                        dim3(64 * WGM * WGN), 0, stream, g);
     return hipGetLastError() == hipSuccess ? BT_OK : BT_ERR_DEVICE;
 }
@@ -788,8 +945,8 @@ bt_status dispatch_gemm(const GemmArgs& g, hipStream_t stream) {
     constexpr int BM = BT_GEMM_WA * BT_GEMM_WGM;
     constexpr int BN = BT_GEMM_WW * BT_GEMM_WGN;
     const int64_t blocks = bt::ceil_div(g.M, BM) * bt::ceil_div(g.N, BN);
-    if (blocks < 512) return launch_gemm<64, 64, 2, 2>(g, stream);
-    return launch_gemm<BT_GEMM_WA, BT_GEMM_WW, BT_GEMM_WGM, BT_GEMM_WGN>(g, stream);
+    if (blocks < 512) return launch_gemm<64, 64, 2, 2, 256>(g, stream);
+    return launch_gemm<BT_GEMM_WA, BT_GEMM_WW, BT_GEMM_WGM, BT_GEMM_WGN, BT_GEMM_KS>(g, stream);
 }
 
 bt_status launched() {
@@ -825,8 +982,14 @@ extern "C" bt_status bt_quantize_act(const float* x, int64_t M, int64_t K, int8_
         (xsum && !bt::aligned16(xsum)))
         return BT_ERR_ALIGN;
     (void)hipGetLastError();
-    hipLaunchKernelGGL(quantize_kernel, dim3(unsigned(M)), dim3(bt::kQuantThreads), 0, stream, x, K,
-                       xq, xscale, xsum);
+    if (K % 4 == 0 && K / 4 <= 64 * kWaveRowRegs) {
+        const int64_t rows_per_wg = bt::kQuantThreads / 64;
+        hipLaunchKernelGGL(quantize_wave_rows_kernel, dim3(unsigned(bt::ceil_div(M, rows_per_wg))),
+                           dim3(bt::kQuantThreads), 0, stream, x, M, K, xq, xscale, xsum);
+    } else {
+        hipLaunchKernelGGL(quantize_kernel, dim3(unsigned(M)), dim3(bt::kQuantThreads), 0, stream,
+                           x, K, xq, xscale, xsum);
+    }
     return launched();
 }
 

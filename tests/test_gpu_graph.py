@@ -1,0 +1,115 @@
+"""The library's launches inside a captured HIP graph: every replay must give
+exactly the eager results (the kernels take the caller's stream and issue no
+memset, allocation or host synchronization, so they are capturable).
+
+Each replay is preceded by eager work on the same buffers (outputs poisoned
+with NaN, an eager launch into other buffers) and a synchronization.
+"""
+
+import numpy as np
+import pytest
+
+import synth
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+import ternary_weight_decoder_bt_amd as bt  # noqa: E402
+
+
+@pytest.fixture(scope="module")
+def dev():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    return torch.device("cuda:0")
+
+
+def _weights(c, dev):
+    n, k = c["w"].shape
+    packed = torch.from_numpy(bt.pack_ternary(c["w"]).reshape(-1)).to(dev)
+    return bt.repack_ternary(packed, n, k)
+
+
+def _capture(fn):
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        fn()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fn()
+    torch.cuda.synchronize()
+    return g
+
+
+def test_graph_replays_match_eager(dev):
+    # a grouped decode step (fused and two-launch), a split-K GEMV and a GEMM
+    cases = [synth.decode_problem(0, proj) for proj in range(4)]
+    ws = [_weights(c, dev) for c in cases]
+    xs = [torch.from_numpy(c["x"]).to(dev) for c in cases]
+
+    def outs(c):
+        m, k, n = c["M"], c["K"], c["N"]
+        return {"xq": torch.empty((m, k), dtype=torch.int8, device=dev),
+                "xscale": torch.empty(m, dtype=torch.float32, device=dev),
+                "xsum": torch.empty(m, dtype=torch.int32, device=dev),
+                "y": torch.empty((m, n), dtype=torch.float32, device=dev),
+                "acc": torch.empty((m, n), dtype=torch.int32, device=dev)}
+
+    two = [outs(c) for c in cases]
+    fused = [outs(c) for c in cases]
+    qplan = bt.QuantPlan([(x, o["xq"], o["xscale"], o["xsum"]) for x, o in zip(xs, two)])
+    mplan = bt.MatmulPlan([dict(o, wdev=w, n=c["N"], w_scale=c["w_scale"])
+                           for o, w, c in zip(two, ws, cases)])
+    fplan = bt.MatmulPlan([dict(o, wdev=w, n=c["N"], w_scale=c["w_scale"], x=x)
+                           for o, w, c, x in zip(fused, ws, cases, xs)])
+    sk = synth.small_problem(21, 3, 1536, 8960)
+    sk_w, sk_x = _weights(sk, dev), torch.from_numpy(sk["x"]).to(dev)
+    sk_q = bt.quantize_act(sk_x)
+    sk_ws = bt.new_workspace(3, 1536, 8960, dev)
+    sk_y = torch.empty((3, 1536), dtype=torch.float32, device=dev)
+    gm = synth.small_problem(22, 200, 2048, 1536, "t3")
+    gm_w, gm_x = _weights(gm, dev), torch.from_numpy(gm["x"]).to(dev)
+    gm_q = [torch.empty((200, 1536), dtype=torch.int8, device=dev),
+            torch.empty(200, dtype=torch.float32, device=dev),
+            torch.empty(200, dtype=torch.int32, device=dev)]
+    gm_y = torch.empty((200, 2048), dtype=torch.float32, device=dev)
+
+    def work():
+        qplan.launch()
+        mplan.launch()
+        fplan.launch()
+        bt.ternary_matmul(*sk_q, sk_w, 1536, sk["w_scale"], y=sk_y, workspace=sk_ws)
+        bt.quantize_act(gm_x, *gm_q)
+        bt.ternary_matmul(*gm_q, gm_w, 2048, gm["w_scale"], y=gm_y)
+
+    def snapshot():
+        torch.cuda.synchronize()
+        tensors = [t for o in two + fused for t in o.values()] + [sk_y, gm_y] + gm_q
+        return [t.clone() for t in tensors]
+
+    def poison():
+        for o in two + fused:
+            o["y"].fill_(float("nan"))
+            o["acc"].fill_(-1)
+            o["xq"].fill_(99)
+        sk_y.fill_(float("nan"))
+        gm_y.fill_(float("nan"))
+        gm_q[0].fill_(99)
+
+    work()
+    eager = snapshot()
+    g = _capture(work)
+    for rep in range(4):
+        poison()
+        # unrelated eager launch between replays
+        bt.ternary_matmul(*sk_q, sk_w, 1536, sk["w_scale"], workspace=sk_ws)
+        torch.cuda.synchronize()
+        g.replay()
+        got = snapshot()
+        for i, (a, b) in enumerate(zip(got, eager)):
+            assert torch.equal(a.view(torch.uint8) if a.dtype == torch.float32 else a,
+                               b.view(torch.uint8) if b.dtype == torch.float32 else b), (rep, i)
+    assert int(sk_ws.count_nonzero()) == 0
