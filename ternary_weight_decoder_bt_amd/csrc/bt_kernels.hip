@@ -691,10 +691,6 @@ size_t gemv_lds_bytes(const GemvDesc& d) { return size_t(d.M + 1) * size_t(d.lds
 // remapped to give each XCD a contiguous band of output tiles (whole rows of
 // tiles along N): the activation rows of a band stay in that XCD's L2.
 
-#ifndef BT_GEMM_SCHED
-#define BT_GEMM_SCHED 0
-#endif
-
 struct GemmArgs {
     const int8_t* xq;
     const float* xscale;
@@ -715,7 +711,38 @@ __device__ __forceinline__ void lds_dma16(__amdgpu_buffer_rsrc_t r, int8_t* lds_
                                               int(soff), 0, 0);
 }
 
-template <int WA, int WW, int WGM, int WGN, int KS>
+// vmcnt(n) with the other counters left alone (gfx9 encoding: vmcnt in
+// bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// Epilogue of a full 16 x 64 output block of one wave (token rows mb..mb+15,
+// columns nb..nb+63) given in the MFMA layout: lane l holds v[t] = columns
+// 16t + 4(l/16) .. +3 of row l%16. Stored straight, every store instruction
+// would write 16 rows x 64 bytes (half cache lines). Instead the block passes
+// through the wave's own 4 KB of LDS (16-byte slots XOR-swizzled by row, so
+// both the writes and the reads are conflict-free) and is stored row-wise:
+// 16 lanes write 256 contiguous bytes of one row, whole cache lines.
+__device__ __forceinline__ void gemm_store_block_rows(const v4f (&v)[4], float* ep, float* y,
+                                                      int64_t ldy, int64_t mb, int64_t nb,
+                                                      int lane) {
+    const int rl = lane & 15;
+    const int cq = lane >> 4;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) lds_st<v4f>(ep + rl * 64 + (((4 * t + cq) ^ rl) * 4), v[t]);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int r = 4 * j + cq;
+        const int c = lane & 15;
+        const v4f row = lds_ld<v4f>(ep + r * 64 + ((c ^ r) * 4));
+        __builtin_nontemporal_store(row, (BT_GLOBAL v4f*)(y + (mb + r) * ldy + nb + 4 * c));
+    }
+}
+
+template <int WA, int WW, int WGM, int WGN, int KS, int NS>
 __global__ __launch_bounds__(64 * WGM * WGN) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void gemm_kernel(GemmArgs g) {
     constexpr int BM = WA * WGM;
@@ -723,16 +750,21 @@ void gemm_kernel(GemmArgs g) {
     constexpr int NW = WGM * WGN;
     constexpr int TA = WA / 16;    // MFMA blocks along tokens per wave
     constexpr int TW = WW / 16;    // MFMA blocks (16-row weight tiles) per wave
+    constexpr int NK = KS / 64;    // 64-wide MFMA steps per stage
     constexpr int CPR = KS / 16;   // 16-byte chunks per activation row per stage
-    constexpr int SPW = KS / 64;   // 64-wide MFMA steps per stage
     constexpr int kStage = BM * KS;                   // LDS bytes per activation stage
     constexpr int kDmaPerWave = BM * CPR / 64 / NW;   // 1 KB copies per wave per stage
+    constexpr int kLoads = TW + kDmaPerWave;          // vector-memory ops per wave and stage
     static_assert(KS == 128 || KS == 256, "stage width");
+    static_assert(WA % 16 == 0 && WW % 16 == 0, "wave tile");
+    static_assert(NS >= 2 && (NS - 2) * kLoads < 64, "pipeline depth");
     static_assert(kDmaPerWave * 64 * NW == BM * CPR, "A stage must split evenly over waves");
-    __shared__ __attribute__((aligned(16))) int8_t As[2 * kStage];
+    __shared__ __attribute__((aligned(16))) int8_t As[NS * kStage];
+    constexpr bool kRowStores = WW == 64;   // row-wise epilogue through LDS
+    __shared__ __attribute__((aligned(16))) float Ep[kRowStores ? NW * 16 * 64 : 4];
 
     // Swizzled LDS slot of logical chunk c of row r: the 16 rows an MFMA
-    // fragment read touches land in 16 distinct 4-bank groups.
+    // fragment read serves at once land in 16 distinct 4-bank groups.
     auto slot_of = [](int r, int c) {
         return KS == 256 ? (c ^ (r & 15)) : (c ^ ((r >> 1) & 7));
     };
@@ -750,57 +782,70 @@ void gemm_kernel(GemmArgs g) {
     const int wn = wave - wm * WGN;
     const int64_t m0 = int64_t(mt) * BM;
     const int n0 = nt * BN;
-    const int t0 = min(n0 / bt::kTileN + wn * TW, g.tiles - 1);
+    const int t0 = min(n0 / bt::kTileN + wn * (WW / bt::kTileN), g.tiles - 1);
     const uint32_t tile_bytes = uint32_t(g.steps) * 1024u;
     const int nst = (g.K + KS - 1) / KS;
 
-    // This wave's weight tiles as one buffer; tiles past N read as zero.
-    // Per stage a lane needs KS/64 words of each tile: 16 bytes (KS = 256) or
-    // the matching 8-byte half (KS = 128) of its 16 bytes in the 256-wide step.
-    const __amdgpu_buffer_rsrc_t wrsrc =
-        make_rsrc(g.w + int64_t(t0) * tile_bytes, uint32_t(min(TW, g.tiles - t0)) * tile_bytes);
+    // This wave's weight tiles as one buffer. The tile is part of the
+    // per-lane (VGPR) offset, which the buffer's range check sees, so tiles
+    // past N read as zero; the scalar offset only selects the stage. Per
+    // stage a lane needs KS/64 words of its 16 bytes in a tile's 256-wide
+    // step: all 16 bytes (KS = 256) or the matching 8-byte half (KS = 128).
+    const __amdgpu_buffer_rsrc_t wrsrc = make_rsrc(
+        g.w + int64_t(t0) * tile_bytes,
+        uint32_t(min(WW / bt::kTileN, g.tiles - t0)) * tile_bytes);
     using BVec = typename std::conditional<KS == 256, v4u, v2u>::type;
-    auto load_b = [&](BVec (&b)[TW], int s) {
-        const uint32_t soff = KS == 256 ? uint32_t(s) * 1024u
+    // A stage past K (padding of the pipeline) reads zeros: bit 31 set in
+    // its per-lane offsets puts them out of range (buffers here stay below
+    // 2^31 bytes and the scalar offset below 2^30, so the sum cannot wrap),
+    // and no byte is fetched. The masks are ORed in, never branched on: a
+    // branch around the loads would make the compiler's wait counts
+    // conservative.
+    constexpr uint32_t kNowhere = 0x80000000u;
+    auto load_b = [&](BVec (&b)[TW], int s, uint32_t pad) {
+        const uint32_t koff = KS == 256 ? uint32_t(s) * 1024u
                                         : uint32_t(s >> 1) * 1024u + uint32_t(s & 1) * 8u;
 #pragma unroll
         for (int t = 0; t < TW; ++t) {
+            const uint32_t voff = (uint32_t(lane) * 16u + uint32_t(t) * tile_bytes) | pad;
             if constexpr (KS == 256)
-                b[t] = buf_ld16u(wrsrc, uint32_t(lane) * 16u, uint32_t(t) * tile_bytes + soff);
+                b[t] = buf_ld16u(wrsrc, voff, koff);
             else
-                b[t] = __builtin_bit_cast(v2u, __builtin_amdgcn_raw_buffer_load_b64(
-                    wrsrc, int(uint32_t(lane) * 16u), int(uint32_t(t) * tile_bytes + soff), 0));
+                b[t] = __builtin_bit_cast(
+                    v2u, __builtin_amdgcn_raw_buffer_load_b64(wrsrc, int(voff), int(koff), 0));
         }
     };
 
-    // The workgroup's activation rows as one buffer; rows past M read as zero.
+    // The workgroup's activation rows as one buffer; rows past M read as zero
+    // (the row is part of the per-lane offset, which the range check sees).
     const uint32_t arows = uint32_t(min(int64_t(BM), int64_t(g.M) - m0));
     const __amdgpu_buffer_rsrc_t arsrc = make_rsrc(g.xq + m0 * g.K, arows * uint32_t(g.K));
     // Copy j of this wave fills LDS slots p = (wave*kDmaPerWave + j)*64 + lane:
     // row r = p / CPR, slot p % CPR, logical chunk c = slot_of^-1 (an XOR, its
     // own inverse). The row advances by 64/CPR per copy; the swizzle repeats
-    // every 4 copies, so four per-lane offsets serve all copies.
+    // every 4 copies, so four per-lane chunk offsets serve all copies.
     constexpr int RPC = 64 / CPR;   // rows per copy
     const int r0 = wave * kDmaPerWave * RPC + lane / CPR;
     uint32_t avoff[4];
-    bool ahigh[4];   // chunk in the upper 128 bytes of a 256-wide stage
+    uint32_t ahigh[4];   // kNowhere for a chunk in the upper 128 bytes of a 256-wide stage
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
         const int r = r0 + RPC * q;
         const int c = slot_of(r, lane % CPR);
         avoff[q] = uint32_t(r0) * uint32_t(g.K) + uint32_t(c) * 16u;
-        ahigh[q] = c >= 8;
+        ahigh[q] = c >= 8 ? kNowhere : 0u;
     }
     const bool tail128 = KS == 256 && (g.K & 255) != 0;
-    auto load_a = [&](int buf, int s) {
+    auto load_a = [&](int buf, int s, uint32_t pad) {
         const uint32_t kcol = uint32_t(s) * KS;
-        const bool last_tail = tail128 && s == nst - 1;
+        // in the last stage of a K that ends half way through it, a chunk
+        // past K must read zero, not the next row: push it out of range too
+        const uint32_t tail = (tail128 && s == nst - 1) ? 0xffffffffu : 0u;
 #pragma unroll
         for (int j = 0; j < kDmaPerWave; ++j) {
-            // a chunk past K must read zero, not the next row: push it out of bounds
-            const uint32_t voff = (last_tail && ahigh[j & 3]) ? 0xfffffff0u : avoff[j & 3];
-            lds_dma16(arsrc, As + buf * kStage + (wave * kDmaPerWave + j) * 1024, voff,
-                      kcol + uint32_t(RPC * j) * uint32_t(g.K));
+            const uint32_t voff = (avoff[j & 3] + uint32_t(RPC * j) * uint32_t(g.K)) | pad |
+                                  (ahigh[j & 3] & tail);
+            lds_dma16(arsrc, As + buf * kStage + (wave * kDmaPerWave + j) * 1024, voff, kcol);
         }
     };
 
@@ -813,70 +858,86 @@ void gemm_kernel(GemmArgs g) {
 #pragma unroll
         for (int t = 0; t < TW; ++t) acc[i][t] = v4i{0, 0, 0, 0};
 
-    // fragment reads: row (wm*WA + 16i + lane%16), logical chunk 4jj + lane/16
+    // fragment reads: row (wm*WA + 16i + lane%16), logical chunk 4kk + lane/16
     const int8_t* afrag = As + (wm * WA + (lane & 15)) * KS;
-    int aslot[SPW];
+    int aslot[NK];
 #pragma unroll
-    for (int jj = 0; jj < SPW; ++jj) aslot[jj] = slot_of(lane & 15, 4 * jj + (lane >> 4)) * 16;
+    for (int kk = 0; kk < NK; ++kk) aslot[kk] = slot_of(lane & 15, 4 * kk + (lane >> 4)) * 16;
 
-    auto stage = [&](int s, const BVec (&bc)[TW], BVec (&bn)[TW]) {
-        const int cur = s & 1;
-        const bool more = s + 1 < nst;
-        if (more) {
-            load_a(cur ^ 1, s + 1);
-            load_b(bn, s + 1);
-        }
-        asm volatile("" ::: "memory");
-        const int8_t* abuf = afrag + cur * kStage;
+    // Software pipeline over NS stage buffers: the loads of stage s + NS - 1
+    // go out while stage s is consumed, so each load has NS - 1 stages of
+    // MFMAs to land. Stage s uses LDS buffer s % NS and weight registers
+    // b[s % NS]; the loop is unrolled by NS so both indices are static. The
+    // stage count is padded to a multiple of NS with stages that read zeros,
+    // so every stage issues the same loads and every wait count is a
+    // constant (conditional issues would make the compiler's own counts
+    // conservative and stall on loads just issued).
+    BVec b[NS][TW];
+    auto issue = [&](int buf, BVec (&bn)[TW], int s) {
+        const uint32_t pad = s < nst ? 0u : kNowhere;
+        load_b(bn, s, pad);   // weights first: the stage wait then covers both
+        load_a(buf, s, pad);
+    };
+    auto consume = [&](int buf, const BVec (&bc)[TW]) {
+        const int8_t* abuf = afrag + buf * kStage;
 #pragma unroll
-        for (int jj = 0; jj < SPW; ++jj) {
+        for (int kk = 0; kk < NK; ++kk) {
             v4i af[TA];
 #pragma unroll
-            for (int i = 0; i < TA; ++i) af[i] = lds_ld<v4i>(abuf + i * 16 * KS + aslot[jj]);
+            for (int i = 0; i < TA; ++i) af[i] = lds_ld<v4i>(abuf + i * 16 * KS + aslot[kk]);
 #pragma unroll
             for (int t = 0; t < TW; ++t) {
-                const v4i bf = unpack16(bc[t][jj]);
+                const v4i bf = unpack16(bc[t][kk]);
 #pragma unroll
                 for (int i = 0; i < TA; ++i) acc[i][t] = mfma16x16x64(bf, af[i], acc[i][t]);
             }
         }
-#if BT_GEMM_SCHED
-        // Optional fixed interleave (off by default: measured slower than the
-        // compiler's own order on the 64 x 64 tile): each MFMA followed by up
-        // to two VALU slots, fragment reads spread over the first MFMAs.
-#pragma unroll
-        for (int jj = 0; jj < SPW; ++jj) {
-#pragma unroll
-            for (int k = 0; k < TA; ++k) {
-                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // DS read
-                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
-                __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);   // VALU
-            }
-#pragma unroll
-            for (int k = 0; k < TA * TW - TA; ++k) {
-                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
-                __builtin_amdgcn_sched_group_barrier(0x002, 1, 0);   // VALU
-            }
-        }
-#endif
-        // the next stage's LDS copies and weight words must have landed
-        __builtin_amdgcn_s_waitcnt(0);
-        __syncthreads();
     };
 
-    BVec b0[TW], b1[TW];
-    load_a(0, 0);
-    load_b(b0, 0);
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    for (int s = 0; s < nst; s += 2) {
-        stage(s, b0, b1);
-        if (s + 1 < nst) stage(s + 1, b1, b0);
+    const int nst_pad = (nst + NS - 1) / NS * NS;
+#pragma unroll
+    for (int p = 0; p < NS - 1; ++p) issue(p, b[p], p);
+    for (int s0 = 0; s0 < nst_pad; s0 += NS) {
+#pragma unroll
+        for (int u = 0; u < NS; ++u) {
+            // Stage s0 + u: its loads have landed once at most the NS - 2
+            // later stages' are in flight; the barrier then also tells every
+            // wave that all are done with buffer (u - 1) % NS, refilled next.
+            __builtin_amdgcn_sched_barrier(0);
+            wait_vmcnt<(NS - 2) * kLoads>();
+            __builtin_amdgcn_s_barrier();
+            asm volatile("" ::: "memory");
+            __builtin_amdgcn_sched_barrier(0);
+            const int nb = (u + NS - 1) % NS;   // static once unrolled
+            issue(nb, b[nb], s0 + u + NS - 1);
+            asm volatile("" ::: "memory");
+            consume(u, b[u]);
+        }
     }
+    // the padding loads still in flight write zeros into LDS: let them land
+    // before the workgroup can exit
+    wait_vmcnt<0>();
 
     // epilogue: acc[i][t][r] = C[n = n0 + wn*WW + 16t + 4(l/16) + r][m = m0 + wm*WA + 16i + l%16]
     const int nq = n0 + wn * WW + 4 * (lane >> 4);
     const bool full = m0 + BM <= g.M && n0 + BN <= g.N && (g.N & 3) == 0;
+    if (kRowStores && full && !g.acc) {
+        float* ep = Ep + wave * (16 * 64);
+#pragma unroll
+        for (int i = 0; i < TA; ++i) {
+            const int64_t mb = m0 + wm * WA + 16 * i;
+            const int32_t qs = gld<int32_t>(g.xsum + mb + (lane & 15));
+            const float rs = gld<float>(g.xscale + mb + (lane & 15)) * g.w_scale;
+            v4f v[4];
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                const v4i a = acc[i][t] - qs;
+                v[t] = v4f{float(a.x) * rs, float(a.y) * rs, float(a.z) * rs, float(a.w) * rs};
+            }
+            gemm_store_block_rows(v, ep, g.y, g.N, mb, n0 + wn * WW, lane);
+        }
+        return;
+    }
 #pragma unroll
     for (int i = 0; i < TA; ++i) {
         const int64_t mm = m0 + wm * WA + 16 * i + (lane & 15);
@@ -906,6 +967,235 @@ void gemm_kernel(GemmArgs g) {
     }
 }
 
+// Persistent prefill GEMM. A workgroup of NW waves side by side along N
+// owns a WA x (WW*NW) output tile at a time and walks a run of tiles: the
+// tiles of one XCD's contiguous band, taken round-robin by that XCD's
+// workgroups (consecutive tiles share token rows, which stay in the XCD's
+// L2). Its stage pipeline runs straight across tile boundaries: while the
+// last stages of a tile are consumed, the first stages of the next tile are
+// already being loaded, so a tile costs no start-up latency and the epilogue
+// of one tile overlaps the loads of the next. Stages per tile are padded to a
+// multiple of NS with stages that read zeros (a buffer's range check turns
+// their loads into no-ops), which keeps every stage's wait count constant.
+template <int WA, int WW, int NW, int KS, int NS>
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void gemm_persistent_kernel(GemmArgs g) {
+    constexpr int BM = WA;
+    constexpr int BN = WW * NW;
+    constexpr int TA = WA / 16;
+    constexpr int TW = WW / 16;
+    constexpr int NK = KS / 64;
+    constexpr int CPR = KS / 16;
+    constexpr int kStage = BM * KS;
+    constexpr int kDmaPerWave = BM * CPR / 64 / NW;
+    constexpr int kLoads = TW + kDmaPerWave;
+    static_assert(KS == 128 || KS == 256, "stage width");
+    static_assert(WA % 16 == 0 && WW % 16 == 0, "wave tile");
+    static_assert(NS >= 2 && (NS - 2) * kLoads < 64, "pipeline depth");
+    static_assert(kDmaPerWave * 64 * NW == BM * CPR, "A stage must split evenly over waves");
+    __shared__ __attribute__((aligned(16))) int8_t As[NS * kStage];
+    constexpr bool kRowStores = WW == 64;   // row-wise epilogue through LDS
+    __shared__ __attribute__((aligned(16))) float Ep[kRowStores ? NW * 16 * 64 : 4];
+
+    auto slot_of = [](int r, int c) {
+        return KS == 256 ? (c ^ (r & 15)) : (c ^ ((r >> 1) & 7));
+    };
+
+    // this workgroup's tiles: first, first + per_wg, ... below hi
+    const int xcd = blockIdx.x % kXcds;
+    const int per_wg = int(gridDim.x) / kXcds;
+    const int total = g.m_tiles * g.n_tiles;
+    const int lo = xcd * g.per_xcd;
+    const int hi = min(lo + g.per_xcd, total);
+    const int first = lo + int(blockIdx.x) / kXcds;
+    if (first >= hi) return;
+    const int count = (hi - first + per_wg - 1) / per_wg;
+
+    const int tid = threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lane = tid & 63;
+    const uint32_t tile_bytes = uint32_t(g.steps) * 1024u;
+    const int nst = (g.K + KS - 1) / KS;
+    const int nst_pad = (nst + NS - 1) / NS * NS;
+
+    // Buffers of a tile: its token rows and this wave's weight tiles. Rows
+    // past M and weight tiles past N read as zero (range check).
+    auto tile_rsrc = [&](int tile_id, __amdgpu_buffer_rsrc_t& ra, __amdgpu_buffer_rsrc_t& rw) {
+        const int mt = tile_id / g.n_tiles;
+        const int nt = tile_id - mt * g.n_tiles;
+        const int64_t m0 = int64_t(mt) * BM;
+        const int t0 = min(nt * (BN / bt::kTileN) + wave * TW, g.tiles - 1);
+        ra = make_rsrc(g.xq + m0 * g.K, uint32_t(min(int64_t(BM), int64_t(g.M) - m0)) * uint32_t(g.K));
+        rw = make_rsrc(g.w + int64_t(t0) * tile_bytes, uint32_t(min(TW, g.tiles - t0)) * tile_bytes);
+    };
+
+    constexpr uint32_t kNowhere = 0x80000000u;
+    using BVec = typename std::conditional<KS == 256, v4u, v2u>::type;
+    auto load_b = [&](BVec (&b)[TW], __amdgpu_buffer_rsrc_t rw, int s, uint32_t pad) {
+        const uint32_t koff = KS == 256 ? uint32_t(s) * 1024u
+                                        : uint32_t(s >> 1) * 1024u + uint32_t(s & 1) * 8u;
+#pragma unroll
+        for (int t = 0; t < TW; ++t) {
+            const uint32_t voff = (uint32_t(lane) * 16u + uint32_t(t) * tile_bytes) | pad;
+            if constexpr (KS == 256)
+                b[t] = buf_ld16u(rw, voff, koff);
+            else
+                b[t] = __builtin_bit_cast(
+                    v2u, __builtin_amdgcn_raw_buffer_load_b64(rw, int(voff), int(koff), 0));
+        }
+    };
+    constexpr int RPC = 64 / CPR;
+    const int r0 = wave * kDmaPerWave * RPC + lane / CPR;
+    uint32_t avoff[4];
+    uint32_t ahigh[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const int r = r0 + RPC * q;
+        const int c = slot_of(r, lane % CPR);
+        avoff[q] = uint32_t(r0) * uint32_t(g.K) + uint32_t(c) * 16u;
+        ahigh[q] = c >= 8 ? kNowhere : 0u;
+    }
+    const bool tail128 = KS == 256 && (g.K & 255) != 0;
+    auto load_a = [&](int buf, __amdgpu_buffer_rsrc_t ra, int s, uint32_t pad) {
+        const uint32_t kcol = uint32_t(s) * KS;
+        const uint32_t tail = (tail128 && s == nst - 1) ? 0xffffffffu : 0u;
+#pragma unroll
+        for (int j = 0; j < kDmaPerWave; ++j) {
+            const uint32_t voff = (avoff[j & 3] + uint32_t(RPC * j) * uint32_t(g.K)) | pad |
+                                  (ahigh[j & 3] & tail);
+            lds_dma16(ra, As + buf * kStage + (wave * kDmaPerWave + j) * 1024, voff, kcol);
+        }
+    };
+
+    v4i acc[TA][TW];
+#pragma unroll
+    for (int i = 0; i < TA; ++i)
+#pragma unroll
+        for (int t = 0; t < TW; ++t) acc[i][t] = v4i{0, 0, 0, 0};
+    const int8_t* afrag = As + (lane & 15) * KS;
+    int aslot[NK];
+#pragma unroll
+    for (int kk = 0; kk < NK; ++kk) aslot[kk] = slot_of(lane & 15, 4 * kk + (lane >> 4)) * 16;
+    auto consume = [&](int buf, const BVec (&bc)[TW]) {
+        const int8_t* abuf = afrag + buf * kStage;
+#pragma unroll
+        for (int kk = 0; kk < NK; ++kk) {
+            v4i af[TA];
+#pragma unroll
+            for (int i = 0; i < TA; ++i) af[i] = lds_ld<v4i>(abuf + i * 16 * KS + aslot[kk]);
+#pragma unroll
+            for (int t = 0; t < TW; ++t) {
+                const v4i bf = unpack16(bc[t][kk]);
+#pragma unroll
+                for (int i = 0; i < TA; ++i) acc[i][t] = mfma16x16x64(bf, af[i], acc[i][t]);
+            }
+        }
+    };
+
+    BVec b[NS][TW];
+    __amdgpu_buffer_rsrc_t ra_cur, rw_cur, ra_nxt, rw_nxt;
+    tile_rsrc(first, ra_cur, rw_cur);
+#pragma unroll
+    for (int p = 0; p < NS - 1; ++p) {
+        const uint32_t pad = p < nst ? 0u : kNowhere;
+        load_b(b[p], rw_cur, p, pad);
+        load_a(p, ra_cur, p, pad);
+    }
+
+    for (int k = 0; k < count; ++k) {
+        const int tile_id = first + k * per_wg;
+        const bool has_next = k + 1 < count;
+        tile_rsrc(has_next ? tile_id + per_wg : tile_id, ra_nxt, rw_nxt);
+        const int mt = tile_id / g.n_tiles;
+        const int nt = tile_id - mt * g.n_tiles;
+        const int64_t m0 = int64_t(mt) * BM;
+        const int n0 = nt * BN;
+
+        // the epilogue's per-token row sums and scales, fetched early
+        int32_t qs[TA];
+        float rs[TA];
+#pragma unroll
+        for (int i = 0; i < TA; ++i) {
+            const int64_t mc = min(m0 + 16 * i + (lane & 15), int64_t(g.M) - 1);
+            qs[i] = gld<int32_t>(g.xsum + mc);
+            rs[i] = gld<float>(g.xscale + mc) * g.w_scale;
+        }
+
+        for (int s0 = 0; s0 < nst_pad; s0 += NS) {
+#pragma unroll
+            for (int u = 0; u < NS; ++u) {
+                // stage s0 + u: wait for its loads (the NS - 2 later stages'
+                // may stay in flight), then a barrier, after which every wave
+                // is also done with buffer (u - 1) % NS, refilled next
+                __builtin_amdgcn_sched_barrier(0);
+                wait_vmcnt<(NS - 2) * kLoads>();
+                __builtin_amdgcn_s_barrier();
+                asm volatile("" ::: "memory");
+                __builtin_amdgcn_sched_barrier(0);
+                const int nb = (u + NS - 1) % NS;   // static once unrolled
+                const int tgt = s0 + u + NS - 1;
+                const bool in_cur = tgt < nst_pad;
+                const int st = in_cur ? tgt : tgt - nst_pad;
+                const bool valid = st < nst && (in_cur || has_next);
+                const uint32_t pad = valid ? 0u : kNowhere;
+                load_b(b[nb], in_cur ? rw_cur : rw_nxt, st, pad);
+                load_a(nb, in_cur ? ra_cur : ra_nxt, st, pad);
+                asm volatile("" ::: "memory");
+                consume(u, b[u]);
+            }
+        }
+
+        // epilogue: acc[i][t][r] = C[n = n0 + wave*WW + 16t + 4(l/16) + r][m = m0 + 16i + l%16]
+        const int nq = n0 + wave * WW + 4 * (lane >> 4);
+        const bool full = m0 + BM <= g.M && n0 + BN <= g.N && (g.N & 3) == 0;
+        const bool rows = kRowStores && full && !g.acc;
+#pragma unroll
+        for (int i = 0; i < TA; ++i) {
+            const int64_t mm = m0 + 16 * i + (lane & 15);
+            if (rows) {
+                v4f v[4];
+#pragma unroll
+                for (int t = 0; t < 4; ++t) {
+                    const v4i a = acc[i][t] - qs[i];
+                    const float r = rs[i];
+                    v[t] = v4f{float(a.x) * r, float(a.y) * r, float(a.z) * r, float(a.w) * r};
+                }
+                gemm_store_block_rows(v, Ep + wave * (16 * 64), g.y, g.N, m0 + 16 * i,
+                                      n0 + wave * WW, lane);
+            } else if (full || mm < g.M) {
+                float* yrow = g.y + mm * g.N;
+                int32_t* arow = g.acc ? g.acc + mm * g.N : nullptr;
+#pragma unroll
+                for (int t = 0; t < TW; ++t) {
+                    const int n = nq + 16 * t;
+                    const v4i a = acc[i][t] - qs[i];
+                    const float r = rs[i];
+                    const v4f yv = {float(a.x) * r, float(a.y) * r, float(a.z) * r, float(a.w) * r};
+                    if (full) {
+                        __builtin_nontemporal_store(yv, (BT_GLOBAL v4f*)(yrow + n));
+                        if (arow) __builtin_nontemporal_store(a, (BT_GLOBAL v4i*)(arow + n));
+                    } else {
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            if (n + e < g.N) {
+                                gst<float>(yrow + n + e, yv[e]);
+                                if (arow) gst<int32_t>(arow + n + e, a[e]);
+                            }
+                        }
+                    }
+                }
+            }
+#pragma unroll
+            for (int t = 0; t < TW; ++t) acc[i][t] = v4i{0, 0, 0, 0};
+        }
+        ra_cur = ra_nxt;
+        rw_cur = rw_nxt;
+    }
+    // the padding loads still in flight write zeros into LDS: let them land
+    // before the workgroup can exit
+    wait_vmcnt<0>();
+}
+
 #ifndef BT_GEMM_WA
 #define BT_GEMM_WA 128
 #endif
@@ -913,19 +1203,23 @@ void gemm_kernel(GemmArgs g) {
 #define BT_GEMM_WW 64
 #endif
 #ifndef BT_GEMM_WGM
-#define BT_GEMM_WGM 2
+#define BT_GEMM_WGM 1
 #endif
 #ifndef BT_GEMM_WGN
-#define BT_GEMM_WGN 2
+#define BT_GEMM_WGN 4
 #endif
 #ifndef BT_GEMM_KS
 #define BT_GEMM_KS 128
 #endif
+#ifndef BT_GEMM_NS
+#define BT_GEMM_NS 2
+#endif
+
 
 // Shape dispatch of the GEMM: the default tile, or a 128 x 128 tile (waves of
 // 64 x 64) when the default leaves fewer than two workgroups per compute unit
 // (e.g. 4096 x 1536 outputs).
-template <int WA, int WW, int WGM, int WGN, int KS>
+template <int WA, int WW, int WGM, int WGN, int KS, int NS>
 bt_status launch_gemm(GemmArgs g, hipStream_t stream) {
     constexpr int BM = WA * WGM;
     constexpr int BN = WW * WGN;
@@ -936,17 +1230,78 @@ bt_status launch_gemm(GemmArgs g, hipStream_t stream) {
     const int64_t grid = int64_t(g.per_xcd) * kXcds;
     if (grid > (int64_t(1) << 31) - 1) return BT_ERR_SHAPE;
     (void)hipGetLastError();
-    hipLaunchKernelGGL((gemm_kernel<WA, WW, WGM, WGN, KS>), dim3(unsigned(grid)),
+    hipLaunchKernelGGL((gemm_kernel<WA, WW, WGM, WGN, KS, NS>), dim3(unsigned(grid)),
                        dim3(64 * WGM * WGN), 0, stream, g);
     return hipGetLastError() == hipSuccess ? BT_OK : BT_ERR_DEVICE;
 }
 
+#ifndef BT_GEMM_PERSISTENT
+#define BT_GEMM_PERSISTENT 1
+#endif
+#ifndef BT_GEMM_P_WA
+#define BT_GEMM_P_WA 128
+#endif
+#ifndef BT_GEMM_P_NW
+#define BT_GEMM_P_NW 4
+#endif
+#ifndef BT_GEMM_P_NS
+#define BT_GEMM_P_NS 3
+#endif
+#ifndef BT_GEMM_P_WGS_PER_CU
+#define BT_GEMM_P_WGS_PER_CU 2
+#endif
+
+// Compute units of the current device, read once per device.
+int device_cus() {
+    static int cus[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (cus[dev] == 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+            n <= 0)
+            n = 256;
+        cus[dev] = n;
+    }
+    return cus[dev];
+}
+
+template <int WA, int WW, int NW, int KS, int NS>
+bt_status launch_gemm_persistent(GemmArgs g, hipStream_t stream) {
+    constexpr int BM = WA;
+    constexpr int BN = WW * NW;
+    g.m_tiles = int32_t(bt::ceil_div(g.M, BM));
+    g.n_tiles = int32_t(bt::ceil_div(g.N, BN));
+    const int64_t total = int64_t(g.m_tiles) * g.n_tiles;
+    if (total > (int64_t(1) << 31) - 1) return BT_ERR_SHAPE;
+    g.per_xcd = int32_t(bt::ceil_div(total, kXcds));
+    // one workgroup per resident slot, a multiple of the XCD count, and no
+    // more than there are tiles in an XCD's band
+    const int64_t slots = int64_t(device_cus()) * BT_GEMM_P_WGS_PER_CU / kXcds;
+    const int64_t per_xcd_wgs = std::max<int64_t>(1, std::min<int64_t>(slots, g.per_xcd));
+    (void)hipGetLastError();
+    hipLaunchKernelGGL((gemm_persistent_kernel<WA, WW, NW, KS, NS>),
+                       dim3(unsigned(per_xcd_wgs * kXcds)), dim3(64 * NW), 0, stream, g);
+    return hipGetLastError() == hipSuccess ? BT_OK : BT_ERR_DEVICE;
+}
+
 bt_status dispatch_gemm(const GemmArgs& g, hipStream_t stream) {
+#if BT_GEMM_PERSISTENT
+    {
+        constexpr int BM = BT_GEMM_P_WA;
+        constexpr int BN = 64 * BT_GEMM_P_NW;
+        const int64_t tiles = bt::ceil_div(g.M, BM) * bt::ceil_div(g.N, BN);
+        if (tiles >= 2 * int64_t(device_cus()))
+            return launch_gemm_persistent<BT_GEMM_P_WA, 64, BT_GEMM_P_NW, 128, BT_GEMM_P_NS>(g,
+                                                                                        stream);
+    }
+#endif
     constexpr int BM = BT_GEMM_WA * BT_GEMM_WGM;
     constexpr int BN = BT_GEMM_WW * BT_GEMM_WGN;
     const int64_t blocks = bt::ceil_div(g.M, BM) * bt::ceil_div(g.N, BN);
-    if (blocks < 512) return launch_gemm<64, 64, 2, 2, 256>(g, stream);
-    return launch_gemm<BT_GEMM_WA, BT_GEMM_WW, BT_GEMM_WGM, BT_GEMM_WGN, BT_GEMM_KS>(g, stream);
+    if (blocks < 512) return launch_gemm<64, 64, 2, 2, 256, 2>(g, stream);
+    return launch_gemm<BT_GEMM_WA, BT_GEMM_WW, BT_GEMM_WGM, BT_GEMM_WGN, BT_GEMM_KS, BT_GEMM_NS>(
+        g, stream);
 }
 
 bt_status launched() {

@@ -199,6 +199,15 @@ def test_gemm_shapes(dev, m, n, k):
     check_full(synth.small_problem(4, m, n, k, "t3", (0.3, 0.4, 0.3)), dev)
 
 
+# Shapes with enough output tiles for the persistent GEMM (several tiles per
+# workgroup, pipeline crossing tile boundaries), with ragged M, N a multiple
+# of 4 but not of the tile, N not a multiple of 4, and stage counts that are
+# and are not a multiple of the pipeline depth. Every output is compared.
+@pytest.mark.parametrize("m,n,k", [(4133, 4100, 384), (4100, 4099, 256), (4096, 8192, 640)])
+def test_gemm_many_tiles_ragged(dev, m, n, k):
+    check_full(synth.small_problem(5, m, n, k, "t3", (0.3, 0.4, 0.3)), dev)
+
+
 @pytest.mark.parametrize("proj", [0, 1, 2, 3])
 def test_prefill_one_layer(dev, proj):
     check_full(synth.prefill_problem(proj), dev)
