@@ -97,6 +97,25 @@ size_t bt_repacked_bytes(int64_t N, int64_t K);
 bt_status bt_repack_ternary(const uint8_t* packed_dev, int64_t N, int64_t K, void* wdev,
                             hipStream_t stream);
 
+/* The same repack for many tensors in one launch (a model's weights at load
+ * time: one launch instead of one per tensor, which for the decoder's 112
+ * tensors of 0.6-7 MB would otherwise be bound by launch gaps). A plan is
+ * built on the host, copied by the caller into device memory (same bytes),
+ * and launched: plan_host sizes the grid, plan_dev is read by the kernel.
+ * Each descriptor obeys bt_repack_ternary's rules; errors are reported by
+ * bt_repack_plan_build before anything is launched. */
+typedef struct bt_repack_desc {
+    const uint8_t* packed_dev;   /* device, bt_packed_bytes(N,K) canonical bytes */
+    void* wdev;                  /* device, bt_repacked_bytes(N,K) bytes, written */
+    int64_t N, K;
+} bt_repack_desc;
+
+size_t bt_repack_plan_bytes(int32_t count);
+bt_status bt_repack_plan_build(const bt_repack_desc* descs, int32_t count, void* plan_host,
+                               size_t plan_bytes);
+bt_status bt_repack_ternary_grouped(const void* plan_host, const void* plan_dev,
+                                    hipStream_t stream);
+
 /* ---------------------------------------------------------------------------
  * Per-token absmax INT8 quantization (technical report section 2.2.2:
  * activations quantized to INT8 online per token).

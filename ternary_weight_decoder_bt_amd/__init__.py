@@ -15,6 +15,7 @@ from .ops import (  # noqa: F401
     GROUP_K,
     MatmulPlan,
     QuantPlan,
+    RepackPlan,
     matmul_workspace_bytes,
     new_workspace,
     pack_ternary,

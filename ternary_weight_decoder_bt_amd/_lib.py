@@ -31,6 +31,9 @@ SIGNATURES = {
     "bt_ternary_matmul": (C.c_int, [_i64, _i64, _i64, _p, _p, _p, _p, _f, _p, _p, _p, _sz, _p]),
     "bt_ternary_matmul_fused": (C.c_int, [_i64, _i64, _i64, _p, _p, _f, _p, _p, _p, _p, _p, _p,
                                           _sz, _p]),
+    "bt_repack_plan_bytes": (_sz, [_i32]),
+    "bt_repack_plan_build": (C.c_int, [_p, _i32, _p, _sz]),
+    "bt_repack_ternary_grouped": (C.c_int, [_p, _p, _p]),
     "bt_quant_plan_bytes": (_sz, [_i32]),
     "bt_quant_plan_build": (C.c_int, [_p, _i32, _p, _sz]),
     "bt_quantize_act_grouped": (C.c_int, [_p, _p, _p]),
@@ -39,6 +42,10 @@ SIGNATURES = {
     "bt_matmul_plan_build": (C.c_int, [_p, _i32, _p, _sz, _p, _sz]),
     "bt_ternary_matmul_grouped": (C.c_int, [_p, _p, _p]),
 }
+
+
+class BtRepackDesc(C.Structure):
+    _fields_ = [("packed_dev", _p), ("wdev", _p), ("N", _i64), ("K", _i64)]
 
 
 class BtQuantDesc(C.Structure):

@@ -149,6 +149,39 @@ extern "C" size_t bt_matmul_workspace_bytes(int64_t M, int64_t N, int64_t K) {
 
 // ------------------------------------------------------------------ plans
 
+extern "C" size_t bt_repack_plan_bytes(int32_t count) {
+    if (count < 1) return 0;
+    return sizeof(bt::PlanHeader) + size_t(count) * sizeof(bt::RepackDesc);
+}
+
+extern "C" bt_status bt_repack_plan_build(const bt_repack_desc* descs, int32_t count,
+                                          void* plan_host, size_t plan_bytes) {
+    if (!descs || !plan_host) return BT_ERR_NULL;
+    if (count < 1) return BT_ERR_SHAPE;
+    if (plan_bytes < bt_repack_plan_bytes(count)) return BT_ERR_WORKSPACE;
+    for (int32_t i = 0; i < count; ++i) {
+        const bt_repack_desc& r = descs[i];
+        if (!r.packed_dev || !r.wdev) return BT_ERR_NULL;
+        if (!valid_nk(r.N, r.K)) return BT_ERR_SHAPE;
+        if (!bt::aligned16(r.packed_dev) || !bt::aligned16(r.wdev)) return BT_ERR_ALIGN;
+    }
+    auto* hdr = static_cast<bt::PlanHeader*>(plan_host);
+    auto* out = reinterpret_cast<bt::RepackDesc*>(hdr + 1);
+    int64_t blocks = 0;
+    for (int32_t i = 0; i < count; ++i) {
+        const bt_repack_desc& r = descs[i];
+        const int64_t steps = bt::ceil_div(r.K, bt::kSuperK);
+        const int64_t nb = bt::ceil_div(r.N, bt::kTileN) * steps;
+        out[i] = bt::RepackDesc{r.packed_dev, static_cast<uint8_t*>(r.wdev), int32_t(r.N),
+                                int32_t(r.K), int32_t(steps), 0, blocks, nb};
+        blocks += nb;
+    }
+    hdr->magic = bt::kPlanMagicRepack;
+    hdr->count = count;
+    hdr->total_blocks = blocks;
+    return BT_OK;
+}
+
 extern "C" size_t bt_quant_plan_bytes(int32_t count) {
     if (count < 1) return 0;
     return sizeof(bt::PlanHeader) + size_t(count) * sizeof(bt::QuantDesc);

@@ -18,6 +18,7 @@ constexpr int kQuantThreads = 256;  // threads per quantized row
 constexpr uint32_t kPlanMagicQuant = 0x42545141u;   // "AQTB"
 constexpr uint32_t kPlanMagicGemv = 0x42544d47u;    // "GMTB"
 constexpr uint32_t kPlanMagicGemvFused = 0x42544646u;   // "FFTB"
+constexpr uint32_t kPlanMagicRepack = 0x4254504bu;      // "KPTB"
 
 inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
@@ -69,6 +70,16 @@ struct QuantDesc {
     int32_t* xsum;
     int64_t M, K;
     int64_t row_begin;      // first workgroup (= row) of this problem in a grouped launch
+};
+
+struct RepackDesc {
+    const uint8_t* packed;
+    uint8_t* out;
+    int32_t N, K;
+    int32_t steps;          // ceil(K / 256): 1 KB output blocks per 16-row tile
+    int32_t pad_;
+    int64_t block_begin;    // first output block of this tensor in a grouped launch
+    int64_t blocks;         // ceil(N / 16) * steps
 };
 
 struct PlanHeader {

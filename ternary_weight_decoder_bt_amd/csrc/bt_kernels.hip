@@ -109,31 +109,114 @@ __device__ __forceinline__ void lds_st(void* p, T v) {
 
 // ------------------------------------------------------------------ repack
 
-// One thread per output word. Word (tile t, step S, lane l, word jj) gathers
-// the 16 codes of row 16t + l%16 at K = k0 .. k0+15, k0 = 256S + 64jj + 16(l/16).
-// In the canonical layout those 16 elements share one bit pair (k0 % 128) / 32
-// of 16 consecutive bytes starting at byte 32*(k0/128) + k0 % 32 of the row.
-__global__ __launch_bounds__(256) void repack_kernel(const uint8_t* __restrict__ packed, int32_t N,
-                                                     int32_t K, int32_t Kp, int64_t total_words,
-                                                     uint32_t* __restrict__ out) {
-    for (int64_t gid = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; gid < total_words;
-         gid += int64_t(gridDim.x) * blockDim.x) {
-        const int64_t t = gid / Kp;                 // a tile holds Kp words
-        const int32_t d = int32_t(gid - t * Kp);
-        const int32_t S = d >> 8;
-        const int32_t lane = (d & 255) >> 2;
-        const int32_t jj = d & 3;
-        const int64_t n = t * bt::kTileN + (lane & 15);
-        const int32_t k0 = bt::kSuperK * S + bt::kStepK * jj + 16 * (lane >> 4);
-        uint32_t word = 0x55555555u;   // padding: code 1 = weight 0
-        if (n < N && k0 < K) {
-            const uint8_t* row = packed + n * (K / 4);
-            const uint4 c = *reinterpret_cast<const uint4*>(row + 32 * (k0 >> 7) + (k0 & 31));
-            const int sh = 2 * ((k0 & 127) >> 5);
-            word = ((c.x >> sh) & kLow2) | (((c.y >> sh) & kLow2) << 2) |
-                   (((c.z >> sh) & kLow2) << 4) | (((c.w >> sh) & kLow2) << 6);
+// One wave per 1 KB output block (16-row tile t, 256-wide step S); lane l
+// writes its 16 bytes, the four words jj = 0..3 of row r = 16t + l%16 at
+// K = 256S + 64jj + 16q + e (q = l/16, e = 0..15). In the canonical layout
+// those 16 elements are the 16 consecutive bytes starting at byte
+// 32(jj/2) + 16(q%2) of the row's 64-byte piece for step S, at bit pair
+// 2(jj%2) + q/2. So a lane reads two 16-byte chunks of its row (jj = 0, 1
+// share one, jj = 2, 3 the other) and the wave reads its 16 rows' pieces
+// whole; padding rows and columns get code 1 (weight 0).
+// The two canonical 16-byte chunks lane l needs for output block blk (zero
+// where the block is padding; `valid` says which halves are real).
+struct RepackIn {
+    uint4 c[2];
+    bool valid[2];
+};
+
+__device__ __forceinline__ RepackIn repack_load(const uint8_t* __restrict__ packed, int32_t N,
+                                                int32_t K, int32_t steps, int64_t blk, int lane) {
+    const int r = lane & 15;
+    const int q = lane >> 4;
+    const int64_t t = blk / steps;
+    const int32_t S = int32_t(blk - t * steps);
+    const int64_t n = t * bt::kTileN + r;
+    RepackIn in;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const int64_t k0 = int64_t(bt::kSuperK) * S + 128 * h;   // group 2S + h
+        in.valid[h] = n < N && k0 < K;
+        in.c[h] = in.valid[h] ? *reinterpret_cast<const uint4*>(packed + n * (K / 4) + k0 / 4 +
+                                                                16 * (q & 1))
+                              : uint4{0, 0, 0, 0};
+    }
+    return in;
+}
+
+__device__ __forceinline__ void repack_store(const RepackIn& in, uint8_t* __restrict__ out,
+                                             int64_t blk, int lane) {
+    const int q = lane >> 4;
+    uint32_t w[4];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const uint4 c = in.c[h];
+#pragma unroll
+        for (int jl = 0; jl < 2; ++jl) {
+            const int sh = 2 * (2 * jl + (q >> 1));
+            w[2 * h + jl] = in.valid[h] ? ((c.x >> sh) & kLow2) | (((c.y >> sh) & kLow2) << 2) |
+                                              (((c.z >> sh) & kLow2) << 4) |
+                                              (((c.w >> sh) & kLow2) << 6)
+                                        : 0x55555555u;   // padding: code 1 = weight 0
         }
-        out[gid] = word;
+    }
+    *reinterpret_cast<uint4*>(out + blk * 1024 + lane * 16) = uint4{w[0], w[1], w[2], w[3]};
+}
+
+#ifndef BT_REPACK_PER_WAVE
+#define BT_REPACK_PER_WAVE 8
+#endif
+constexpr int kRepackPerWave = BT_REPACK_PER_WAVE;   // output blocks a wave handles per pass
+
+__global__ __launch_bounds__(256) void repack_kernel(const uint8_t* __restrict__ packed, int32_t N,
+                                                     int32_t K, int32_t steps, int64_t blocks,
+                                                     uint8_t* __restrict__ out) {
+    const int lane = threadIdx.x & 63;
+    const int64_t waves = (int64_t(gridDim.x) * blockDim.x) >> 6;
+    for (int64_t b0 = ((int64_t(blockIdx.x) * blockDim.x + threadIdx.x) >> 6) * kRepackPerWave;
+         b0 < blocks; b0 += waves * kRepackPerWave) {
+        RepackIn in[kRepackPerWave];
+#pragma unroll
+        for (int u = 0; u < kRepackPerWave; ++u)
+            in[u] = repack_load(packed, N, K, steps, min(b0 + u, blocks - 1), lane);
+#pragma unroll
+        for (int u = 0; u < kRepackPerWave; ++u)
+            if (b0 + u < blocks) repack_store(in[u], out, b0 + u, lane);
+    }
+}
+
+// Many tensors in one launch: a wave takes runs of global output blocks and
+// finds each block's tensor with one lane per descriptor (64 offsets compared
+// at once, counted with a ballot) instead of a chain of dependent loads.
+__global__ __launch_bounds__(256) void repack_grouped_kernel(
+    const bt::RepackDesc* __restrict__ descs, int32_t count, int64_t total_blocks) {
+    const int lane = threadIdx.x & 63;
+    const int64_t waves = (int64_t(gridDim.x) * blockDim.x) >> 6;
+    for (int64_t b0 = ((int64_t(blockIdx.x) * blockDim.x + threadIdx.x) >> 6) * kRepackPerWave;
+         b0 < total_blocks; b0 += waves * kRepackPerWave) {
+        int idx[kRepackPerWave];
+#pragma unroll
+        for (int u = 0; u < kRepackPerWave; ++u) idx[u] = -1;
+        for (int base = 0; base < count; base += 64) {
+            const int i = base + lane;
+            const int64_t begin = i < count ? descs[i].block_begin : INT64_MAX;
+#pragma unroll
+            for (int u = 0; u < kRepackPerWave; ++u)
+                idx[u] += __popcll(__ballot(begin <= min(b0 + u, total_blocks - 1)));
+        }
+        RepackIn in[kRepackPerWave];
+#pragma unroll
+        for (int u = 0; u < kRepackPerWave; ++u) {
+            const bt::RepackDesc& d = descs[idx[u]];
+            in[u] = repack_load(d.packed, d.N, d.K, d.steps,
+                                min(b0 + u, total_blocks - 1) - d.block_begin, lane);
+        }
+#pragma unroll
+        for (int u = 0; u < kRepackPerWave; ++u) {
+            if (b0 + u < total_blocks) {
+                const bt::RepackDesc& d = descs[idx[u]];
+                repack_store(in[u], d.out, b0 + u - d.block_begin, lane);
+            }
+        }
     }
 }
 
@@ -1319,12 +1402,30 @@ extern "C" bt_status bt_repack_ternary(const uint8_t* packed_dev, int64_t N, int
     if (!packed_dev || !wdev) return BT_ERR_NULL;
     if (!nk_ok(N, K)) return BT_ERR_SHAPE;
     if (!bt::aligned16(packed_dev) || !bt::aligned16(wdev)) return BT_ERR_ALIGN;
-    const int64_t Kp = bt::ceil_div(K, bt::kSuperK) * bt::kSuperK;
-    const int64_t words = bt::ceil_div(N, bt::kTileN) * Kp;   // 16 rows * Kp/4 bytes / 4
-    const int64_t blocks = std::min<int64_t>(bt::ceil_div(words, 256), int64_t(1) << 20);
+    const int64_t steps = bt::ceil_div(K, bt::kSuperK);
+    const int64_t blocks = bt::ceil_div(N, bt::kTileN) * steps;   // 1 KB output blocks
+    const int64_t grid = std::min<int64_t>(bt::ceil_div(blocks, 4 * kRepackPerWave), int64_t(1) << 20);
     (void)hipGetLastError();
-    hipLaunchKernelGGL(repack_kernel, dim3(unsigned(blocks)), dim3(256), 0, stream, packed_dev,
-                       int32_t(N), int32_t(K), int32_t(Kp), words, static_cast<uint32_t*>(wdev));
+    hipLaunchKernelGGL(repack_kernel, dim3(unsigned(grid)), dim3(256), 0, stream, packed_dev,
+                       int32_t(N), int32_t(K), int32_t(steps), blocks,
+                       static_cast<uint8_t*>(wdev));
+    return launched();
+}
+
+extern "C" bt_status bt_repack_ternary_grouped(const void* plan_host, const void* plan_dev,
+                                               hipStream_t stream) {
+    if (!plan_host || !plan_dev) return BT_ERR_NULL;
+    const auto* hdr = static_cast<const bt::PlanHeader*>(plan_host);
+    if (hdr->magic != bt::kPlanMagicRepack || hdr->count < 1 || hdr->total_blocks < 1)
+        return BT_ERR_VALUE;
+    if (!bt::aligned16(plan_dev)) return BT_ERR_ALIGN;
+    const auto* descs = reinterpret_cast<const bt::RepackDesc*>(
+        static_cast<const char*>(plan_dev) + sizeof(bt::PlanHeader));
+    const int64_t grid = std::min<int64_t>(bt::ceil_div(hdr->total_blocks, 4 * kRepackPerWave),
+                                           int64_t(1) << 20);
+    (void)hipGetLastError();
+    hipLaunchKernelGGL(repack_grouped_kernel, dim3(unsigned(grid)), dim3(256), 0, stream, descs,
+                       hdr->count, hdr->total_blocks);
     return launched();
 }
 

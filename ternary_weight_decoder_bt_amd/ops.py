@@ -11,7 +11,7 @@ import ctypes as C
 
 import numpy as np
 
-from ._lib import BtMatmulDesc, BtQuantDesc, BtError, check, lib
+from ._lib import BtMatmulDesc, BtQuantDesc, BtRepackDesc, BtError, check, lib
 
 GROUP_K = 128
 GEMV_MAX_M = 16
@@ -202,6 +202,34 @@ class _Plan:
         return _np_ptr(self.host), _ptr(self.dev)
 
 
+class RepackPlan(_Plan):
+    """Many device repacks in one launch (bt_repack_ternary_grouped).
+
+    items: sequence of (packed_dev, n, k, out) with out a uint8 CUDA tensor of
+    repacked_bytes(n, k) bytes.
+    """
+
+    def __init__(self, items):
+        torch = _torch()
+        descs = (BtRepackDesc * len(items))()
+        self._keep = list(items)
+        for i, (packed, n, k, out) in enumerate(items):
+            _dev(packed, torch.uint8, None, "packed_dev")
+            if packed.numel() != packed_bytes(n, k):
+                raise ValueError("packed_dev must hold N*K/4 bytes")
+            _dev(out, torch.uint8, (repacked_bytes(n, k),), "out")
+            descs[i] = BtRepackDesc(_ptr(packed), _ptr(out), n, k)
+        nbytes = int(lib().bt_repack_plan_bytes(len(items)))
+        host = np.zeros(nbytes, np.uint8)
+        check(lib().bt_repack_plan_build(descs, len(items), _np_ptr(host), nbytes),
+              "bt_repack_plan_build")
+        super().__init__(host, items[0][0].device)
+
+    def launch(self, stream=None):
+        h, d = self._ptrs()
+        check(lib().bt_repack_ternary_grouped(h, d, _stream(stream)), "bt_repack_ternary_grouped")
+
+
 class QuantPlan(_Plan):
     """Many independent quantizations in one launch (bt_quantize_act_grouped).
 
@@ -260,6 +288,6 @@ class MatmulPlan(_Plan):
 __all__ = [
     "BtError", "GROUP_K", "GEMV_MAX_M", "packed_bytes", "repacked_bytes",
     "matmul_workspace_bytes", "pack_ternary", "unpack_ternary", "repack_ternary",
-    "quantize_act", "new_workspace", "ternary_matmul", "ternary_matmul_fused", "QuantPlan",
-    "MatmulPlan",
+    "quantize_act", "new_workspace", "ternary_matmul", "ternary_matmul_fused", "RepackPlan",
+    "QuantPlan", "MatmulPlan",
 ]

@@ -96,6 +96,35 @@ def check_full(case, dev, mode="f64", wdev=None):
     return y, acc
 
 
+# ------------------------------------------------------------------- repack
+
+def test_grouped_repack_matches_single_and_oracle(dev):
+    """One grouped launch gives every tensor the same bytes as its own repack
+    (ragged N, K with a half 256-wide step, the decoder's shapes), twice in a
+    row, and the grouped output drives the matmul to the oracle's result."""
+    rng = np.random.default_rng(7)
+    items, singles = [], []
+    for n, k in [(2048, 1536), (40, 384), (17, 128), (1536, 8960), (33, 640)]:
+        w = rng.integers(-1, 2, size=(n, k), dtype=np.int8)
+        packed = to_dev(bt.pack_ternary(w).reshape(-1), dev)
+        singles.append(bt.repack_ternary(packed, n, k))
+        out = torch.full((bt.repacked_bytes(n, k),), 0xAB, dtype=torch.uint8, device=dev)
+        items.append((packed, n, k, out))
+    plan = bt.RepackPlan(items)
+    for _ in range(2):
+        for *_, out in items:
+            out.fill_(0xAB)
+        plan.launch()
+        torch.cuda.synchronize()
+        for (_, n, k, out), single in zip(items, singles):
+            assert torch.equal(out, single), (n, k)
+    c = synth.small_problem(6, 5, 40, 384, "outlier")
+    packed = to_dev(bt.pack_ternary(c["w"]).reshape(-1), dev)
+    out = torch.empty(bt.repacked_bytes(40, 384), dtype=torch.uint8, device=dev)
+    bt.RepackPlan([(packed, 40, 384, out)]).launch()
+    check_full(c, dev, wdev=out)
+
+
 # ------------------------------------------------------------ quantization
 
 def test_quantize_single_gemv_input(dev):

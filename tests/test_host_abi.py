@@ -16,7 +16,7 @@ import pytest
 import oracle
 import ternary_weight_decoder_bt_amd as bt
 from ternary_weight_decoder_bt_amd import _lib
-from ternary_weight_decoder_bt_amd._lib import BtMatmulDesc, BtQuantDesc
+from ternary_weight_decoder_bt_amd._lib import BtMatmulDesc, BtQuantDesc, BtRepackDesc
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "bt.h")
@@ -48,6 +48,7 @@ def test_struct_layouts_match_header_sizes():
     # two int64 + pointer fields; no padding surprises between C and ctypes
     assert C.sizeof(BtQuantDesc) == 6 * 8
     assert C.sizeof(BtMatmulDesc) == 3 * 8 + 4 * 8 + 8 + 3 * 8
+    assert C.sizeof(BtRepackDesc) == 4 * 8
 
 
 def test_status_strings():
@@ -196,6 +197,39 @@ def test_plan_building_on_host():
     assert first_k == 8960
     # a launch with a plan of the wrong kind is refused on the host
     assert L.bt_quantize_act_grouped(host.ctypes.data, f, None) == VALUE
+
+
+def test_repack_plan_building_on_host():
+    L = bt.lib()
+    f = FAKE
+    r = (BtRepackDesc * 3)(BtRepackDesc(f, f, 2048, 1536), BtRepackDesc(f, f, 40, 384),
+                           BtRepackDesc(f, f, 1536, 8960))
+    nb = L.bt_repack_plan_bytes(3)
+    assert nb == 16 + 3 * 48
+    host = np.zeros(nb, np.uint8)
+    assert L.bt_repack_plan_build(r, 3, host.ctypes.data, nb) == OK
+    assert host[:4].view(np.uint32)[0] == 0x4254504B
+    # 1 KB output blocks: ceil(N/16) tiles x ceil(K/256) steps, summed
+    blocks = 128 * 6 + 3 * 2 + 96 * 35
+    assert host[8:16].view(np.int64)[0] == blocks
+    # RepackDesc: 2 pointers, N, K, steps, pad (int32), then block_begin, blocks (int64)
+    d = host[16:].reshape(3, 48)
+    assert d[1, 32:40].view(np.int64)[0] == 128 * 6 and d[2, 40:48].view(np.int64)[0] == 96 * 35
+    assert L.bt_repack_plan_build(r, 3, host.ctypes.data, nb - 1) == WORKSPACE
+    assert L.bt_repack_plan_build(r, 0, host.ctypes.data, nb) == SHAPE
+    r[1].K = 200                                 # K must be a multiple of 128
+    assert L.bt_repack_plan_build(r, 3, host.ctypes.data, nb) == SHAPE
+    r[1].K = 384
+    r[2].wdev = f + 8
+    assert L.bt_repack_plan_build(r, 3, host.ctypes.data, nb) == ALIGN
+    r[2].wdev = None
+    assert L.bt_repack_plan_build(r, 3, host.ctypes.data, nb) == NULL
+    # a launch with a plan of the wrong kind is refused on the host
+    q = (BtQuantDesc * 1)(BtQuantDesc(f, f, f, f, 3, 1536))
+    qb = np.zeros(L.bt_quant_plan_bytes(1), np.uint8)
+    assert L.bt_quant_plan_build(q, 1, qb.ctypes.data, qb.size) == OK
+    assert L.bt_repack_ternary_grouped(qb.ctypes.data, f, None) == VALUE
+    assert L.bt_repack_ternary_grouped(None, f, None) == NULL
 
 
 def test_binding_has_no_cpu_fallback():
