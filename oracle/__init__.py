@@ -21,3 +21,9 @@ from .ternary_ref import (  # noqa: F401
     dequant_ref,
     forward_ref,
 )
+from .fused_ref import (  # noqa: F401
+    rmsnorm_sumsq,
+    rmsnorm_scale,
+    rmsnorm_scaled_ref,
+    rmsnorm_quantize_ref,
+)
