@@ -285,6 +285,30 @@ class LongPrefill:
             res[name] = (ms, 2 * self.m * p["n"] * p["k"] / (ms * 1e-3) / 1e12)
         return res
 
+    def time_activation_prologues(self, reps: int = 20):
+        """Per-token quantization of layer 0's qkv (K=1536) and down (K=8960) inputs,
+        plain and fused with RMS normalization: {name: (ms, GB/s)}."""
+        torch, bt = self.torch, self.bt
+        res = {}
+        for p in (self.probs[0], self.probs[3]):
+            m, k = self.m, p["k"]
+            g = torch.linspace(0.5, 1.5, k, device=p["x"].device)
+            for name, call, extra in (
+                    ("quantize", lambda: bt.quantize_act(p["x"], p["xq"], p["xs"], p["xsum"]), 0),
+                    ("rmsnorm_quantize", lambda: bt.rmsnorm_quantize(p["x"], g, 1e-6, p["xq"],
+                                                                     p["xs"], p["xsum"]), 4 * k)):
+                call()
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record()
+                for _ in range(reps):
+                    call()
+                e1.record()
+                torch.cuda.synchronize()
+                ms = e0.elapsed_time(e1) / reps
+                nbytes = 4 * m * k + m * k + 8 * m + extra
+                res[f"{name}_M{m}_K{k}"] = (ms, nbytes / (ms * 1e-3) / 1e9)
+        return res
+
     def parity(self):
         """Sampled oracle comparison (rows and columns) on the first and last projection."""
         import oracle
@@ -560,6 +584,9 @@ def main():
         tops = lp.ops / (ms * 1e-3) / 1e12
         gemm_tops = lp.ops / (gemm_ms * 1e-3) / 1e12
         shapes = lp.time_shapes()
+        prologues = lp.time_activation_prologues()
+        for k_, (ms_, gbs) in prologues.items():
+            log(f"{k_}: {ms_ * 1e3:.1f} us ({gbs:.0f} GB/s, {100 * gbs / HBM_PEAK_GBS:.1f}% of HBM)")
         log(f"prefill: {ms:.3f} ms/stack ({tops:.0f} TOPS), GEMMs {gemm_ms:.3f} ms ({gemm_tops:.0f} TOPS)")
         out["prefill"] = {
             "workload": "long prefill, M=4096 tokens x 28 layers x 4 projections (quantize + GEMM "
@@ -571,6 +598,10 @@ def main():
             "parity_ok": pf_ok, "steps": args.prefill_steps,
             "gemm_tops_per_shape": {k: round(v[1], 1) for k, v in shapes.items()},
             "gemm_us_per_shape": {k: round(v[0] * 1e3, 2) for k, v in shapes.items()},
+            "activation_prologues": {
+                k: {"us": round(v[0] * 1e3, 2), "gb_per_s": round(v[1], 1),
+                    "pct_of_hbm_peak": round(100 * v[1] / HBM_PEAK_GBS, 2)}
+                for k, v in prologues.items()},
             "roofline": {"bound": "mfma",
                          "kernel": "gemm_persistent_kernel (gate_up) + gemm_kernel (qkv, o, down)",
                          "achieved": round(gemm_tops, 2), "peak": I8_PEAK_TOPS,

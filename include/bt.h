@@ -147,6 +147,20 @@ bt_status bt_quantize_act(const float* x, int64_t M, int64_t K, int8_t* xq, floa
  *   must be ordered on one stream.
  * w_scale must be finite (BT_ERR_VALUE otherwise).
  * ------------------------------------------------------------------------- */
+/* RMS normalization with a per-channel scale fused with the quantization above
+ * ("VibeVoice-ASR-BitNet Technical Report" section 2.4.1: rms_norm_scaled, an
+ * RMS normalization with a scale parameter; section 2.2.2: INT8 activations
+ * per token). Per row m, with S = sum_k x[m,k]^2 taken in fp64 (each square is
+ * exact; any summation order):
+ *   ms = fl32(S / K); r = fl32(1 / fl32(sqrt(fl32(ms + eps)))), or r = 0 if
+ *   that is not finite; h[k] = fl32(fl32(x[m,k] * r) * g[k]);
+ * then h is quantized exactly as bt_quantize_act quantizes x (q, d, row sum).
+ * h itself is not written. x: device fp32 M x K; g: device fp32 [K]; eps: fp32,
+ * finite and >= 0 (BT_ERR_VALUE otherwise); xq, xscale, xsum as in
+ * bt_quantize_act. Same shape and alignment rules as bt_quantize_act. */
+bt_status bt_rmsnorm_quantize(const float* x, const float* g, float eps, int64_t M, int64_t K,
+                              int8_t* xq, float* xscale, int32_t* xsum, hipStream_t stream);
+
 size_t bt_matmul_workspace_bytes(int64_t M, int64_t N, int64_t K);
 
 /* Quantization fused into the GEMV (M <= BT_GEMV_MAX_M): the same result as

@@ -23,6 +23,7 @@ from .ops import (  # noqa: F401
     quantize_act,
     repack_ternary,
     repacked_bytes,
+    rmsnorm_quantize,
     ternary_matmul,
     ternary_matmul_fused,
     unpack_ternary,

@@ -27,6 +27,7 @@ SIGNATURES = {
     "bt_repacked_bytes": (_sz, [_i64, _i64]),
     "bt_repack_ternary": (C.c_int, [_p, _i64, _i64, _p, _p]),
     "bt_quantize_act": (C.c_int, [_p, _i64, _i64, _p, _p, _p, _p]),
+    "bt_rmsnorm_quantize": (C.c_int, [_p, _p, _f, _i64, _i64, _p, _p, _p, _p]),
     "bt_matmul_workspace_bytes": (_sz, [_i64, _i64, _i64]),
     "bt_ternary_matmul": (C.c_int, [_i64, _i64, _i64, _p, _p, _p, _p, _f, _p, _p, _p, _sz, _p]),
     "bt_ternary_matmul_fused": (C.c_int, [_i64, _i64, _i64, _p, _p, _f, _p, _p, _p, _p, _p, _p,

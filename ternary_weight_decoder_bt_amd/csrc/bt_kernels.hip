@@ -392,6 +392,171 @@ __global__ __launch_bounds__(bt::kQuantThreads) void quantize_wave_rows_kernel(
     }
 }
 
+// ----------------------------------- RMS normalization fused with quantization
+//
+// "rms_norm_scaled" (technical report section 2.4.1: RMS normalization with a
+// scale parameter) feeding the per-token INT8 quantization (section 2.2.2), in
+// one pass over x: h = fl32(fl32(x * r) * g) with r = fl32(1 / fl32(sqrt(fl32(
+// ms + eps)))), ms = fl32(S / K), S the sum of squares in fp64 (each fp32
+// square is exact in fp64, so only the additions round); a row whose r is not
+// finite gets r = 0. h is then quantized exactly as quantize_row does, and the
+// normalized row is never written to memory.
+
+__device__ __forceinline__ double wave_sum_f64(double v) {
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
+    return v;
+}
+
+__device__ __forceinline__ double sumsq4(v4f v) {
+    const double a = v.x, b = v.y, c = v.z, d = v.w;
+    return ((a * a + b * b) + c * c) + d * d;
+}
+
+__device__ __forceinline__ float rms_factor(double S, int64_t K, float eps) {
+    const float ms = float(S / double(K));
+    const float r = 1.0f / sqrtf(ms + eps);
+    return r <= FLT_MAX ? r : 0.0f;   // not finite (or NaN) -> 0
+}
+
+struct RmsShared {
+    double s[bt::kQuantThreads / 64];
+    QuantShared q;
+};
+
+__device__ __forceinline__ double block_sum_f64(double v, RmsShared& sh) {
+    v = wave_sum_f64(v);
+    const int w = threadIdx.x >> 6;
+    if ((threadIdx.x & 63) == 0) sh.s[w] = v;
+    __syncthreads();
+    double r = sh.s[0];
+#pragma unroll
+    for (int i = 1; i < bt::kQuantThreads / 64; ++i) r += sh.s[i];
+    return r;
+}
+
+// One wave per row (K % 4 == 0, K <= 2048), rows in registers.
+__global__ __launch_bounds__(bt::kQuantThreads) void rmsnorm_quantize_wave_rows_kernel(
+    const float* __restrict__ x, const float* __restrict__ g, float eps, int64_t M, int64_t K,
+    int8_t* __restrict__ xq, float* __restrict__ xscale, int32_t* __restrict__ xsum) {
+    const int lane = threadIdx.x & 63;
+    const int64_t m = int64_t(blockIdx.x) * (bt::kQuantThreads / 64) + (threadIdx.x >> 6);
+    if (m >= M) return;
+    const int64_t K4 = K >> 2;
+    const float* xr = x + m * K;
+    v4f v[kWaveRowRegs];
+    double ss = 0.0;
+#pragma unroll
+    for (int j = 0; j < kWaveRowRegs; ++j) {
+        const int64_t i = lane + 64 * j;
+        v[j] = i < K4 ? gld<v4f>(xr + 4 * i) : v4f{0.0f, 0.0f, 0.0f, 0.0f};
+        ss += sumsq4(v[j]);
+    }
+    const float r = rms_factor(wave_sum_f64(ss), K, eps);
+    float amax = 0.0f;
+#pragma unroll
+    for (int j = 0; j < kWaveRowRegs; ++j) {
+        const int64_t i = lane + 64 * j;
+        if (i < K4) {
+            v[j] = (v[j] * r) * gld<v4f>(g + 4 * i);
+            amax = fmaxf(amax, fmaxf(fmaxf(fabsf(v[j].x), fabsf(v[j].y)),
+                                     fmaxf(fabsf(v[j].z), fabsf(v[j].w))));
+        }
+    }
+    amax = wave_max(amax);
+    float inv = 127.0f / amax;
+    const bool dead = !(inv <= FLT_MAX);
+    if (dead) inv = 0.0f;
+    int s = 0;
+    int* qr = reinterpret_cast<int*>(xq + m * K);
+#pragma unroll
+    for (int j = 0; j < kWaveRowRegs; ++j) {
+        const int64_t i = lane + 64 * j;
+        if (i < K4) {
+            const int a = quant1(v[j].x * inv), b = quant1(v[j].y * inv);
+            const int c = quant1(v[j].z * inv), d = quant1(v[j].w * inv);
+            gst<int>(qr + i, pack4(a, b, c, d));
+            s += a + b + c + d;
+        }
+    }
+    s = wave_sum(s);
+    if (lane == 0) {
+        gst<float>(xscale + m, dead ? 0.0f : amax / 127.0f);
+        if (xsum) gst<int32_t>(xsum + m, s);
+    }
+}
+
+// One workgroup per row: the row in registers when K % 4 == 0 and K <= 9216,
+// else three passes over x and g (sum of squares, absmax of h, quantize).
+__global__ __launch_bounds__(bt::kQuantThreads) void rmsnorm_quantize_kernel(
+    const float* __restrict__ x, const float* __restrict__ g, float eps, int64_t K,
+    int8_t* __restrict__ xq, float* __restrict__ xscale, int32_t* __restrict__ xsum) {
+    __shared__ RmsShared sh;
+    const int64_t m = blockIdx.x;
+    const float* xr = x + m * K;
+    int8_t* qrow = xq + m * K;
+    const int tid = threadIdx.x;
+    constexpr int T = bt::kQuantThreads;
+    const int64_t K4 = K >> 2;
+    float amax = 0.0f;
+    int s = 0;
+    if ((K & 3) == 0 && K4 <= int64_t(kQuantRegs) * T) {
+        v4f v[kQuantRegs];
+        double ss = 0.0;
+#pragma unroll
+        for (int i = 0; i < kQuantRegs; ++i) {
+            const int64_t idx = tid + int64_t(i) * T;
+            v[i] = idx < K4 ? gld<v4f>(xr + 4 * idx) : v4f{0.0f, 0.0f, 0.0f, 0.0f};
+            ss += sumsq4(v[i]);
+        }
+        const float r = rms_factor(block_sum_f64(ss, sh), K, eps);
+#pragma unroll
+        for (int i = 0; i < kQuantRegs; ++i) {
+            const int64_t idx = tid + int64_t(i) * T;
+            if (idx < K4) {
+                v[i] = (v[i] * r) * gld<v4f>(g + 4 * idx);
+                amax = fmaxf(amax, fmaxf(fmaxf(fabsf(v[i].x), fabsf(v[i].y)),
+                                         fmaxf(fabsf(v[i].z), fabsf(v[i].w))));
+            }
+        }
+        amax = block_max(amax, sh.q);
+        float inv = 127.0f / amax;
+        if (!(inv <= FLT_MAX)) inv = 0.0f;
+#pragma unroll
+        for (int i = 0; i < kQuantRegs; ++i) {
+            const int64_t idx = tid + int64_t(i) * T;
+            if (idx < K4) {
+                const int a = quant1(v[i].x * inv), b = quant1(v[i].y * inv);
+                const int c = quant1(v[i].z * inv), d = quant1(v[i].w * inv);
+                reinterpret_cast<int*>(qrow)[idx] = pack4(a, b, c, d);
+                s += a + b + c + d;
+            }
+        }
+    } else {
+        double ss = 0.0;
+        for (int64_t k = tid; k < K; k += T) {
+            const double a = xr[k];
+            ss += a * a;
+        }
+        const float r = rms_factor(block_sum_f64(ss, sh), K, eps);
+        for (int64_t k = tid; k < K; k += T) amax = fmaxf(amax, fabsf((xr[k] * r) * g[k]));
+        amax = block_max(amax, sh.q);
+        float inv = 127.0f / amax;
+        if (!(inv <= FLT_MAX)) inv = 0.0f;
+        for (int64_t k = tid; k < K; k += T) {
+            const int a = quant1(((xr[k] * r) * g[k]) * inv);
+            qrow[k] = int8_t(a);
+            s += a;
+        }
+    }
+    s = block_sum(s, sh.q);
+    if (tid == 0) {
+        const bool dead = !(127.0f / amax <= FLT_MAX);
+        xscale[m] = dead ? 0.0f : amax / 127.0f;
+        if (xsum) xsum[m] = s;
+    }
+}
+
 __global__ __launch_bounds__(bt::kQuantThreads) void quantize_grouped_kernel(
     const QuantDesc* __restrict__ descs, int32_t count) {
     __shared__ QuantShared sh;
@@ -1445,6 +1610,29 @@ extern "C" bt_status bt_quantize_act(const float* x, int64_t M, int64_t K, int8_
     } else {
         hipLaunchKernelGGL(quantize_kernel, dim3(unsigned(M)), dim3(bt::kQuantThreads), 0, stream,
                            x, K, xq, xscale, xsum);
+    }
+    return launched();
+}
+
+extern "C" bt_status bt_rmsnorm_quantize(const float* x, const float* g, float eps, int64_t M,
+                                         int64_t K, int8_t* xq, float* xscale, int32_t* xsum,
+                                         hipStream_t stream) {
+    if (!x || !g || !xq || !xscale) return BT_ERR_NULL;
+    if (M < 1 || K < 1 || M > (int64_t(1) << 31) - 1 || K > (int64_t(1) << 30))
+        return BT_ERR_SHAPE;
+    if (!bt::aligned16(x) || !bt::aligned16(g) || !bt::aligned16(xq) || !bt::aligned16(xscale) ||
+        (xsum && !bt::aligned16(xsum)))
+        return BT_ERR_ALIGN;
+    if (!isfinite(eps) || eps < 0.0f) return BT_ERR_VALUE;
+    (void)hipGetLastError();
+    if (K % 4 == 0 && K / 4 <= 64 * kWaveRowRegs) {
+        const int64_t rows_per_wg = bt::kQuantThreads / 64;
+        hipLaunchKernelGGL(rmsnorm_quantize_wave_rows_kernel,
+                           dim3(unsigned(bt::ceil_div(M, rows_per_wg))), dim3(bt::kQuantThreads),
+                           0, stream, x, g, eps, M, K, xq, xscale, xsum);
+    } else {
+        hipLaunchKernelGGL(rmsnorm_quantize_kernel, dim3(unsigned(M)), dim3(bt::kQuantThreads), 0,
+                           stream, x, g, eps, K, xq, xscale, xsum);
     }
     return launched();
 }

@@ -125,6 +125,29 @@ def quantize_act(x, xq=None, xscale=None, xsum=None, stream=None):
     return xq, xscale, xsum
 
 
+def rmsnorm_quantize(x, g, eps: float, xq=None, xscale=None, xsum=None, stream=None):
+    """RMS normalization with per-channel scale g, then per-token INT8 quantization,
+    in one launch (bt_rmsnorm_quantize): returns (int8 (M, K), fp32 (M,), int32 (M,))."""
+    torch = _torch()
+    _dev(x, torch.float32, None, "x")
+    if x.dim() != 2:
+        raise ValueError("x must be (M, K)")
+    m, k = x.shape
+    _dev(g, torch.float32, (k,), "g")
+    if xq is None:
+        xq = torch.empty((m, k), dtype=torch.int8, device=x.device)
+    if xscale is None:
+        xscale = torch.empty(m, dtype=torch.float32, device=x.device)
+    if xsum is None:
+        xsum = torch.empty(m, dtype=torch.int32, device=x.device)
+    _dev(xq, torch.int8, (m, k), "xq")
+    _dev(xscale, torch.float32, (m,), "xscale")
+    _dev(xsum, torch.int32, (m,), "xsum")
+    check(lib().bt_rmsnorm_quantize(_ptr(x), _ptr(g), float(eps), m, k, _ptr(xq), _ptr(xscale),
+                                    _ptr(xsum), _stream(stream)), "bt_rmsnorm_quantize")
+    return xq, xscale, xsum
+
+
 def new_workspace(m: int, n: int, k: int, device="cuda"):
     """Zero-filled workspace for bt_ternary_matmul (None when none is needed)."""
     torch = _torch()
@@ -288,6 +311,6 @@ class MatmulPlan(_Plan):
 __all__ = [
     "BtError", "GROUP_K", "GEMV_MAX_M", "packed_bytes", "repacked_bytes",
     "matmul_workspace_bytes", "pack_ternary", "unpack_ternary", "repack_ternary",
-    "quantize_act", "new_workspace", "ternary_matmul", "ternary_matmul_fused", "RepackPlan",
+    "quantize_act", "rmsnorm_quantize", "new_workspace", "ternary_matmul", "ternary_matmul_fused", "RepackPlan",
     "QuantPlan", "MatmulPlan",
 ]

@@ -123,6 +123,13 @@ def test_device_entry_points_validate_before_launch():
     assert L.bt_quantize_act(f, 0, 128, f, f, f, None) == SHAPE
     assert L.bt_quantize_act(f, 1, 0, f, f, f, None) == SHAPE
     assert L.bt_quantize_act(f, 1, 128, f + 1, f, f, None) == ALIGN
+    # RMS normalization + quantize
+    assert L.bt_rmsnorm_quantize(f, None, 1e-6, 1, 128, f, f, f, None) == NULL
+    assert L.bt_rmsnorm_quantize(f, f, 1e-6, 0, 128, f, f, f, None) == SHAPE
+    assert L.bt_rmsnorm_quantize(f, f + 4, 1e-6, 1, 128, f, f, f, None) == ALIGN
+    assert L.bt_rmsnorm_quantize(f, f, -1.0, 1, 128, f, f, f, None) == VALUE
+    assert L.bt_rmsnorm_quantize(f, f, float("nan"), 1, 128, f, f, f, None) == VALUE
+    assert L.bt_rmsnorm_quantize(f, f, float("inf"), 1, 128, f, f, f, None) == VALUE
     # matmul
     args = lambda **kw: [kw.get("M", 1), kw.get("N", 16), kw.get("K", 128), kw.get("xq", f),
                          kw.get("xs", f), kw.get("xsum", f), kw.get("w", f),
