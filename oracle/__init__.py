@@ -26,4 +26,5 @@ from .fused_ref import (  # noqa: F401
     rmsnorm_scale,
     rmsnorm_scaled_ref,
     rmsnorm_quantize_ref,
+    epilogue_ref,
 )

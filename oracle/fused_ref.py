@@ -28,9 +28,21 @@ Readings where the pages are silent (each also listed in the design notes):
   one fp32 unit of ms, and only a row whose S lies that close to an fp32
   rounding boundary can round ms differently.
 
-Every function here is pinned in tests/test_oracle_pins.py by closed forms
-(constant rows, power-of-two scalings, eps inside the root) and a hand-worked
-example (tests/golden/rmsnorm_worked.txt), not by re-typed formulas.
+* The fused epilogues of section 2.4.1 applied to the matmul's fp32 output y:
+  ``mul_mat_add_relu`` (matrix multiply + bias + ReLU) and ``add_scaled``
+  (residual addition with layer-scale multiplication). Order and precision,
+  each step one fp32 operation: y1 = fl32(y + bias[n]); y2 = y1 if y1 > 0
+  else +0;
+  y3 = fl32(gamma[n] * y2); out = fl32(residual[m, n] + y3). The layer scale
+  multiplies the branch before the residual is added, as in the ConvNeXt
+  blocks the report's tokenizer is built from (section 2.2.1). Every step is
+  optional.
+
+Every function here is pinned in tests/test_oracle_pins_fused.py by closed
+forms (constant rows, power-of-two scalings, eps inside the root, exact small
+integers through the epilogue) and hand-worked examples
+(tests/golden/rmsnorm_worked.txt, tests/golden/epilogue_worked.txt), not by
+re-typed formulas.
 """
 
 from __future__ import annotations
@@ -83,3 +95,33 @@ def rmsnorm_quantize_ref(x: np.ndarray, g: np.ndarray, eps: float):
     """RMS normalization with scale, then the per-token INT8 quantization:
     (q int8 (M, K), d fp32 (M,), qsum int32 (M,))."""
     return quantize_ref(rmsnorm_scaled_ref(x, g, eps))
+
+
+def epilogue_ref(y: np.ndarray, bias=None, relu: bool = False, layer_scale=None,
+                 residual=None) -> np.ndarray:
+    """fp32 y (M, N) -> fp32 out (M, N): bias add, ReLU, layer scale, residual add,
+    in that order, each optional and each one fp32 operation."""
+    y = np.asarray(y, dtype=np.float32)
+    if y.ndim != 2:
+        raise OracleError("y must be (M, N)")
+    n = y.shape[1]
+    out = y
+    if bias is not None:
+        bias = np.asarray(bias, dtype=np.float32)
+        if bias.shape != (n,):
+            raise OracleError("bias must hold one value per output")
+        out = (out + bias[None, :]).astype(np.float32)
+    if relu:
+        # y if y > 0 else +0: a negative zero comes out as +0
+        out = np.where(out > 0, out, np.float32(0)).astype(np.float32)
+    if layer_scale is not None:
+        layer_scale = np.asarray(layer_scale, dtype=np.float32)
+        if layer_scale.shape != (n,):
+            raise OracleError("the layer scale must hold one value per output")
+        out = (layer_scale[None, :] * out).astype(np.float32)
+    if residual is not None:
+        residual = np.asarray(residual, dtype=np.float32)
+        if residual.shape != y.shape:
+            raise OracleError("the residual must have the output's shape")
+        out = (residual + out).astype(np.float32)
+    return out

@@ -142,3 +142,55 @@ def test_pins_detect_planted_sum_instead_of_mean(monkeypatch):
     _planted(monkeypatch, wrong)
     with pytest.raises(AssertionError):
         test_rmsnorm_constant_rows_closed_form()
+
+
+# ------------------------------------------------------------- epilogues
+
+def _epi_golden(golden):
+    return {r[0]: np.array(r[1:], np.float64) for r in golden("epilogue_worked.txt")}
+
+
+def test_epilogue_matches_hand_worked_golden(golden):
+    from oracle import ternary_ref as tr
+    v = _epi_golden(golden)
+    y = tr.dequant_ref(v["acc"].astype(np.int64)[None, :], np.float32(v["d"]), np.float32(v["s_w"]))
+    assert np.array_equal(y[0], v["y"].astype(np.float32))
+    b, gm, res = (v[k].astype(np.float32) for k in ("bias", "gamma", "residual"))
+    assert np.array_equal(fused.epilogue_ref(y, bias=b, relu=True)[0], v["bias_relu"])
+    assert np.array_equal(fused.epilogue_ref(y, b, True, gm, res[None, :])[0], v["all"])
+    assert np.array_equal(fused.epilogue_ref(y, b, False, gm, res[None, :])[0], v["all_no_relu"])
+
+
+def test_epilogue_closed_forms():
+    rng = np.random.default_rng(7)
+    y = rng.standard_normal((4, 50)).astype(np.float32)
+    assert np.array_equal(fused.epilogue_ref(y), y)                                  # identity
+    assert (fused.epilogue_ref(-np.abs(y) - 1, relu=True) == 0).all()                # ReLU
+    assert np.array_equal(fused.epilogue_ref(np.abs(y), relu=True), np.abs(y))
+    assert np.array_equal(fused.epilogue_ref(y, layer_scale=np.full(50, 0.25, np.float32)),
+                          y / 4)                                                     # exact 2^-2
+    assert np.array_equal(fused.epilogue_ref(y, residual=np.zeros_like(y)), y)
+    # integers stay exact through every step
+    yi = rng.integers(-1000, 1000, (3, 20)).astype(np.float32)
+    bi = rng.integers(-50, 50, 20).astype(np.float32)
+    gi = rng.integers(-4, 5, 20).astype(np.float32)
+    ri = rng.integers(-9, 9, (3, 20)).astype(np.float32)
+    want = ri + gi * np.maximum(yi + bi, 0)
+    assert np.array_equal(fused.epilogue_ref(yi, bi, True, gi, ri), want)
+
+
+def test_pins_detect_planted_scale_after_residual(monkeypatch, golden):
+    def wrong(y, bias=None, relu=False, layer_scale=None, residual=None):
+        out = y + bias if bias is not None else y
+        out = np.maximum(out, 0) if relu else out
+        out = out + residual if residual is not None else out
+        return (out * layer_scale).astype(np.float32) if layer_scale is not None else out
+    monkeypatch.setattr(fused, "epilogue_ref", wrong)
+    with pytest.raises(AssertionError):
+        test_epilogue_matches_hand_worked_golden(golden)
+
+
+def test_epilogue_relu_gives_positive_zero():
+    y = np.array([[-0.0, 0.0, -1e-30, 2.0]], np.float32)
+    out = fused.epilogue_ref(y, relu=True)
+    assert np.array_equal(out, [[0, 0, 0, 2]]) and not np.signbit(out).any()
