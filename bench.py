@@ -285,6 +285,34 @@ class LongPrefill:
             res[name] = (ms, 2 * self.m * p["n"] * p["k"] / (ms * 1e-3) / 1e12)
         return res
 
+    def time_epilogues(self, reps: int = 20):
+        """Layer 0's gate_up with bias + ReLU and down with layer scale + residual add
+        (the fused epilogues), each against the same GEMM without: {name: (ms, TOPS)}."""
+        torch, bt = self.torch, self.bt
+        res = {}
+        for p, kind in ((self.probs[2], "bias_relu"), (self.probs[3], "scale_residual")):
+            n = p["n"]
+            vec = torch.linspace(-1, 1, n, device=p["y"].device)
+            resid = torch.ones_like(p["y"])
+            if kind == "bias_relu":
+                kw = dict(bias=vec, relu=True)
+            else:
+                kw = dict(layer_scale=vec, residual=resid)
+            name = synth.PROJECTIONS[p["proj"]][0]
+            for tag, extra in (("plain", {}), (kind, kw)):
+                call = lambda: bt.ternary_matmul(p["xq"], p["xs"], p["xsum"], p["wdev"], n, p["s"],
+                                                 y=p["y"], **extra)
+                call()
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record()
+                for _ in range(reps):
+                    call()
+                e1.record()
+                torch.cuda.synchronize()
+                ms = e0.elapsed_time(e1) / reps
+                res[f"{name}_{tag}"] = (ms, 2 * self.m * n * p["k"] / (ms * 1e-3) / 1e12)
+        return res
+
     def time_activation_prologues(self, reps: int = 20):
         """Per-token quantization of layer 0's qkv (K=1536) and down (K=8960) inputs,
         plain and fused with RMS normalization: {name: (ms, GB/s)}."""
@@ -585,6 +613,9 @@ def main():
         gemm_tops = lp.ops / (gemm_ms * 1e-3) / 1e12
         shapes = lp.time_shapes()
         prologues = lp.time_activation_prologues()
+        epilogues = lp.time_epilogues()
+        for k_, (ms_, tops_) in epilogues.items():
+            log(f"gemm {k_}: {ms_ * 1e3:.1f} us ({tops_:.0f} TOPS)")
         for k_, (ms_, gbs) in prologues.items():
             log(f"{k_}: {ms_ * 1e3:.1f} us ({gbs:.0f} GB/s, {100 * gbs / HBM_PEAK_GBS:.1f}% of HBM)")
         log(f"prefill: {ms:.3f} ms/stack ({tops:.0f} TOPS), GEMMs {gemm_ms:.3f} ms ({gemm_tops:.0f} TOPS)")
@@ -598,6 +629,8 @@ def main():
             "parity_ok": pf_ok, "steps": args.prefill_steps,
             "gemm_tops_per_shape": {k: round(v[1], 1) for k, v in shapes.items()},
             "gemm_us_per_shape": {k: round(v[0] * 1e3, 2) for k, v in shapes.items()},
+            "gemm_epilogues": {k: {"us": round(v[0] * 1e3, 2), "tops": round(v[1], 1)}
+                               for k, v in epilogues.items()},
             "activation_prologues": {
                 k: {"us": round(v[0] * 1e3, 2), "gb_per_s": round(v[1], 1),
                     "pct_of_hbm_peak": round(100 * v[1] / HBM_PEAK_GBS, 2)}

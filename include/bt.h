@@ -180,6 +180,31 @@ bt_status bt_ternary_matmul(int64_t M, int64_t N, int64_t K, const int8_t* xq,
                             float w_scale, float* y, int32_t* acc, void* workspace,
                             size_t workspace_bytes, hipStream_t stream);
 
+/* The fused epilogues of the technical report's section 2.4.1 on the output
+ * ("mul_mat_add_relu": matrix multiply + bias + ReLU; "add_scaled": residual
+ * addition with layer-scale multiplication). With y the plain output above,
+ * each step one fp32 operation and each optional:
+ *   y1 = fl32(y + bias[n]);  y2 = relu ? (y1 > 0 ? y1 : +0) : y1;
+ *   y3 = fl32(layer_scale[n] * y2);  out[m,n] = fl32(residual[m,n] + y3).
+ * acc, when requested, is still the plain int32 sum. bias and layer_scale are
+ * device fp32 [N], residual device fp32 M x N (row-major); each may be NULL and
+ * must be 16-byte aligned. residual may be y itself (an in-place residual
+ * update) but must not partly overlap it (BT_ERR_VALUE). */
+typedef struct bt_epilogue {
+    const float* bias;
+    const float* layer_scale;
+    const float* residual;
+    int32_t relu;
+    int32_t reserved;       /* set to 0 */
+} bt_epilogue;
+
+/* bt_ternary_matmul followed by the epilogue *epi (host memory; NULL = none). */
+bt_status bt_ternary_matmul_epilogue(int64_t M, int64_t N, int64_t K, const int8_t* xq,
+                                     const float* xscale, const int32_t* xsum, const void* wdev,
+                                     float w_scale, const bt_epilogue* epi, float* y,
+                                     int32_t* acc, void* workspace, size_t workspace_bytes,
+                                     hipStream_t stream);
+
 /* ---------------------------------------------------------------------------
  * Grouped launches: many independent projections in one kernel launch.
  *

@@ -30,6 +30,8 @@ SIGNATURES = {
     "bt_rmsnorm_quantize": (C.c_int, [_p, _p, _f, _i64, _i64, _p, _p, _p, _p]),
     "bt_matmul_workspace_bytes": (_sz, [_i64, _i64, _i64]),
     "bt_ternary_matmul": (C.c_int, [_i64, _i64, _i64, _p, _p, _p, _p, _f, _p, _p, _p, _sz, _p]),
+    "bt_ternary_matmul_epilogue": (C.c_int, [_i64, _i64, _i64, _p, _p, _p, _p, _f, _p, _p, _p,
+                                             _p, _sz, _p]),
     "bt_ternary_matmul_fused": (C.c_int, [_i64, _i64, _i64, _p, _p, _f, _p, _p, _p, _p, _p, _p,
                                           _sz, _p]),
     "bt_repack_plan_bytes": (_sz, [_i32]),
@@ -43,6 +45,11 @@ SIGNATURES = {
     "bt_matmul_plan_build": (C.c_int, [_p, _i32, _p, _sz, _p, _sz]),
     "bt_ternary_matmul_grouped": (C.c_int, [_p, _p, _p]),
 }
+
+
+class BtEpilogue(C.Structure):
+    _fields_ = [("bias", _p), ("layer_scale", _p), ("residual", _p), ("relu", _i32),
+                ("reserved", _i32)]
 
 
 class BtRepackDesc(C.Structure):

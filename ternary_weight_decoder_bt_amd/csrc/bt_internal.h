@@ -37,6 +37,16 @@ constexpr int kGemvBatch = BT_GEMV_BATCH;
 constexpr int kGemvLdsBytes = 40960;
 constexpr int kGemvGroupedTilesPerWave = BT_GEMV_TILES_PER_WAVE;
 
+// Epilogue on the fp32 output (all optional): bias add, ReLU, per-output
+// layer scale, residual add, in that order.
+struct EpiArgs {
+    const float* bias;      // [N] or null
+    const float* gamma;     // [N] or null
+    const float* res;       // M x N or null (may be the output buffer itself)
+    int32_t relu;
+    int32_t pad_;
+};
+
 // One GEMV problem as the kernel sees it. The single-matrix call passes it by
 // value; a grouped plan stores an array of them in device memory.
 struct GemvDesc {
@@ -61,6 +71,7 @@ struct GemvDesc {
     int64_t groups;         // workgroups per chunk = ceil(tiles / (4 * tiles_per_wave))
     int64_t block_begin;    // first workgroup of this problem in a grouped launch
     int64_t blocks;         // workgroups of this problem = groups * chunks
+    EpiArgs epi;            // zero: no epilogue
 };
 
 struct QuantDesc {

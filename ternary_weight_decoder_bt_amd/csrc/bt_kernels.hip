@@ -107,6 +107,39 @@ __device__ __forceinline__ void lds_st(void* p, T v) {
     *(BT_LDS T*)p = v;
 }
 
+// ---------------------------------------------------------------- epilogue
+//
+// The fused epilogues of the technical report's section 2.4.1 on the fp32
+// output y = fl32(fl32(acc) * fl32(d * s_w)): bias add, ReLU (a non-positive
+// value becomes +0), layer scale, residual add; each one fp32 operation.
+
+using bt::EpiArgs;
+
+__host__ __device__ __forceinline__ bool epi_any(const EpiArgs& e) {
+    return e.bias || e.gamma || e.res || e.relu;
+}
+
+// bias, ReLU and layer scale on one value of output column n
+__device__ __forceinline__ float epi_col(const EpiArgs& e, float y, int64_t n) {
+    if (e.bias) y = y + e.bias[n];
+    if (e.relu) y = y > 0.0f ? y : 0.0f;
+    if (e.gamma) y = e.gamma[n] * y;
+    return y;
+}
+
+// the same on four consecutive columns n .. n+3 (n % 4 == 0, 16-byte loads)
+__device__ __forceinline__ v4f epi_col4(const EpiArgs& e, v4f y, int64_t n) {
+    if (e.bias) y = y + gld<v4f>(e.bias + n);
+    if (e.relu) {
+        y.x = y.x > 0.0f ? y.x : 0.0f;
+        y.y = y.y > 0.0f ? y.y : 0.0f;
+        y.z = y.z > 0.0f ? y.z : 0.0f;
+        y.w = y.w > 0.0f ? y.w : 0.0f;
+    }
+    if (e.gamma) y = gld<v4f>(e.gamma + n) * y;
+    return y;
+}
+
 // ------------------------------------------------------------------ repack
 
 // One wave per 1 KB output block (16-row tile t, 256-wide step S); lane l
@@ -667,8 +700,11 @@ __device__ __forceinline__ void gemv_finish(const GemvDesc& d, int64_t tile, v4i
                 const float dm = sh.d[mm];
                 const int32_t acc = c[i] - qsum;
                 const float rs = dm * d.w_scale;
-                gst<float>(d.y + int64_t(mm) * d.N + n, float(acc) * rs);
-                if (d.acc) gst<int32_t>(d.acc + int64_t(mm) * d.N + n, acc);
+                const int64_t o = int64_t(mm) * d.N + n;
+                float v = epi_col(d.epi, float(acc) * rs, n);
+                if (d.epi.res) v = d.epi.res[o] + v;
+                gst<float>(d.y + o, v);
+                if (d.acc) gst<int32_t>(d.acc + o, acc);
             }
         }
     }
@@ -949,6 +985,7 @@ struct GemmArgs {
     float w_scale;
     int32_t M, N, K, tiles, steps;   // steps: 256-wide stages (Kp / 256)
     int32_t m_tiles, n_tiles, per_xcd;
+    EpiArgs epi;
 };
 
 constexpr int kXcds = 8;
@@ -974,19 +1011,53 @@ __device__ __forceinline__ void wait_vmcnt() {
 // through the wave's own 4 KB of LDS (16-byte slots XOR-swizzled by row, so
 // both the writes and the reads are conflict-free) and is stored row-wise:
 // 16 lanes write 256 contiguous bytes of one row, whole cache lines.
+// A wave's bias and layer-scale values for its 64 columns nb.. in the MFMA
+// layout (columns nb + 16t + 4(l/16) .. +3), loaded once per tile.
+struct EpiCols {
+    v4f bias[4];
+    v4f gamma[4];
+};
+
+__device__ __forceinline__ EpiCols epi_cols_load(const EpiArgs& e, int64_t nb, int lane) {
+    EpiCols c;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+        const int64_t n = nb + 16 * t + 4 * (lane >> 4);
+        c.bias[t] = e.bias ? gld<v4f>(e.bias + n) : v4f{0.0f, 0.0f, 0.0f, 0.0f};
+        c.gamma[t] = e.gamma ? gld<v4f>(e.gamma + n) : v4f{1.0f, 1.0f, 1.0f, 1.0f};
+    }
+    return c;
+}
+
+// The epilogue's column steps run in the MFMA layout, its residual add in the
+// row layout (16-byte residual loads of whole rows).
 __device__ __forceinline__ void gemm_store_block_rows(const v4f (&v)[4], float* ep, float* y,
                                                       int64_t ldy, int64_t mb, int64_t nb,
-                                                      int lane) {
+                                                      int lane, const EpiArgs& e,
+                                                      const EpiCols& ec) {
     const int rl = lane & 15;
     const int cq = lane >> 4;
 #pragma unroll
-    for (int t = 0; t < 4; ++t) lds_st<v4f>(ep + rl * 64 + (((4 * t + cq) ^ rl) * 4), v[t]);
+    for (int t = 0; t < 4; ++t) {
+        v4f vt = v[t];
+        if (e.bias) vt = vt + ec.bias[t];
+        if (e.relu) {
+            vt.x = vt.x > 0.0f ? vt.x : 0.0f;
+            vt.y = vt.y > 0.0f ? vt.y : 0.0f;
+            vt.z = vt.z > 0.0f ? vt.z : 0.0f;
+            vt.w = vt.w > 0.0f ? vt.w : 0.0f;
+        }
+        if (e.gamma) vt = ec.gamma[t] * vt;
+        lds_st<v4f>(ep + rl * 64 + (((4 * t + cq) ^ rl) * 4), vt);
+    }
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
         const int r = 4 * j + cq;
         const int c = lane & 15;
-        const v4f row = lds_ld<v4f>(ep + r * 64 + ((c ^ r) * 4));
-        __builtin_nontemporal_store(row, (BT_GLOBAL v4f*)(y + (mb + r) * ldy + nb + 4 * c));
+        v4f row = lds_ld<v4f>(ep + r * 64 + ((c ^ r) * 4));
+        const int64_t o = (mb + r) * ldy + nb + 4 * c;
+        if (e.res) row = gld<v4f>(e.res + o) + row;
+        __builtin_nontemporal_store(row, (BT_GLOBAL v4f*)(y + o));
     }
 }
 
@@ -1171,6 +1242,7 @@ void gemm_kernel(GemmArgs g) {
     const bool full = m0 + BM <= g.M && n0 + BN <= g.N && (g.N & 3) == 0;
     if (kRowStores && full && !g.acc) {
         float* ep = Ep + wave * (16 * 64);
+        const EpiCols ec = epi_cols_load(g.epi, n0 + wn * WW, lane);
 #pragma unroll
         for (int i = 0; i < TA; ++i) {
             const int64_t mb = m0 + wm * WA + 16 * i;
@@ -1182,7 +1254,7 @@ void gemm_kernel(GemmArgs g) {
                 const v4i a = acc[i][t] - qs;
                 v[t] = v4f{float(a.x) * rs, float(a.y) * rs, float(a.z) * rs, float(a.w) * rs};
             }
-            gemm_store_block_rows(v, ep, g.y, g.N, mb, n0 + wn * WW, lane);
+            gemm_store_block_rows(v, ep, g.y, g.N, mb, n0 + wn * WW, lane, g.epi, ec);
         }
         return;
     }
@@ -1198,15 +1270,19 @@ void gemm_kernel(GemmArgs g) {
         for (int t = 0; t < TW; ++t) {
             const int n = nq + 16 * t;
             const v4i a = acc[i][t] - qs;
-            const v4f yv = {float(a.x) * rs, float(a.y) * rs, float(a.z) * rs, float(a.w) * rs};
+            v4f yv = {float(a.x) * rs, float(a.y) * rs, float(a.z) * rs, float(a.w) * rs};
             if (full) {
+                yv = epi_col4(g.epi, yv, n);
+                if (g.epi.res) yv = gld<v4f>(g.epi.res + mm * g.N + n) + yv;
                 __builtin_nontemporal_store(yv, (BT_GLOBAL v4f*)(yrow + n));
                 if (arow) __builtin_nontemporal_store(a, (BT_GLOBAL v4i*)(arow + n));
             } else {
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     if (n + r < g.N) {
-                        gst<float>(yrow + n + r, yv[r]);
+                        float v = epi_col(g.epi, yv[r], n + r);
+                        if (g.epi.res) v = g.epi.res[mm * g.N + n + r] + v;
+                        gst<float>(yrow + n + r, v);
                         if (arow) gst<int32_t>(arow + n + r, a[r]);
                     }
                 }
@@ -1215,7 +1291,9 @@ void gemm_kernel(GemmArgs g) {
     }
 }
 
-// Persistent prefill GEMM. A workgroup of NW waves side by side along N
+// Persistent prefill GEMM (without the fused epilogue: a call that asks for
+// one runs gemm_kernel, which has the registers for it). A workgroup of NW
+// waves side by side along N
 // owns a WA x (WW*NW) output tile at a time and walks a run of tiles: the
 // tiles of one XCD's contiguous band, taken round-robin by that XCD's
 // workgroups (consecutive tiles share token rows, which stay in the XCD's
@@ -1409,7 +1487,7 @@ void gemm_persistent_kernel(GemmArgs g) {
                     v[t] = v4f{float(a.x) * r, float(a.y) * r, float(a.z) * r, float(a.w) * r};
                 }
                 gemm_store_block_rows(v, Ep + wave * (16 * 64), g.y, g.N, m0 + 16 * i,
-                                      n0 + wave * WW, lane);
+                                      n0 + wave * WW, lane, EpiArgs{}, EpiCols{});
             } else if (full || mm < g.M) {
                 float* yrow = g.y + mm * g.N;
                 int32_t* arow = g.acc ? g.acc + mm * g.N : nullptr;
@@ -1539,7 +1617,7 @@ bt_status dispatch_gemm(const GemmArgs& g, hipStream_t stream) {
         constexpr int BM = BT_GEMM_P_WA;
         constexpr int BN = 64 * BT_GEMM_P_NW;
         const int64_t tiles = bt::ceil_div(g.M, BM) * bt::ceil_div(g.N, BN);
-        if (tiles >= 2 * int64_t(device_cus()))
+        if (tiles >= 2 * int64_t(device_cus()) && !epi_any(g.epi))
             return launch_gemm_persistent<BT_GEMM_P_WA, 64, BT_GEMM_P_NW, 128, BT_GEMM_P_NS>(g,
                                                                                         stream);
     }
@@ -1678,16 +1756,41 @@ extern "C" bt_status bt_ternary_matmul_fused(int64_t M, int64_t N, int64_t K, co
     return launched();
 }
 
-extern "C" bt_status bt_ternary_matmul(int64_t M, int64_t N, int64_t K, const int8_t* xq,
-                                       const float* xscale, const int32_t* xsum, const void* wdev,
-                                       float w_scale, float* y, int32_t* acc, void* workspace,
-                                       size_t workspace_bytes, hipStream_t stream) {
+// Checks an epilogue against the output it is applied to and converts it.
+static bt_status epilogue_args(const bt_epilogue* epi, int64_t M, int64_t N, const float* y,
+                               EpiArgs* out) {
+    memset(out, 0, sizeof(*out));
+    if (!epi) return BT_OK;
+    if (!bt::aligned16(epi->bias) || !bt::aligned16(epi->layer_scale) ||
+        !bt::aligned16(epi->residual))
+        return BT_ERR_ALIGN;
+    if (epi->residual && epi->residual != y) {
+        // the residual is the output itself, or disjoint from it
+        const uintptr_t r0 = reinterpret_cast<uintptr_t>(epi->residual);
+        const uintptr_t y0 = reinterpret_cast<uintptr_t>(y);
+        const uintptr_t bytes = uintptr_t(M) * uintptr_t(N) * sizeof(float);
+        if (r0 < y0 + bytes && y0 < r0 + bytes) return BT_ERR_VALUE;
+    }
+    out->bias = epi->bias;
+    out->gamma = epi->layer_scale;
+    out->res = epi->residual;
+    out->relu = epi->relu ? 1 : 0;
+    return BT_OK;
+}
+
+static bt_status matmul_impl(int64_t M, int64_t N, int64_t K, const int8_t* xq,
+                             const float* xscale, const int32_t* xsum, const void* wdev,
+                             float w_scale, const bt_epilogue* epi, float* y, int32_t* acc,
+                             void* workspace, size_t workspace_bytes, hipStream_t stream) {
     if (!xq || !xscale || !xsum || !wdev || !y) return BT_ERR_NULL;
     if (M < 1 || M > (int64_t(1) << 31) - 1 || !nk_ok(N, K)) return BT_ERR_SHAPE;
     if (!bt::aligned16(xq) || !bt::aligned16(xscale) || !bt::aligned16(xsum) ||
         !bt::aligned16(wdev) || !bt::aligned16(y) || (acc && !bt::aligned16(acc)))
         return BT_ERR_ALIGN;
     if (!isfinite(w_scale)) return BT_ERR_VALUE;
+    EpiArgs e;
+    const bt_status est = epilogue_args(epi, M, N, y, &e);
+    if (est != BT_OK) return est;
     if (M <= BT_GEMV_MAX_M) {
         GemvDesc d;
         bt::gemv_shape(M, N, K, false, &d);
@@ -1700,6 +1803,7 @@ extern "C" bt_status bt_ternary_matmul(int64_t M, int64_t N, int64_t K, const in
         d.y = y;
         d.acc = acc;
         d.w_scale = w_scale;
+        d.epi = e;
         (void)hipGetLastError();
         hipLaunchKernelGGL(gemv_kernel<false>, dim3(unsigned(d.blocks)), dim3(64 * bt::kGemvWaves),
                            gemv_lds_bytes(d), stream, d);
@@ -1707,6 +1811,7 @@ extern "C" bt_status bt_ternary_matmul(int64_t M, int64_t N, int64_t K, const in
     }
     GemmArgs g;
     memset(&g, 0, sizeof(g));
+    g.epi = e;
     g.xq = xq;
     g.xscale = xscale;
     g.xsum = xsum;
@@ -1720,6 +1825,24 @@ extern "C" bt_status bt_ternary_matmul(int64_t M, int64_t N, int64_t K, const in
     g.tiles = int32_t(bt::ceil_div(N, bt::kTileN));
     g.steps = int32_t(bt::ceil_div(K, bt::kSuperK));
     return dispatch_gemm(g, stream);
+}
+
+extern "C" bt_status bt_ternary_matmul(int64_t M, int64_t N, int64_t K, const int8_t* xq,
+                                       const float* xscale, const int32_t* xsum, const void* wdev,
+                                       float w_scale, float* y, int32_t* acc, void* workspace,
+                                       size_t workspace_bytes, hipStream_t stream) {
+    return matmul_impl(M, N, K, xq, xscale, xsum, wdev, w_scale, nullptr, y, acc, workspace,
+                       workspace_bytes, stream);
+}
+
+extern "C" bt_status bt_ternary_matmul_epilogue(int64_t M, int64_t N, int64_t K, const int8_t* xq,
+                                                const float* xscale, const int32_t* xsum,
+                                                const void* wdev, float w_scale,
+                                                const bt_epilogue* epi, float* y, int32_t* acc,
+                                                void* workspace, size_t workspace_bytes,
+                                                hipStream_t stream) {
+    return matmul_impl(M, N, K, xq, xscale, xsum, wdev, w_scale, epi, y, acc, workspace,
+                       workspace_bytes, stream);
 }
 
 extern "C" bt_status bt_quantize_act_grouped(const void* plan_host, const void* plan_dev,

@@ -11,7 +11,7 @@ import ctypes as C
 
 import numpy as np
 
-from ._lib import BtMatmulDesc, BtQuantDesc, BtRepackDesc, BtError, check, lib
+from ._lib import BtEpilogue, BtMatmulDesc, BtQuantDesc, BtRepackDesc, BtError, check, lib
 
 GROUP_K = 128
 GEMV_MAX_M = 16
@@ -156,8 +156,13 @@ def new_workspace(m: int, n: int, k: int, device="cuda"):
 
 
 def ternary_matmul(xq, xscale, xsum, wdev, n: int, w_scale: float, y=None, acc=None,
-                   workspace=None, want_acc=False, stream=None):
-    """y = (xq @ W^T) * xscale * w_scale via bt_ternary_matmul; returns y (and acc)."""
+                   workspace=None, want_acc=False, stream=None, bias=None, relu=False,
+                   layer_scale=None, residual=None):
+    """y = (xq @ W^T) * xscale * w_scale via bt_ternary_matmul; returns y (and acc).
+
+    bias, relu, layer_scale, residual: the fused epilogue (bt_ternary_matmul_epilogue),
+    y = residual + layer_scale * relu(y + bias); residual may be y itself.
+    """
     torch = _torch()
     _dev(xq, torch.int8, None, "xq")
     m, k = xq.shape
@@ -175,9 +180,20 @@ def ternary_matmul(xq, xscale, xsum, wdev, n: int, w_scale: float, y=None, acc=N
     if need and workspace is None:
         workspace = new_workspace(m, n, k, xq.device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    check(lib().bt_ternary_matmul(m, n, k, _ptr(xq), _ptr(xscale), _ptr(xsum), _ptr(wdev),
-                                  float(w_scale), _ptr(y), _ptr(acc), _ptr(workspace), ws_bytes,
-                                  _stream(stream)), "bt_ternary_matmul")
+    if bias is None and not relu and layer_scale is None and residual is None:
+        check(lib().bt_ternary_matmul(m, n, k, _ptr(xq), _ptr(xscale), _ptr(xsum), _ptr(wdev),
+                                      float(w_scale), _ptr(y), _ptr(acc), _ptr(workspace),
+                                      ws_bytes, _stream(stream)), "bt_ternary_matmul")
+    else:
+        for t, shp, name in ((bias, (n,), "bias"), (layer_scale, (n,), "layer_scale"),
+                             (residual, (m, n), "residual")):
+            if t is not None:
+                _dev(t, torch.float32, shp, name)
+        epi = BtEpilogue(_ptr(bias), _ptr(layer_scale), _ptr(residual), 1 if relu else 0, 0)
+        check(lib().bt_ternary_matmul_epilogue(m, n, k, _ptr(xq), _ptr(xscale), _ptr(xsum),
+                                               _ptr(wdev), float(w_scale), C.byref(epi), _ptr(y),
+                                               _ptr(acc), _ptr(workspace), ws_bytes,
+                                               _stream(stream)), "bt_ternary_matmul_epilogue")
     return (y, acc) if (want_acc or acc is not None) else y
 
 

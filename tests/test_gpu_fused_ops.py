@@ -119,3 +119,69 @@ def test_rmsnorm_quantize_feeds_the_matmul(dev):
     torch.cuda.synchronize()
     assert np.array_equal(acc.cpu().numpy(), ref["acc"])
     assert np.array_equal(y.cpu().numpy(), ref["y"])
+
+
+# ------------------------------------------------------------- epilogues
+
+def load_weights(w, dev):
+    n, k = w.shape
+    return bt.repack_ternary(to_dev(bt.pack_ternary(w).reshape(-1), dev), n, k)
+
+
+EPILOGUES = {
+    "bias_relu": dict(bias=True, relu=True),
+    "scale_residual": dict(layer_scale=True, residual=True),
+    "all": dict(bias=True, relu=True, layer_scale=True, residual=True),
+    "relu_only": dict(relu=True),
+}
+
+
+@pytest.mark.parametrize("m,n,k", [(1, 200, 384), (5, 1536, 1536), (16, 130, 8960),
+                                   (40, 200, 384), (300, 1536, 1536), (4133, 4100, 384),
+                                   (4096, 1540, 256)])
+@pytest.mark.parametrize("kind", list(EPILOGUES))
+def test_matmul_epilogues(dev, m, n, k, kind):
+    """GEMV (M <= 16), GEMM full and ragged tiles, with each epilogue; y against
+    the oracle bit for bit, acc still the plain sum."""
+    spec = EPILOGUES[kind]
+    c = synth.small_problem(30, m, n, k, "t3", (0.3, 0.4, 0.3))
+    rng = np.random.default_rng(m + n + k)
+    bias = rng.standard_normal(n).astype(np.float32) if spec.get("bias") else None
+    gamma = rng.uniform(-2, 2, n).astype(np.float32) if spec.get("layer_scale") else None
+    res = rng.standard_normal((m, n)).astype(np.float32) if spec.get("residual") else None
+    ref = oracle.forward_ref(c["x"], c["w"], c["w_scale"], "f64")
+    want = oracle.epilogue_ref(ref["y"], bias, spec.get("relu", False), gamma, res)
+    xq, xs, xsum = (to_dev(ref[k_], dev) for k_ in ("q", "d", "qsum"))
+    y = torch.full((m, n), float("nan"), dtype=torch.float32, device=dev)
+    acc = torch.full((m, n), POISON_I32, dtype=torch.int32, device=dev)
+    bt.ternary_matmul(xq, xs, xsum, load_weights(c["w"], dev), n, c["w_scale"], y=y, acc=acc,
+                      bias=None if bias is None else to_dev(bias, dev),
+                      relu=spec.get("relu", False),
+                      layer_scale=None if gamma is None else to_dev(gamma, dev),
+                      residual=None if res is None else to_dev(res, dev))
+    torch.cuda.synchronize()
+    got = y.cpu().numpy()
+    assert np.array_equal(acc.cpu().numpy(), ref["acc"])
+    bad = ~((got == want) | (np.isnan(got) & np.isnan(want)))
+    assert not bad.any(), (np.argwhere(bad)[:3], got[bad][:3], want[bad][:3])
+    if spec.get("relu") and not spec.get("layer_scale"):
+        assert not np.signbit(got).any()          # ReLU gives +0, never -0
+
+
+@pytest.mark.parametrize("m,n,k", [(3, 200, 384), (4096, 2048, 256)])
+def test_matmul_residual_in_place(dev, m, n, k):
+    """residual = y: out = y_old + layer_scale * relu(y + bias), written over y_old."""
+    c = synth.small_problem(31, m, n, k, "normal")
+    rng = np.random.default_rng(31)
+    old = rng.standard_normal((m, n)).astype(np.float32)
+    bias = rng.standard_normal(n).astype(np.float32)
+    gamma = rng.uniform(-2, 2, n).astype(np.float32)
+    ref = oracle.forward_ref(c["x"], c["w"], c["w_scale"], "f64")
+    want = oracle.epilogue_ref(ref["y"], bias, True, gamma, old)
+    xq, xs, xsum = (to_dev(ref[k_], dev) for k_ in ("q", "d", "qsum"))
+    y = to_dev(old, dev)
+    bt.ternary_matmul(xq, xs, xsum, load_weights(c["w"], dev), n, c["w_scale"], y=y,
+                      bias=to_dev(bias, dev), relu=True, layer_scale=to_dev(gamma, dev),
+                      residual=y)
+    torch.cuda.synchronize()
+    assert np.array_equal(y.cpu().numpy(), want)
