@@ -28,3 +28,4 @@ from .fused_ref import (  # noqa: F401
     rmsnorm_quantize_ref,
     epilogue_ref,
 )
+from .i8s_ref import I8_KMAX, i8s_matmul_ref, i8s_forward_ref  # noqa: F401,E402
