@@ -360,6 +360,59 @@ class LongPrefill:
 
 # ------------------------------------------------------------ CPU baseline
 
+# The tokenizer's ConvNeXt stages ("VibeVoice-ASR-BitNet Technical Report",
+# section 2.2.1, Table 1: channels D and sequence length L for 20 s of audio);
+# each block's FFN is D -> 4D -> D, run here as two I8_S GEMMs with M = L.
+VAE_STAGES = ((32, 480000), (64, 240000), (128, 120000), (256, 30000), (512, 6000),
+              (1024, 1200), (2048, 150))
+
+
+def run_i8s_tokenizer_ffn(torch, bt, dev, reps: int = 10):
+    """Time the I8_S GEMMs of the tokenizer's FFN layers (synthetic int8 codes and
+    weights). Returns {stage: {...}} and the aggregate."""
+    out = {}
+    tot_ops, tot_ms, tot_bytes = 0, 0.0, 0
+    gen = torch.Generator(device=dev).manual_seed(7)
+    for st, (d, L) in enumerate(VAE_STAGES):
+        row = {}
+        for name, (n, k) in (("up", (4 * d, d)), ("down", (d, 4 * d))):
+            xq = torch.randint(-127, 128, (L, k), dtype=torch.int8, device=dev, generator=gen)
+            xs = torch.rand(L, device=dev, generator=gen) * 0.01 + 0.001
+            w8 = torch.randint(-128, 128, (n, k), dtype=torch.int8, device=dev, generator=gen)
+            wdev = bt.repack_int8(w8)
+            y = torch.empty((L, n), dtype=torch.float32, device=dev)
+            bt.int8_matmul(xq, xs, wdev, n, 0.01, y=y)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(reps):
+                bt.int8_matmul(xq, xs, wdev, n, 0.01, y=y)
+            e1.record()
+            torch.cuda.synchronize()
+            ms = e0.elapsed_time(e1) / reps
+            ops = 2 * L * n * k
+            nbytes = L * k + n * k + 4 * L * n + 4 * L
+            row[name] = {"M": L, "N": n, "K": k, "us": round(ms * 1e3, 2),
+                         "tops": round(ops / (ms * 1e-3) / 1e12, 1),
+                         "gb_per_s": round(nbytes / (ms * 1e-3) / 1e9, 1),
+                         "bound": "hbm" if ops / nbytes < I8_PEAK_TOPS / HBM_PEAK_GBS * 1e3
+                                  else "mfma"}
+            tot_ops += ops
+            tot_ms += ms
+            tot_bytes += nbytes
+            del xq, xs, w8, wdev, y
+        out[f"stage{st}_D{d}_L{L}"] = row
+        log(f"i8s stage {st} (D={d}, L={L}): up {row['up']['tops']} TOPS / "
+            f"{row['up']['gb_per_s']} GB/s, down {row['down']['tops']} TOPS / "
+            f"{row['down']['gb_per_s']} GB/s")
+    torch.cuda.empty_cache()
+    return {"workload": "I8_S GEMMs of the tokenizer's FFN layers (D -> 4D -> D, M = L) for "
+                        "the 7 stages of a 20 s input, synthetic int8 codes and weights, "
+                        "fp32 output",
+            "stages": out, "total_us": round(tot_ms * 1e3, 1),
+            "tops": round(tot_ops / (tot_ms * 1e-3) / 1e12, 1),
+            "gb_per_s": round(tot_bytes / (tot_ms * 1e-3) / 1e9, 1)}
+
+
 def cpu_baseline(seconds: float):
     """The oracle as it stands (quantize, exact fp64-BLAS integer matmul,
     rescale) over the whole decode step, repeated until `seconds` (at least
@@ -642,6 +695,10 @@ def main():
         }
         del lp
         torch.cuda.empty_cache()
+
+    # ---- I8_S (the tokenizer's INT8 GEMMs), secondary
+    if not args.no_prefill:
+        out["i8s"] = run_i8s_tokenizer_ffn(torch, bt, dev)
 
     if not args.no_cpu_baseline:
         log("timing the CPU oracle")

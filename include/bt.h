@@ -206,6 +206,31 @@ bt_status bt_ternary_matmul_epilogue(int64_t M, int64_t N, int64_t K, const int8
                                      hipStream_t stream);
 
 /* ---------------------------------------------------------------------------
+ * I8_S: int8 weights x int8 activations ("VibeVoice-ASR-BitNet Technical
+ * Report" section 2.2.1: the tokenizer's INT8 datapath; section 2.4.2 and
+ * Figure 4: one integer multiply-add pipeline shared with I2_S, which only
+ * adds the 2-bit unpack). acc[m,n] = sum_k xq[m,k] * w[n,k] exactly in int32,
+ * y = fl32(fl32(acc) * fl32(xscale[m] * w_scale)), then the optional epilogue.
+ * Weights are int8 over [-128, 127] with one fp32 scale per tensor;
+ * activations come from bt_quantize_act (or bt_rmsnorm_quantize).
+ * K % 32 == 0 and K <= 131072 (so that |acc| <= 127*128*K < 2^31).
+ * ------------------------------------------------------------------------- */
+
+/* ceil(N/16)*16 * ceil(K/256)*256, or 0 for invalid N, K. */
+size_t bt_int8_repacked_bytes(int64_t N, int64_t K);
+
+/* w_dev: device int8 N x K row-major. wdev: device, bt_int8_repacked_bytes
+ * bytes, written (the kernels' tile order; padding holds zeros). */
+bt_status bt_repack_int8(const int8_t* w_dev, int64_t N, int64_t K, void* wdev,
+                         hipStream_t stream);
+
+/* xq: device int8 M x K; xscale: device fp32 [M]; w8dev from bt_repack_int8;
+ * epi: host, NULL for none (as bt_ternary_matmul_epilogue); acc may be NULL. */
+bt_status bt_int8_matmul(int64_t M, int64_t N, int64_t K, const int8_t* xq, const float* xscale,
+                         const void* w8dev, float w_scale, const bt_epilogue* epi, float* y,
+                         int32_t* acc, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
  * Grouped launches: many independent projections in one kernel launch.
  *
  * The technical report's kernels have "batch" tiling variants chosen by shape

@@ -16,11 +16,14 @@ from .ops import (  # noqa: F401
     MatmulPlan,
     QuantPlan,
     RepackPlan,
+    int8_matmul,
+    int8_repacked_bytes,
     matmul_workspace_bytes,
     new_workspace,
     pack_ternary,
     packed_bytes,
     quantize_act,
+    repack_int8,
     repack_ternary,
     repacked_bytes,
     rmsnorm_quantize,

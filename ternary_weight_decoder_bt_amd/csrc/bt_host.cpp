@@ -149,6 +149,14 @@ extern "C" size_t bt_matmul_workspace_bytes(int64_t M, int64_t N, int64_t K) {
 
 // ------------------------------------------------------------------ plans
 
+extern "C" size_t bt_int8_repacked_bytes(int64_t N, int64_t K) {
+    // K % 32 == 0 (whole 16-byte fragments, the report's 32-element I8_S
+    // blocks) and 127 * 128 * K < 2^31
+    if (N < 1 || K < 32 || K % 32 != 0 || K > 131072 || N > (int64_t(1) << 31) - 16)
+        return 0;
+    return size_t(bt::ceil_div(N, bt::kTileN) * bt::kTileN) * size_t(bt::ceil_div(K, bt::kSuperK) * bt::kSuperK);
+}
+
 extern "C" size_t bt_repack_plan_bytes(int32_t count) {
     if (count < 1) return 0;
     return sizeof(bt::PlanHeader) + size_t(count) * sizeof(bt::RepackDesc);

@@ -253,6 +253,27 @@ __global__ __launch_bounds__(256) void repack_grouped_kernel(
     }
 }
 
+// Int8 weights (the I8_S product) in the same tile order: 16-row tiles, K
+// padded to Kp = ceil(K/256)*256, each 64-wide step one 1 KB block in which
+// lane l holds the 16 bytes of row l%16 at K = 64S + 16(l/16) .. +15, the
+// fragment one matrix-core step reads. One wave per 1 KB block; padding is 0.
+__global__ __launch_bounds__(256) void repack_int8_kernel(const int8_t* __restrict__ w, int32_t N,
+                                                          int32_t K, int32_t steps64,
+                                                          int64_t blocks,
+                                                          int8_t* __restrict__ out) {
+    const int lane = threadIdx.x & 63;
+    for (int64_t blk = (int64_t(blockIdx.x) * blockDim.x + threadIdx.x) >> 6; blk < blocks;
+         blk += (int64_t(gridDim.x) * blockDim.x) >> 6) {
+        const int64_t t = blk / steps64;
+        const int32_t S = int32_t(blk - t * steps64);
+        const int64_t n = t * bt::kTileN + (lane & 15);
+        const int64_t k = int64_t(64) * S + 16 * (lane >> 4);
+        v4u v = {0u, 0u, 0u, 0u};
+        if (n < N && k < K) v = gld<v4u>(w + n * K + k);   // K % 16 == 0: whole 16 bytes
+        gst<v4u>(out + blk * 1024 + lane * 16, v);
+    }
+}
+
 // ---------------------------------------------------------------- quantize
 
 __device__ __forceinline__ float wave_max(float v) {
@@ -1061,7 +1082,16 @@ __device__ __forceinline__ void gemm_store_block_rows(const v4f (&v)[4], float* 
     }
 }
 
-template <int WA, int WW, int WGM, int WGN, int KS, int NS>
+// Weight registers of one tile and stage for int8 weights: one 16-byte
+// fragment per 64-wide step.
+template <int NK>
+struct W8Frag {
+    v4u k[NK];
+};
+
+// kW8: the I8_S product (int8 weights, repacked by bt_repack_int8): the
+// fragments go to the matrix cores as loaded and no row-sum correction applies.
+template <int WA, int WW, int WGM, int WGN, int KS, int NS, bool kW8 = false>
 __global__ __launch_bounds__(64 * WGM * WGN) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void gemm_kernel(GemmArgs g) {
     constexpr int BM = WA * WGM;
@@ -1102,7 +1132,8 @@ void gemm_kernel(GemmArgs g) {
     const int64_t m0 = int64_t(mt) * BM;
     const int n0 = nt * BN;
     const int t0 = min(n0 / bt::kTileN + wn * (WW / bt::kTileN), g.tiles - 1);
-    const uint32_t tile_bytes = uint32_t(g.steps) * 1024u;
+    // a tile's 256-wide step is 1 KB of 2-bit codes, or 4 KB of int8 weights
+    const uint32_t tile_bytes = uint32_t(g.steps) * (kW8 ? 4096u : 1024u);
     const int nst = (g.K + KS - 1) / KS;
 
     // This wave's weight tiles as one buffer. The tile is part of the
@@ -1113,7 +1144,8 @@ void gemm_kernel(GemmArgs g) {
     const __amdgpu_buffer_rsrc_t wrsrc = make_rsrc(
         g.w + int64_t(t0) * tile_bytes,
         uint32_t(min(WW / bt::kTileN, g.tiles - t0)) * tile_bytes);
-    using BVec = typename std::conditional<KS == 256, v4u, v2u>::type;
+    using BVec = typename std::conditional<
+        kW8, W8Frag<NK>, typename std::conditional<KS == 256, v4u, v2u>::type>::type;
     // A stage past K (padding of the pipeline) reads zeros: bit 31 set in
     // its per-lane offsets puts them out of range (buffers here stay below
     // 2^31 bytes and the scalar offset below 2^30, so the sum cannot wrap),
@@ -1122,16 +1154,21 @@ void gemm_kernel(GemmArgs g) {
     // conservative.
     constexpr uint32_t kNowhere = 0x80000000u;
     auto load_b = [&](BVec (&b)[TW], int s, uint32_t pad) {
-        const uint32_t koff = KS == 256 ? uint32_t(s) * 1024u
-                                        : uint32_t(s >> 1) * 1024u + uint32_t(s & 1) * 8u;
 #pragma unroll
         for (int t = 0; t < TW; ++t) {
             const uint32_t voff = (uint32_t(lane) * 16u + uint32_t(t) * tile_bytes) | pad;
-            if constexpr (KS == 256)
-                b[t] = buf_ld16u(wrsrc, voff, koff);
-            else
+            if constexpr (kW8) {
+                // int8: 64-wide steps of 1 KB, NK of them per stage
+#pragma unroll
+                for (int kk = 0; kk < NK; ++kk)
+                    b[t].k[kk] = buf_ld16u(wrsrc, voff, uint32_t(s * NK + kk) * 1024u);
+            } else if constexpr (KS == 256) {
+                b[t] = buf_ld16u(wrsrc, voff, uint32_t(s) * 1024u);
+            } else {
+                const uint32_t koff = uint32_t(s >> 1) * 1024u + uint32_t(s & 1) * 8u;
                 b[t] = __builtin_bit_cast(
                     v2u, __builtin_amdgcn_raw_buffer_load_b64(wrsrc, int(voff), int(koff), 0));
+            }
         }
     };
 
@@ -1146,24 +1183,23 @@ void gemm_kernel(GemmArgs g) {
     constexpr int RPC = 64 / CPR;   // rows per copy
     const int r0 = wave * kDmaPerWave * RPC + lane / CPR;
     uint32_t avoff[4];
-    uint32_t ahigh[4];   // kNowhere for a chunk in the upper 128 bytes of a 256-wide stage
+    uint32_t ccol[4];    // byte offset of this lane's chunk inside a stage
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
         const int r = r0 + RPC * q;
         const int c = slot_of(r, lane % CPR);
         avoff[q] = uint32_t(r0) * uint32_t(g.K) + uint32_t(c) * 16u;
-        ahigh[q] = c >= 8 ? kNowhere : 0u;
+        ccol[q] = uint32_t(c) * 16u;
     }
-    const bool tail128 = KS == 256 && (g.K & 255) != 0;
     auto load_a = [&](int buf, int s, uint32_t pad) {
         const uint32_t kcol = uint32_t(s) * KS;
-        // in the last stage of a K that ends half way through it, a chunk
-        // past K must read zero, not the next row: push it out of range too
-        const uint32_t tail = (tail128 && s == nst - 1) ? 0xffffffffu : 0u;
+        // bytes of K left in this stage: a chunk past K (K % 16 == 0, so a
+        // chunk is wholly in or out) must read zero, not the next row
+        const uint32_t left = uint32_t(g.K) > kcol ? uint32_t(g.K) - kcol : 0u;
 #pragma unroll
         for (int j = 0; j < kDmaPerWave; ++j) {
             const uint32_t voff = (avoff[j & 3] + uint32_t(RPC * j) * uint32_t(g.K)) | pad |
-                                  (ahigh[j & 3] & tail);
+                                  (ccol[j & 3] >= left ? kNowhere : 0u);
             lds_dma16(arsrc, As + buf * kStage + (wave * kDmaPerWave + j) * 1024, voff, kcol);
         }
     };
@@ -1206,7 +1242,11 @@ void gemm_kernel(GemmArgs g) {
             for (int i = 0; i < TA; ++i) af[i] = lds_ld<v4i>(abuf + i * 16 * KS + aslot[kk]);
 #pragma unroll
             for (int t = 0; t < TW; ++t) {
-                const v4i bf = unpack16(bc[t][kk]);
+                v4i bf;
+                if constexpr (kW8)
+                    bf = __builtin_bit_cast(v4i, bc[t].k[kk]);
+                else
+                    bf = unpack16(bc[t][kk]);
 #pragma unroll
                 for (int i = 0; i < TA; ++i) acc[i][t] = mfma16x16x64(bf, af[i], acc[i][t]);
             }
@@ -1246,7 +1286,7 @@ void gemm_kernel(GemmArgs g) {
 #pragma unroll
         for (int i = 0; i < TA; ++i) {
             const int64_t mb = m0 + wm * WA + 16 * i;
-            const int32_t qs = gld<int32_t>(g.xsum + mb + (lane & 15));
+            const int32_t qs = kW8 ? 0 : gld<int32_t>(g.xsum + mb + (lane & 15));
             const float rs = gld<float>(g.xscale + mb + (lane & 15)) * g.w_scale;
             v4f v[4];
 #pragma unroll
@@ -1262,7 +1302,7 @@ void gemm_kernel(GemmArgs g) {
     for (int i = 0; i < TA; ++i) {
         const int64_t mm = m0 + wm * WA + 16 * i + (lane & 15);
         if (!full && mm >= g.M) continue;
-        const int32_t qs = gld<int32_t>(g.xsum + mm);
+        const int32_t qs = kW8 ? 0 : gld<int32_t>(g.xsum + mm);
         const float rs = gld<float>(g.xscale + mm) * g.w_scale;
         float* yrow = g.y + mm * g.N;
         int32_t* arow = g.acc ? g.acc + mm * g.N : nullptr;
@@ -1545,7 +1585,7 @@ void gemm_persistent_kernel(GemmArgs g) {
 // Shape dispatch of the GEMM: the default tile, or a 128 x 128 tile (waves of
 // 64 x 64) when the default leaves fewer than two workgroups per compute unit
 // (e.g. 4096 x 1536 outputs).
-template <int WA, int WW, int WGM, int WGN, int KS, int NS>
+template <int WA, int WW, int WGM, int WGN, int KS, int NS, bool kW8 = false>
 bt_status launch_gemm(GemmArgs g, hipStream_t stream) {
     constexpr int BM = WA * WGM;
     constexpr int BN = WW * WGN;
@@ -1556,7 +1596,7 @@ bt_status launch_gemm(GemmArgs g, hipStream_t stream) {
     const int64_t grid = int64_t(g.per_xcd) * kXcds;
     if (grid > (int64_t(1) << 31) - 1) return BT_ERR_SHAPE;
     (void)hipGetLastError();
-    hipLaunchKernelGGL((gemm_kernel<WA, WW, WGM, WGN, KS, NS>), dim3(unsigned(grid)),
+    hipLaunchKernelGGL((gemm_kernel<WA, WW, WGM, WGN, KS, NS, kW8>), dim3(unsigned(grid)),
                        dim3(64 * WGM * WGN), 0, stream, g);
     return hipGetLastError() == hipSuccess ? BT_OK : BT_ERR_DEVICE;
 }
@@ -1843,6 +1883,56 @@ extern "C" bt_status bt_ternary_matmul_epilogue(int64_t M, int64_t N, int64_t K,
                                                 hipStream_t stream) {
     return matmul_impl(M, N, K, xq, xscale, xsum, wdev, w_scale, epi, y, acc, workspace,
                        workspace_bytes, stream);
+}
+
+// ------------------------------------------------------------------ I8_S
+
+static bool i8_nk_ok(int64_t N, int64_t K) { return bt_int8_repacked_bytes(N, K) != 0; }
+
+extern "C" bt_status bt_repack_int8(const int8_t* w_dev, int64_t N, int64_t K, void* wdev,
+                                    hipStream_t stream) {
+    if (!w_dev || !wdev) return BT_ERR_NULL;
+    if (!i8_nk_ok(N, K)) return BT_ERR_SHAPE;
+    if (!bt::aligned16(w_dev) || !bt::aligned16(wdev)) return BT_ERR_ALIGN;
+    const int64_t steps64 = bt::ceil_div(K, bt::kSuperK) * (bt::kSuperK / 64);
+    const int64_t blocks = bt::ceil_div(N, bt::kTileN) * steps64;
+    const int64_t grid = std::min<int64_t>(bt::ceil_div(blocks, 4), int64_t(1) << 20);
+    (void)hipGetLastError();
+    hipLaunchKernelGGL(repack_int8_kernel, dim3(unsigned(grid)), dim3(256), 0, stream, w_dev,
+                       int32_t(N), int32_t(K), int32_t(steps64), blocks,
+                       static_cast<int8_t*>(wdev));
+    return launched();
+}
+
+extern "C" bt_status bt_int8_matmul(int64_t M, int64_t N, int64_t K, const int8_t* xq,
+                                    const float* xscale, const void* w8dev, float w_scale,
+                                    const bt_epilogue* epi, float* y, int32_t* acc,
+                                    hipStream_t stream) {
+    if (!xq || !xscale || !w8dev || !y) return BT_ERR_NULL;
+    if (M < 1 || M > (int64_t(1) << 31) - 1 || !i8_nk_ok(N, K)) return BT_ERR_SHAPE;
+    if (!bt::aligned16(xq) || !bt::aligned16(xscale) || !bt::aligned16(w8dev) ||
+        !bt::aligned16(y) || (acc && !bt::aligned16(acc)))
+        return BT_ERR_ALIGN;
+    if (!isfinite(w_scale)) return BT_ERR_VALUE;
+    GemmArgs g;
+    memset(&g, 0, sizeof(g));
+    const bt_status est = epilogue_args(epi, M, N, y, &g.epi);
+    if (est != BT_OK) return est;
+    g.xq = xq;
+    g.xscale = xscale;
+    g.xsum = nullptr;
+    g.w = static_cast<const uint8_t*>(w8dev);
+    g.y = y;
+    g.acc = acc;
+    g.w_scale = w_scale;
+    g.M = int32_t(M);
+    g.N = int32_t(N);
+    g.K = int32_t(K);
+    g.tiles = int32_t(bt::ceil_div(N, bt::kTileN));
+    g.steps = int32_t(bt::ceil_div(K, bt::kSuperK));
+    const int64_t big = bt::ceil_div(M, 128) * bt::ceil_div(N, 256);
+    if (big >= 512) return launch_gemm<128, 64, 1, 4, 128, 2, true>(g, stream);
+    return launch_gemm<64, 64, 2, 2, 128, 2, true>(g, stream);
 }
 
 extern "C" bt_status bt_quantize_act_grouped(const void* plan_host, const void* plan_dev,

@@ -228,6 +228,56 @@ def ternary_matmul_fused(x, wdev, n: int, w_scale: float, y=None, acc=None, xq=N
     return (y, acc) if (want_acc or acc is not None) else y
 
 
+# -------------------------------------------------------------------- I8_S
+
+def int8_repacked_bytes(n: int, k: int) -> int:
+    return int(lib().bt_int8_repacked_bytes(n, k))
+
+
+def repack_int8(w_dev, out=None, stream=None):
+    """int8 (N, K) weights on the device -> the kernels' tile layout (bt_repack_int8)."""
+    torch = _torch()
+    _dev(w_dev, torch.int8, None, "w_dev")
+    if w_dev.dim() != 2:
+        raise ValueError("w_dev must be (N, K)")
+    n, k = w_dev.shape
+    nbytes = int8_repacked_bytes(n, k)
+    if out is None:
+        out = torch.empty(nbytes, dtype=torch.uint8, device=w_dev.device)
+    _dev(out, torch.uint8, (nbytes,), "out")
+    check(lib().bt_repack_int8(_ptr(w_dev), n, k, _ptr(out), _stream(stream)), "bt_repack_int8")
+    return out
+
+
+def int8_matmul(xq, xscale, w8dev, n: int, w_scale: float, y=None, acc=None, want_acc=False,
+                stream=None, bias=None, relu=False, layer_scale=None, residual=None):
+    """The I8_S product y = (xq @ W8^T) * xscale * w_scale (bt_int8_matmul), with the
+    optional fused epilogue; returns y (and acc)."""
+    torch = _torch()
+    _dev(xq, torch.int8, None, "xq")
+    m, k = xq.shape
+    _dev(xscale, torch.float32, (m,), "xscale")
+    _dev(w8dev, torch.uint8, (int8_repacked_bytes(n, k),), "w8dev")
+    if y is None:
+        y = torch.empty((m, n), dtype=torch.float32, device=xq.device)
+    _dev(y, torch.float32, (m, n), "y")
+    if acc is None and want_acc:
+        acc = torch.empty((m, n), dtype=torch.int32, device=xq.device)
+    if acc is not None:
+        _dev(acc, torch.int32, (m, n), "acc")
+    epi = None
+    if bias is not None or relu or layer_scale is not None or residual is not None:
+        for t, shp, name in ((bias, (n,), "bias"), (layer_scale, (n,), "layer_scale"),
+                             (residual, (m, n), "residual")):
+            if t is not None:
+                _dev(t, torch.float32, shp, name)
+        epi = BtEpilogue(_ptr(bias), _ptr(layer_scale), _ptr(residual), 1 if relu else 0, 0)
+    check(lib().bt_int8_matmul(m, n, k, _ptr(xq), _ptr(xscale), _ptr(w8dev), float(w_scale),
+                               None if epi is None else C.byref(epi), _ptr(y), _ptr(acc),
+                               _stream(stream)), "bt_int8_matmul")
+    return (y, acc) if (want_acc or acc is not None) else y
+
+
 # ------------------------------------------------------------------ grouped
 
 class _Plan:
@@ -326,7 +376,7 @@ class MatmulPlan(_Plan):
 
 __all__ = [
     "BtError", "GROUP_K", "GEMV_MAX_M", "packed_bytes", "repacked_bytes",
-    "matmul_workspace_bytes", "pack_ternary", "unpack_ternary", "repack_ternary",
+    "matmul_workspace_bytes", "int8_repacked_bytes", "repack_int8", "int8_matmul", "pack_ternary", "unpack_ternary", "repack_ternary",
     "quantize_act", "rmsnorm_quantize", "new_workspace", "ternary_matmul", "ternary_matmul_fused", "RepackPlan",
     "QuantPlan", "MatmulPlan",
 ]

@@ -1,0 +1,91 @@
+"""GPU parity for the I8_S product (int8 weights x int8 activations) through
+the C ABI against the CPU oracle (oracle/i8s_ref.py): q, d, acc bit-exact and y
+(fp32 rescale, then the fused epilogues of the tokenizer: matrix multiply +
+bias + ReLU, residual addition with layer scale) bit-exact too, every element.
+
+Shapes follow the tokenizer's FFN layers (D -> 4D -> D, "VibeVoice-ASR-BitNet
+Technical Report" section 2.2.1, Table 1), scaled in L where the oracle would
+take long, plus ragged tiles and K not a multiple of the stage width.
+"""
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+import ternary_weight_decoder_bt_amd as bt  # noqa: E402
+
+POISON_I32 = np.iinfo(np.int32).min
+
+
+@pytest.fixture(scope="module")
+def dev():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    return torch.device("cuda:0")
+
+
+def to_dev(a, dev):
+    return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+
+def case(seed, m, n, k):
+    rng = np.random.default_rng(seed)
+    x = synth.small_problem(seed, m, 16, max(k, 128), "t3")["x"][:, :k].copy()
+    w8 = rng.integers(-128, 128, (n, k), dtype=np.int8)
+    return x, w8, np.float32(rng.uniform(0.001, 0.01))
+
+
+def run(x, w8, s, dev, **epi):
+    m, k = x.shape
+    n = w8.shape[0]
+    xq, xs, _ = bt.quantize_act(to_dev(x, dev))
+    w8dev = bt.repack_int8(to_dev(w8, dev))
+    y = torch.full((m, n), float("nan"), dtype=torch.float32, device=dev)
+    acc = torch.full((m, n), POISON_I32, dtype=torch.int32, device=dev)
+    epi = {k_: (to_dev(v, dev) if isinstance(v, np.ndarray) else v) for k_, v in epi.items()}
+    bt.int8_matmul(xq, xs, w8dev, n, s, y=y, acc=acc, **epi)
+    torch.cuda.synchronize()
+    return xq.cpu().numpy(), y.cpu().numpy(), acc.cpu().numpy()
+
+
+@pytest.mark.parametrize("m,n,k", [(1000, 128, 32), (700, 32, 128), (300, 256, 64),
+                                   (4096, 512, 128), (2000, 128, 512), (150, 8192, 2048),
+                                   (150, 2048, 8192), (37, 130, 96), (5, 16, 32),
+                                   (1200, 4096, 1024)])
+def test_i8s_matmul_shapes(dev, m, n, k):
+    x, w8, s = case(40 + k, m, n, k)
+    ref = oracle.i8s_forward_ref(x, w8, s)
+    q, y, acc = run(x, w8, s, dev)
+    assert np.array_equal(q, ref["q"])
+    assert np.array_equal(acc, ref["acc"])
+    assert np.array_equal(y, ref["y"])
+
+
+def test_i8s_extreme_accumulator(dev):
+    k = 8192
+    x = np.full((40, k), -1.0, np.float32)               # q = -127 everywhere
+    w8 = np.full((32, k), -128, np.int8)
+    w8[16:] = 127
+    q, y, acc = run(x, w8, np.float32(1.0), dev)
+    assert (acc[:, :16] == 127 * 128 * k).all() and (acc[:, 16:] == -127 * 127 * k).all()
+
+
+@pytest.mark.parametrize("m,n,k", [(6000, 2048, 512), (1200, 1024, 4096), (37, 130, 96)])
+def test_i8s_fused_tokenizer_epilogues(dev, m, n, k):
+    """mul_mat_add_relu (FFN up: bias + ReLU) and add_scaled (FFN down: layer
+    scale + residual), the tokenizer's fused operators, on the I8_S product."""
+    x, w8, s = case(50 + k, m, n, k)
+    rng = np.random.default_rng(k)
+    bias = rng.standard_normal(n).astype(np.float32)
+    gamma = rng.uniform(-1, 1, n).astype(np.float32)
+    res = rng.standard_normal((m, n)).astype(np.float32)
+    ref = oracle.i8s_forward_ref(x, w8, s)
+    _, y, _ = run(x, w8, s, dev, bias=bias, relu=True)
+    assert np.array_equal(y, oracle.epilogue_ref(ref["y"], bias=bias, relu=True))
+    _, y, _ = run(x, w8, s, dev, layer_scale=gamma, residual=res)
+    assert np.array_equal(y, oracle.epilogue_ref(ref["y"], layer_scale=gamma, residual=res))

@@ -124,6 +124,23 @@ def test_device_entry_points_validate_before_launch():
     assert L.bt_quantize_act(f, 0, 128, f, f, f, None) == SHAPE
     assert L.bt_quantize_act(f, 1, 0, f, f, f, None) == SHAPE
     assert L.bt_quantize_act(f, 1, 128, f + 1, f, f, None) == ALIGN
+    # I8_S
+    assert L.bt_int8_repacked_bytes(16, 32) == 16 * 256
+    assert L.bt_int8_repacked_bytes(17, 288) == 32 * 512
+    for bad in ((0, 32), (16, 16), (16, 48), (16, 131072 + 32)):
+        assert L.bt_int8_repacked_bytes(*bad) == 0
+    assert L.bt_repack_int8(None, 16, 32, f, None) == NULL
+    assert L.bt_repack_int8(f, 16, 48, f, None) == SHAPE
+    assert L.bt_repack_int8(f, 16, 32, f + 8, None) == ALIGN
+    i8 = lambda **kw: [kw.get("M", 2), kw.get("N", 16), kw.get("K", 64), kw.get("xq", f),
+                       kw.get("xs", f), kw.get("w", f), kw.get("scale", 0.5), kw.get("epi", None),
+                       kw.get("y", f), kw.get("acc", None), None]
+    assert L.bt_int8_matmul(*i8(w=None)) == NULL
+    assert L.bt_int8_matmul(*i8(K=100)) == SHAPE
+    assert L.bt_int8_matmul(*i8(M=0)) == SHAPE
+    assert L.bt_int8_matmul(*i8(xs=f + 4)) == ALIGN
+    assert L.bt_int8_matmul(*i8(scale=float("inf"))) == VALUE
+    assert L.bt_int8_matmul(*i8(epi=C.byref(BtEpilogue(f + 4, None, None, 0, 0)))) == ALIGN
     # RMS normalization + quantize
     assert L.bt_rmsnorm_quantize(f, None, 1e-6, 1, 128, f, f, f, None) == NULL
     assert L.bt_rmsnorm_quantize(f, f, 1e-6, 0, 128, f, f, f, None) == SHAPE
