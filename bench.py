@@ -247,7 +247,8 @@ class LongPrefill:
                      "xs": torch.empty(m, dtype=torch.float32, device=dev),
                      "xsum": torch.empty(m, dtype=torch.int32, device=dev),
                      "y": torch.empty((m, n), dtype=torch.float32, device=dev),
-                     "wdev": wdev, "n": n, "k": k, "s": s, "layer": layer, "proj": proj}
+                     "wdev": wdev, "n": n, "k": k, "s": s, "layer": layer, "proj": proj,
+                     "ws": bt.new_workspace(m, n, k, dev)}
                 self.probs.append(p)
                 self.ops += 2 * m * n * k
         torch.cuda.synchronize()
@@ -259,12 +260,14 @@ class LongPrefill:
         bt = self.bt
         for p in self.probs:
             bt.quantize_act(p["x"], p["xq"], p["xs"], p["xsum"])
-            bt.ternary_matmul(p["xq"], p["xs"], p["xsum"], p["wdev"], p["n"], p["s"], y=p["y"])
+            bt.ternary_matmul(p["xq"], p["xs"], p["xsum"], p["wdev"], p["n"], p["s"], y=p["y"],
+                              workspace=p["ws"])
 
     def gemms(self):
         bt = self.bt
         for p in self.probs:
-            bt.ternary_matmul(p["xq"], p["xs"], p["xsum"], p["wdev"], p["n"], p["s"], y=p["y"])
+            bt.ternary_matmul(p["xq"], p["xs"], p["xsum"], p["wdev"], p["n"], p["s"], y=p["y"],
+                              workspace=p["ws"])
 
     def time_shapes(self, reps: int = 20):
         """GEMM time of each of the four shapes (layer 0), each on its own: {name: (ms, TOPS)}."""
@@ -273,7 +276,7 @@ class LongPrefill:
         for p in self.probs[:len(synth.PROJECTIONS)]:
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             call = lambda: bt.ternary_matmul(p["xq"], p["xs"], p["xsum"], p["wdev"], p["n"],
-                                             p["s"], y=p["y"])
+                                             p["s"], y=p["y"], workspace=p["ws"])
             call()
             e0.record()
             for _ in range(reps):
@@ -301,7 +304,7 @@ class LongPrefill:
             name = synth.PROJECTIONS[p["proj"]][0]
             for tag, extra in (("plain", {}), (kind, kw)):
                 call = lambda: bt.ternary_matmul(p["xq"], p["xs"], p["xsum"], p["wdev"], n, p["s"],
-                                                 y=p["y"], **extra)
+                                                 y=p["y"], workspace=p["ws"], **extra)
                 call()
                 e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
                 e0.record()
@@ -381,11 +384,13 @@ def run_i8s_tokenizer_ffn(torch, bt, dev, reps: int = 10):
             w8 = torch.randint(-128, 128, (n, k), dtype=torch.int8, device=dev, generator=gen)
             wdev = bt.repack_int8(w8)
             y = torch.empty((L, n), dtype=torch.float32, device=dev)
-            bt.int8_matmul(xq, xs, wdev, n, 0.01, y=y)
+            need = bt.int8_matmul_workspace_bytes(L, n, k)
+            ws = torch.zeros(need, dtype=torch.uint8, device=dev) if need else None
+            bt.int8_matmul(xq, xs, wdev, n, 0.01, y=y, workspace=ws)
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             e0.record()
             for _ in range(reps):
-                bt.int8_matmul(xq, xs, wdev, n, 0.01, y=y)
+                bt.int8_matmul(xq, xs, wdev, n, 0.01, y=y, workspace=ws)
             e1.record()
             torch.cuda.synchronize()
             ms = e0.elapsed_time(e1) / reps

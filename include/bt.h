@@ -131,22 +131,6 @@ bt_status bt_repack_ternary_grouped(const void* plan_host, const void* plan_dev,
 bt_status bt_quantize_act(const float* x, int64_t M, int64_t K, int8_t* xq, float* xscale,
                           int32_t* xsum, hipStream_t stream);
 
-/* ---------------------------------------------------------------------------
- * Ternary matmul with fp32 rescale (technical report section 2.4.2, Figure 4).
- *
- * acc[m,n] = sum_k xq[m,k] * w[n,k]   (exact int32; |acc| <= 127*K)
- * y[m,n]   = fl32( fl32(acc[m,n]) * fl32(xscale[m] * w_scale) )
- *
- * xq, xscale, xsum: as written by bt_quantize_act (xsum is required: the
- *   kernels multiply by the codes w+1 and subtract xsum).
- * wdev: bt_repack_ternary output for this N, K.
- * y: device fp32 M x N, written. acc: device int32 M x N or NULL.
- * workspace: device, at least bt_matmul_workspace_bytes(M,N,K) bytes (may be
- *   NULL when that is 0). It must be zero-filled before its first use; every
- *   completed call leaves it zero-filled again. Calls that share one workspace
- *   must be ordered on one stream.
- * w_scale must be finite (BT_ERR_VALUE otherwise).
- * ------------------------------------------------------------------------- */
 /* RMS normalization with a per-channel scale fused with the quantization above
  * ("VibeVoice-ASR-BitNet Technical Report" section 2.4.1: rms_norm_scaled, an
  * RMS normalization with a scale parameter; section 2.2.2: INT8 activations
@@ -161,6 +145,26 @@ bt_status bt_quantize_act(const float* x, int64_t M, int64_t K, int8_t* xq, floa
 bt_status bt_rmsnorm_quantize(const float* x, const float* g, float eps, int64_t M, int64_t K,
                               int8_t* xq, float* xscale, int32_t* xsum, hipStream_t stream);
 
+/* ---------------------------------------------------------------------------
+ * Ternary matmul with fp32 rescale (technical report section 2.4.2, Figure 4).
+ *
+ * acc[m,n] = sum_k xq[m,k] * w[n,k]   (exact int32; |acc| <= 127*K)
+ * y[m,n]   = fl32( fl32(acc[m,n]) * fl32(xscale[m] * w_scale) )
+ *
+ * xq, xscale, xsum: as written by bt_quantize_act (xsum is required: the
+ *   kernels multiply by the codes w+1 and subtract xsum).
+ * wdev: bt_repack_ternary output for this N, K.
+ * y: device fp32 M x N, written. acc: device int32 M x N or NULL.
+ * workspace: device, at least bt_matmul_workspace_bytes(M,N,K) bytes (may be
+ *   NULL when that is 0). It must be zero-filled before its first use; every
+ *   completed call leaves it ready for the next one (whatever must start at
+ *   zero is back at zero). Calls that share one workspace must be ordered on
+ *   one stream. A shape needs one when K is split for
+ *   parallelism: small-N GEMVs (M <= 16), and GEMMs whose output has few
+ *   tiles (fewer than half the device's compute units); the int32 partial sums meet in it
+ *   (exact in any order) and the last K range to arrive stores the output.
+ * w_scale must be finite (BT_ERR_VALUE otherwise).
+ * ------------------------------------------------------------------------- */
 size_t bt_matmul_workspace_bytes(int64_t M, int64_t N, int64_t K);
 
 /* Quantization fused into the GEMV (M <= BT_GEMV_MAX_M): the same result as
@@ -224,11 +228,17 @@ size_t bt_int8_repacked_bytes(int64_t N, int64_t K);
 bt_status bt_repack_int8(const int8_t* w_dev, int64_t N, int64_t K, void* wdev,
                          hipStream_t stream);
 
+/* Workspace bt_int8_matmul needs for this shape (0 if none): shapes with too
+ * few output tiles to fill the device split K, and the partial sums meet in
+ * the workspace. Same rules as for bt_ternary_matmul's workspace. */
+size_t bt_int8_matmul_workspace_bytes(int64_t M, int64_t N, int64_t K);
+
 /* xq: device int8 M x K; xscale: device fp32 [M]; w8dev from bt_repack_int8;
  * epi: host, NULL for none (as bt_ternary_matmul_epilogue); acc may be NULL. */
 bt_status bt_int8_matmul(int64_t M, int64_t N, int64_t K, const int8_t* xq, const float* xscale,
                          const void* w8dev, float w_scale, const bt_epilogue* epi, float* y,
-                         int32_t* acc, hipStream_t stream);
+                         int32_t* acc, void* workspace, size_t workspace_bytes,
+                         hipStream_t stream);
 
 /* ---------------------------------------------------------------------------
  * Grouped launches: many independent projections in one kernel launch.

@@ -17,6 +17,7 @@ from .ops import (  # noqa: F401
     QuantPlan,
     RepackPlan,
     int8_matmul,
+    int8_matmul_workspace_bytes,
     int8_repacked_bytes,
     matmul_workspace_bytes,
     new_workspace,

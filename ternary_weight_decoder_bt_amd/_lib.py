@@ -36,7 +36,8 @@ SIGNATURES = {
                                           _sz, _p]),
     "bt_int8_repacked_bytes": (_sz, [_i64, _i64]),
     "bt_repack_int8": (C.c_int, [_p, _i64, _i64, _p, _p]),
-    "bt_int8_matmul": (C.c_int, [_i64, _i64, _i64, _p, _p, _p, _f, _p, _p, _p, _p]),
+    "bt_int8_matmul_workspace_bytes": (_sz, [_i64, _i64, _i64]),
+    "bt_int8_matmul": (C.c_int, [_i64, _i64, _i64, _p, _p, _p, _f, _p, _p, _p, _p, _sz, _p]),
     "bt_repack_plan_bytes": (_sz, [_i32]),
     "bt_repack_plan_build": (C.c_int, [_p, _i32, _p, _sz]),
     "bt_repack_ternary_grouped": (C.c_int, [_p, _p, _p]),

@@ -137,14 +137,48 @@ size_t gemv_workspace_bytes(const GemvDesc& d) {
     return gemv_partial_bytes(d) + ((size_t(d.tiles) * sizeof(uint32_t) + 255) & ~size_t(255));
 }
 
+GemmChoice gemm_choice(int64_t M, int64_t N, int64_t K, bool int8_weights, bool persistent_ok) {
+    GemmChoice c{1, 1, 0, 0};
+    const int64_t wide = ceil_div(M, 128) * ceil_div(N, 256);
+    if (wide >= kGemmSlots) {
+        c.kind = persistent_ok && !int8_weights ? 0 : 1;
+        c.tiles = wide;
+        return c;
+    }
+    c.kind = 2;
+    c.tiles = ceil_div(M, 128) * ceil_div(N, 128);
+    const int64_t nst = ceil_div(K, int8_weights ? 128 : 256);
+    // split only below one tile per two compute units: every range stores an
+    // M x N int32 slice and a second launch reads them all back, which costs
+    // more than it gains at higher occupancy (measured)
+    int64_t splits = 1;
+    if (c.tiles < kGemmSlots / 4 && nst >= 8)
+        splits = std::min<int64_t>(ceil_div(kGemmSlots, c.tiles), nst / 4);
+    const int64_t sps = ceil_div(nst, std::max<int64_t>(splits, 1));
+    c.sps = int(sps);
+    c.splits = int(ceil_div(nst, sps));
+    return c;
+}
+
+size_t gemm_workspace_bytes(const GemmChoice& c, int64_t M, int64_t N) {
+    if (c.splits <= 1) return 0;
+    return gemm_slice_bytes(M, N) * size_t(c.splits);
+}
+
 }  // namespace bt
 
 extern "C" size_t bt_matmul_workspace_bytes(int64_t M, int64_t N, int64_t K) {
     if (M < 1 || !valid_nk(N, K)) return 0;
-    if (M > BT_GEMV_MAX_M) return 0;   // the GEMM path splits nothing
+    if (M > BT_GEMV_MAX_M)
+        return bt::gemm_workspace_bytes(bt::gemm_choice(M, N, K, false, true), M, N);
     bt::GemvDesc d;
     bt::gemv_shape(M, N, K, false, &d);
     return bt::gemv_workspace_bytes(d);
+}
+
+extern "C" size_t bt_int8_matmul_workspace_bytes(int64_t M, int64_t N, int64_t K) {
+    if (M < 1 || bt_int8_repacked_bytes(N, K) == 0) return 0;
+    return bt::gemm_workspace_bytes(bt::gemm_choice(M, N, K, true, false), M, N);
 }
 
 // ------------------------------------------------------------------ plans

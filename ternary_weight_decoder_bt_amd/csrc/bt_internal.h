@@ -105,6 +105,24 @@ void gemv_shape(int64_t M, int64_t N, int64_t K, bool grouped, GemvDesc* d);
 size_t gemv_workspace_bytes(const GemvDesc& d);
 size_t gemv_partial_bytes(const GemvDesc& d);
 
+// GEMM shape choice (M > 16), made from the shape alone so that the host can
+// size the workspace: the persistent kernel (128 x 256 tiles), the tiled
+// kernel with 128 x 256 tiles, or with 128 x 128 tiles and K split into
+// `splits` ranges of `sps` stages when there are too few tiles to fill the
+// device (partial sums meet in an int32 workspace).
+constexpr int kGemmSlots = 512;   // resident workgroups the split choice aims at
+struct GemmChoice {
+    int kind;        // 0 persistent, 1 tiled 128 x 256, 2 tiled 128 x 128
+    int splits;      // K ranges (kind 2), else 1
+    int sps;         // stages per range (stage = 256-wide K for ternary, 128 for int8)
+    int64_t tiles;   // output tiles of the chosen kind
+};
+GemmChoice gemm_choice(int64_t M, int64_t N, int64_t K, bool int8_weights, bool persistent_ok);
+size_t gemm_workspace_bytes(const GemmChoice& c, int64_t M, int64_t N);
+inline size_t gemm_slice_bytes(int64_t M, int64_t N) {
+    return (size_t(M) * size_t(N) * sizeof(int32_t) + 255) & ~size_t(255);
+}
+
 inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 }  // namespace bt

@@ -1007,6 +1007,9 @@ struct GemmArgs {
     int32_t M, N, K, tiles, steps;   // steps: 256-wide stages (Kp / 256)
     int32_t m_tiles, n_tiles, per_xcd;
     EpiArgs epi;
+    int32_t splits, sps;    // K ranges per tile and stages per range (1, all: no split)
+    int32_t* ws;            // split K: one M x N int32 slice of partial sums per range
+    int64_t ws_slice;       // int32 elements from one slice to the next
 };
 
 constexpr int kXcds = 8;
@@ -1109,8 +1112,11 @@ void gemm_kernel(GemmArgs g) {
     static_assert(NS >= 2 && (NS - 2) * kLoads < 64, "pipeline depth");
     static_assert(kDmaPerWave * 64 * NW == BM * CPR, "A stage must split evenly over waves");
     __shared__ __attribute__((aligned(16))) int8_t As[NS * kStage];
+    // After the main loop the stage buffers are idle (a barrier makes sure):
+    // the row-wise epilogue's blocks live in them.
     constexpr bool kRowStores = WW == 64;   // row-wise epilogue through LDS
-    __shared__ __attribute__((aligned(16))) float Ep[kRowStores ? NW * 16 * 64 : 4];
+    float* const Ep = reinterpret_cast<float*>(As);
+    static_assert(NS * kStage >= NW * 16 * 64 * 4, "epilogue blocks fit the stage buffers");
 
     // Swizzled LDS slot of logical chunk c of row r: the 16 rows an MFMA
     // fragment read serves at once land in 16 distinct 4-bank groups.
@@ -1118,9 +1124,13 @@ void gemm_kernel(GemmArgs g) {
         return KS == 256 ? (c ^ (r & 15)) : (c ^ ((r >> 1) & 7));
     };
 
+    // work unit = (tile, K range); a unit's ranges sit next to each other so
+    // they run on the same XCD and share its L2
     const int xcd = blockIdx.x % kXcds;
-    const int tile_id = xcd * g.per_xcd + blockIdx.x / kXcds;
-    if (tile_id >= g.m_tiles * g.n_tiles) return;
+    const int unit = xcd * g.per_xcd + blockIdx.x / kXcds;
+    if (unit >= g.m_tiles * g.n_tiles * g.splits) return;
+    const int tile_id = unit / g.splits;
+    const int split = unit - tile_id * g.splits;
     const int mt = tile_id / g.n_tiles;
     const int nt = tile_id - mt * g.n_tiles;
 
@@ -1135,6 +1145,8 @@ void gemm_kernel(GemmArgs g) {
     // a tile's 256-wide step is 1 KB of 2-bit codes, or 4 KB of int8 weights
     const uint32_t tile_bytes = uint32_t(g.steps) * (kW8 ? 4096u : 1024u);
     const int nst = (g.K + KS - 1) / KS;
+    const int sb = split * g.sps;                 // first stage of this K range
+    const int lst = min(g.sps, nst - sb);         // its stages
 
     // This wave's weight tiles as one buffer. The tile is part of the
     // per-lane (VGPR) offset, which the buffer's range check sees, so tiles
@@ -1228,10 +1240,10 @@ void gemm_kernel(GemmArgs g) {
     // constant (conditional issues would make the compiler's own counts
     // conservative and stall on loads just issued).
     BVec b[NS][TW];
-    auto issue = [&](int buf, BVec (&bn)[TW], int s) {
-        const uint32_t pad = s < nst ? 0u : kNowhere;
-        load_b(bn, s, pad);   // weights first: the stage wait then covers both
-        load_a(buf, s, pad);
+    auto issue = [&](int buf, BVec (&bn)[TW], int ls) {
+        const uint32_t pad = ls < lst ? 0u : kNowhere;
+        load_b(bn, sb + ls, pad);   // weights first: the stage wait then covers both
+        load_a(buf, sb + ls, pad);
     };
     auto consume = [&](int buf, const BVec (&bc)[TW]) {
         const int8_t* abuf = afrag + buf * kStage;
@@ -1253,7 +1265,7 @@ void gemm_kernel(GemmArgs g) {
         }
     };
 
-    const int nst_pad = (nst + NS - 1) / NS * NS;
+    const int nst_pad = (lst + NS - 1) / NS * NS;
 #pragma unroll
     for (int p = 0; p < NS - 1; ++p) issue(p, b[p], p);
     for (int s0 = 0; s0 < nst_pad; s0 += NS) {
@@ -1273,9 +1285,35 @@ void gemm_kernel(GemmArgs g) {
             consume(u, b[u]);
         }
     }
-    // the padding loads still in flight write zeros into LDS: let them land
-    // before the workgroup can exit
+    // the padding loads still in flight write zeros into LDS: let them land,
+    // and let every wave finish reading the stages, before LDS is reused
     wait_vmcnt<0>();
+    __syncthreads();
+
+    // Split K: this range's partial sums go to its own slice of the
+    // workspace; splitk_reduce_kernel, launched next, adds the slices and
+    // stores the output (the kernel boundary orders the two, with no fence).
+    if (g.splits > 1) {
+        int32_t* slice = g.ws + split * g.ws_slice;
+        const bool vec = (g.N & 3) == 0;
+#pragma unroll
+        for (int i = 0; i < TA; ++i) {
+            const int64_t mm = m0 + wm * WA + 16 * i + (lane & 15);
+            if (mm >= g.M) continue;
+#pragma unroll
+            for (int t = 0; t < TW; ++t) {
+                const int n = n0 + wn * WW + 16 * t + 4 * (lane >> 4);
+                if (vec && n + 3 < g.N) {
+                    gst<v4i>(slice + mm * g.N + n, acc[i][t]);
+                } else {
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        if (n + r < g.N) gst<int32_t>(slice + mm * g.N + n + r, acc[i][t][r]);
+                }
+            }
+        }
+        return;
+    }
 
     // epilogue: acc[i][t][r] = C[n = n0 + wn*WW + 16t + 4(l/16) + r][m = m0 + wm*WA + 16i + l%16]
     const int nq = n0 + wn * WW + 4 * (lane >> 4);
@@ -1591,7 +1629,11 @@ bt_status launch_gemm(GemmArgs g, hipStream_t stream) {
     constexpr int BN = WW * WGN;
     g.m_tiles = int32_t(bt::ceil_div(g.M, BM));
     g.n_tiles = int32_t(bt::ceil_div(g.N, BN));
-    const int64_t total = int64_t(g.m_tiles) * g.n_tiles;
+    if (g.splits <= 1) {
+        g.splits = 1;
+        g.sps = int32_t(bt::ceil_div(g.K, KS));
+    }
+    const int64_t total = int64_t(g.m_tiles) * g.n_tiles * g.splits;
     g.per_xcd = int32_t(bt::ceil_div(total, kXcds));
     const int64_t grid = int64_t(g.per_xcd) * kXcds;
     if (grid > (int64_t(1) << 31) - 1) return BT_ERR_SHAPE;
@@ -1651,23 +1693,81 @@ bt_status launch_gemm_persistent(GemmArgs g, hipStream_t stream) {
     return hipGetLastError() == hipSuccess ? BT_OK : BT_ERR_DEVICE;
 }
 
-bt_status dispatch_gemm(const GemmArgs& g, hipStream_t stream) {
-#if BT_GEMM_PERSISTENT
-    {
-        constexpr int BM = BT_GEMM_P_WA;
-        constexpr int BN = 64 * BT_GEMM_P_NW;
-        const int64_t tiles = bt::ceil_div(g.M, BM) * bt::ceil_div(g.N, BN);
-        if (tiles >= 2 * int64_t(device_cus()) && !epi_any(g.epi))
-            return launch_gemm_persistent<BT_GEMM_P_WA, 64, BT_GEMM_P_NW, 128, BT_GEMM_P_NS>(g,
-                                                                                        stream);
+// Split K, second launch: output element (m, n .. n+3) = the sum of its
+// partial sums over the K ranges (exact int32), then the same rescale and
+// epilogue as the GEMM kernels: one thread per 4 consecutive outputs.
+template <bool kW8>
+__global__ __launch_bounds__(256) void splitk_reduce_kernel(GemmArgs g) {
+    const int64_t quads = int64_t(g.M) * ((g.N + 3) / 4);
+    for (int64_t qd = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; qd < quads;
+         qd += int64_t(gridDim.x) * blockDim.x) {
+        const int64_t m = qd / ((g.N + 3) / 4);
+        const int n = int((qd - m * ((g.N + 3) / 4)) * 4);
+        const int64_t o = m * g.N + n;
+        const int32_t qs = kW8 ? 0 : gld<int32_t>(g.xsum + m);
+        const float rs = gld<float>(g.xscale + m) * g.w_scale;
+        if ((g.N & 3) == 0) {
+            v4i a = gld<v4i>(g.ws + o);
+            for (int sp = 1; sp < g.splits; ++sp) a += gld<v4i>(g.ws + sp * g.ws_slice + o);
+            a -= qs;
+            v4f y = {float(a.x) * rs, float(a.y) * rs, float(a.z) * rs, float(a.w) * rs};
+            y = epi_col4(g.epi, y, n);
+            if (g.epi.res) y = gld<v4f>(g.epi.res + o) + y;
+            __builtin_nontemporal_store(y, (BT_GLOBAL v4f*)(g.y + o));
+            if (g.acc) gst<v4i>(g.acc + o, a);
+        } else {
+            for (int r = 0; r < 4 && n + r < g.N; ++r) {
+                int32_t a = gld<int32_t>(g.ws + o + r);
+                for (int sp = 1; sp < g.splits; ++sp) a += gld<int32_t>(g.ws + sp * g.ws_slice + o + r);
+                a -= qs;
+                float y = epi_col(g.epi, float(a) * rs, n + r);
+                if (g.epi.res) y = g.epi.res[o + r] + y;
+                g.y[o + r] = y;
+                if (g.acc) g.acc[o + r] = a;
+            }
+        }
     }
+}
+
+template <bool kW8>
+bt_status launch_splitk_reduce(const GemmArgs& g, hipStream_t stream) {
+    const int64_t quads = int64_t(g.M) * ((g.N + 3) / 4);
+    const int64_t grid = std::min<int64_t>(bt::ceil_div(quads, 256), int64_t(1) << 20);
+    hipLaunchKernelGGL(splitk_reduce_kernel<kW8>, dim3(unsigned(grid)), dim3(256), 0, stream, g);
+    return hipGetLastError() == hipSuccess ? BT_OK : BT_ERR_DEVICE;
+}
+
+// Runs the kernel gemm_choice picked for the shape; with split K, binds the
+// workspace (partial sums, then one counter per tile).
+bt_status dispatch_gemm(GemmArgs g, bool int8_weights, void* workspace, size_t workspace_bytes,
+                        hipStream_t stream) {
+    const bt::GemmChoice c =
+        bt::gemm_choice(g.M, g.N, g.K, int8_weights, BT_GEMM_PERSISTENT && !epi_any(g.epi));
+    g.splits = 1;
+    if (c.splits > 1) {
+        const size_t need = bt::gemm_workspace_bytes(c, g.M, g.N);
+        if (!workspace || workspace_bytes < need) return BT_ERR_WORKSPACE;
+        if (!bt::aligned16(workspace)) return BT_ERR_ALIGN;
+        g.splits = c.splits;
+        g.sps = c.sps;
+        g.ws = static_cast<int32_t*>(workspace);
+        g.ws_slice = int64_t(bt::gemm_slice_bytes(g.M, g.N) / sizeof(int32_t));
+    }
+    bt_status st;
+    if (int8_weights) {
+        st = c.kind == 2 ? launch_gemm<64, 64, 2, 2, 128, 2, true>(g, stream)
+                         : launch_gemm<128, 64, 1, 4, 128, 2, true>(g, stream);
+        if (st == BT_OK && g.splits > 1) st = launch_splitk_reduce<true>(g, stream);
+        return st;
+    }
+#if BT_GEMM_PERSISTENT
+    if (c.kind == 0)
+        return launch_gemm_persistent<BT_GEMM_P_WA, 64, BT_GEMM_P_NW, 128, BT_GEMM_P_NS>(g, stream);
 #endif
-    constexpr int BM = BT_GEMM_WA * BT_GEMM_WGM;
-    constexpr int BN = BT_GEMM_WW * BT_GEMM_WGN;
-    const int64_t blocks = bt::ceil_div(g.M, BM) * bt::ceil_div(g.N, BN);
-    if (blocks < 512) return launch_gemm<64, 64, 2, 2, 256, 2>(g, stream);
-    return launch_gemm<BT_GEMM_WA, BT_GEMM_WW, BT_GEMM_WGM, BT_GEMM_WGN, BT_GEMM_KS, BT_GEMM_NS>(
-        g, stream);
+    st = c.kind == 2 ? launch_gemm<64, 64, 2, 2, 256, 2>(g, stream)
+                     : launch_gemm<128, 64, 1, 4, 128, 2>(g, stream);
+    if (st == BT_OK && g.splits > 1) st = launch_splitk_reduce<false>(g, stream);
+    return st;
 }
 
 bt_status launched() {
@@ -1864,7 +1964,7 @@ static bt_status matmul_impl(int64_t M, int64_t N, int64_t K, const int8_t* xq,
     g.K = int32_t(K);
     g.tiles = int32_t(bt::ceil_div(N, bt::kTileN));
     g.steps = int32_t(bt::ceil_div(K, bt::kSuperK));
-    return dispatch_gemm(g, stream);
+    return dispatch_gemm(g, false, workspace, workspace_bytes, stream);
 }
 
 extern "C" bt_status bt_ternary_matmul(int64_t M, int64_t N, int64_t K, const int8_t* xq,
@@ -1907,7 +2007,7 @@ extern "C" bt_status bt_repack_int8(const int8_t* w_dev, int64_t N, int64_t K, v
 extern "C" bt_status bt_int8_matmul(int64_t M, int64_t N, int64_t K, const int8_t* xq,
                                     const float* xscale, const void* w8dev, float w_scale,
                                     const bt_epilogue* epi, float* y, int32_t* acc,
-                                    hipStream_t stream) {
+                                    void* workspace, size_t workspace_bytes, hipStream_t stream) {
     if (!xq || !xscale || !w8dev || !y) return BT_ERR_NULL;
     if (M < 1 || M > (int64_t(1) << 31) - 1 || !i8_nk_ok(N, K)) return BT_ERR_SHAPE;
     if (!bt::aligned16(xq) || !bt::aligned16(xscale) || !bt::aligned16(w8dev) ||
@@ -1930,9 +2030,7 @@ extern "C" bt_status bt_int8_matmul(int64_t M, int64_t N, int64_t K, const int8_
     g.K = int32_t(K);
     g.tiles = int32_t(bt::ceil_div(N, bt::kTileN));
     g.steps = int32_t(bt::ceil_div(K, bt::kSuperK));
-    const int64_t big = bt::ceil_div(M, 128) * bt::ceil_div(N, 256);
-    if (big >= 512) return launch_gemm<128, 64, 1, 4, 128, 2, true>(g, stream);
-    return launch_gemm<64, 64, 2, 2, 128, 2, true>(g, stream);
+    return dispatch_gemm(g, true, workspace, workspace_bytes, stream);
 }
 
 extern "C" bt_status bt_quantize_act_grouped(const void* plan_host, const void* plan_dev,

@@ -249,8 +249,13 @@ def repack_int8(w_dev, out=None, stream=None):
     return out
 
 
+def int8_matmul_workspace_bytes(m: int, n: int, k: int) -> int:
+    return int(lib().bt_int8_matmul_workspace_bytes(m, n, k))
+
+
 def int8_matmul(xq, xscale, w8dev, n: int, w_scale: float, y=None, acc=None, want_acc=False,
-                stream=None, bias=None, relu=False, layer_scale=None, residual=None):
+                stream=None, bias=None, relu=False, layer_scale=None, residual=None,
+                workspace=None):
     """The I8_S product y = (xq @ W8^T) * xscale * w_scale (bt_int8_matmul), with the
     optional fused epilogue; returns y (and acc)."""
     torch = _torch()
@@ -272,9 +277,13 @@ def int8_matmul(xq, xscale, w8dev, n: int, w_scale: float, y=None, acc=None, wan
             if t is not None:
                 _dev(t, torch.float32, shp, name)
         epi = BtEpilogue(_ptr(bias), _ptr(layer_scale), _ptr(residual), 1 if relu else 0, 0)
+    need = int8_matmul_workspace_bytes(m, n, k)
+    if need and workspace is None:
+        workspace = torch.zeros(need, dtype=torch.uint8, device=xq.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     check(lib().bt_int8_matmul(m, n, k, _ptr(xq), _ptr(xscale), _ptr(w8dev), float(w_scale),
                                None if epi is None else C.byref(epi), _ptr(y), _ptr(acc),
-                               _stream(stream)), "bt_int8_matmul")
+                               _ptr(workspace), ws_bytes, _stream(stream)), "bt_int8_matmul")
     return (y, acc) if (want_acc or acc is not None) else y
 
 
@@ -376,7 +385,7 @@ class MatmulPlan(_Plan):
 
 __all__ = [
     "BtError", "GROUP_K", "GEMV_MAX_M", "packed_bytes", "repacked_bytes",
-    "matmul_workspace_bytes", "int8_repacked_bytes", "repack_int8", "int8_matmul", "pack_ternary", "unpack_ternary", "repack_ternary",
+    "matmul_workspace_bytes", "int8_repacked_bytes", "repack_int8", "int8_matmul", "int8_matmul_workspace_bytes", "pack_ternary", "unpack_ternary", "repack_ternary",
     "quantize_act", "rmsnorm_quantize", "new_workspace", "ternary_matmul", "ternary_matmul_fused", "RepackPlan",
     "QuantPlan", "MatmulPlan",
 ]

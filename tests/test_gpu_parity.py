@@ -443,3 +443,23 @@ def test_grouped_mixed_m_with_lds_split(dev, fused):
         torch.cuda.synchronize()
         _check_grouped(items, refs)
     assert int(plan.workspace.count_nonzero()) == 0
+
+
+@pytest.mark.parametrize("m,n,k", [(150, 1536, 8960), (520, 1540, 8960), (17, 130, 2048)])
+def test_gemm_split_k_exact_and_workspace_clean(dev, m, n, k):
+    """Few output tiles and a long K: K is split and the int32 partial sums meet
+    in the workspace; the result is the oracle's, bit for bit, on two calls in a
+    row with the same workspace (poisoned in between: every slice is rewritten)."""
+    need = bt.matmul_workspace_bytes(m, n, k)
+    assert need > 0
+    c = synth.small_problem(60, m, n, k, "t3", (0.2, 0.6, 0.2))
+    ref = oracle.forward_ref(c["x"], c["w"], c["w_scale"], "f64")
+    ws = torch.zeros(need, dtype=torch.uint8, device=dev)
+    wdev = load_weights(c["w"], dev)
+    xq, xs, xsum = (to_dev(ref[k_], dev) for k_ in ("q", "d", "qsum"))
+    for _ in range(2):
+        y, acc = run_matmul(xq, xs, xsum, wdev, n, c["w_scale"], dev, workspace=ws)
+        torch.cuda.synchronize()
+        assert_exact("acc", acc.cpu().numpy(), ref["acc"])
+        assert np.array_equal(y.cpu().numpy(), ref["y"])
+        ws.fill_(0x5A)

@@ -99,6 +99,10 @@ def test_unpack_rejects_code_three():
     assert e.value.status == VALUE
 
 
+def L_i8_ws(m, n, k):
+    return bt.lib().bt_int8_matmul_workspace_bytes(m, n, k)
+
+
 def test_sizes():
     assert bt.packed_bytes(1536, 1536) == 589_824
     assert bt.packed_bytes(10, 100) == 0 and bt.repacked_bytes(0, 128) == 0
@@ -108,7 +112,16 @@ def test_sizes():
     total = 28 * sum(bt.packed_bytes(n, k) for k, n in
                      [(1536, 2048), (1536, 1536), (1536, 17920), (8960, 1536)])
     assert total == 327_548_928
-    assert bt.matmul_workspace_bytes(17, 1536, 1536) == 0    # GEMM path needs none
+    # GEMM: none when the output has enough tiles; split K (one M x N int32
+    # slice of partial sums per K range) when it has fewer tiles than half the
+    # compute units and a long K
+    assert bt.matmul_workspace_bytes(4096, 17920, 1536) == 0
+    assert bt.matmul_workspace_bytes(4096, 1536, 8960) == 0   # 384 tiles: enough
+    assert bt.matmul_workspace_bytes(17, 1536, 1536) == 0     # too short a K to split
+    # 2 x 12 tiles, 35 stages: min(ceil(512/24), 35//4) = 8 ranges of 5 -> 7 ranges
+    assert bt.matmul_workspace_bytes(150, 1536, 8960) == 7 * 150 * 1536 * 4
+    # 2 x 16 tiles, 64 stages of 128: min(16, 16) = 16 ranges of 4
+    assert L_i8_ws(150, 2048, 8192) == 16 * 150 * 2048 * 4
     assert bt.matmul_workspace_bytes(1, 1536, 1536) > 0       # split K on a small matrix
 
 
@@ -134,13 +147,18 @@ def test_device_entry_points_validate_before_launch():
     assert L.bt_repack_int8(f, 16, 32, f + 8, None) == ALIGN
     i8 = lambda **kw: [kw.get("M", 2), kw.get("N", 16), kw.get("K", 64), kw.get("xq", f),
                        kw.get("xs", f), kw.get("w", f), kw.get("scale", 0.5), kw.get("epi", None),
-                       kw.get("y", f), kw.get("acc", None), None]
+                       kw.get("y", f), kw.get("acc", None), kw.get("ws", None),
+                       kw.get("wsb", 0), None]
     assert L.bt_int8_matmul(*i8(w=None)) == NULL
     assert L.bt_int8_matmul(*i8(K=100)) == SHAPE
     assert L.bt_int8_matmul(*i8(M=0)) == SHAPE
     assert L.bt_int8_matmul(*i8(xs=f + 4)) == ALIGN
     assert L.bt_int8_matmul(*i8(scale=float("inf"))) == VALUE
     assert L.bt_int8_matmul(*i8(epi=C.byref(BtEpilogue(f + 4, None, None, 0, 0)))) == ALIGN
+    need = L.bt_int8_matmul_workspace_bytes(150, 2048, 8192)
+    assert L.bt_int8_matmul(*i8(M=150, N=2048, K=8192)) == WORKSPACE
+    assert L.bt_int8_matmul(*i8(M=150, N=2048, K=8192, ws=f, wsb=need - 1)) == WORKSPACE
+    assert L.bt_int8_matmul(*i8(M=150, N=2048, K=8192, ws=f + 4, wsb=need)) == ALIGN
     # RMS normalization + quantize
     assert L.bt_rmsnorm_quantize(f, None, 1e-6, 1, 128, f, f, f, None) == NULL
     assert L.bt_rmsnorm_quantize(f, f, 1e-6, 0, 128, f, f, f, None) == SHAPE
@@ -161,6 +179,11 @@ def test_device_entry_points_validate_before_launch():
     assert L.bt_ternary_matmul(*args(acc=f + 2)) == ALIGN
     assert L.bt_ternary_matmul(*args(scale=float("inf"))) == VALUE
     assert L.bt_ternary_matmul(*args(scale=float("nan"))) == VALUE
+    # a GEMM with a split K without (enough) workspace
+    need = bt.matmul_workspace_bytes(150, 1536, 8960)
+    assert L.bt_ternary_matmul(*args(M=150, N=1536, K=8960)) == WORKSPACE
+    assert L.bt_ternary_matmul(*args(M=150, N=1536, K=8960, ws=f, wsb=need - 4)) == WORKSPACE
+    assert L.bt_ternary_matmul(*args(M=150, N=1536, K=8960, ws=f + 4, wsb=need)) == ALIGN
     # the epilogue entry point: same checks, plus the epilogue's own
     eargs = lambda epi, **kw: args(**kw)[:8] + [epi] + args(**kw)[8:]
     assert L.bt_ternary_matmul_epilogue(*eargs(None, y=None)) == NULL
