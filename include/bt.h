@@ -156,13 +156,13 @@ bt_status bt_rmsnorm_quantize(const float* x, const float* g, float eps, int64_t
  * wdev: bt_repack_ternary output for this N, K.
  * y: device fp32 M x N, written. acc: device int32 M x N or NULL.
  * workspace: device, at least bt_matmul_workspace_bytes(M,N,K) bytes (may be
- *   NULL when that is 0). It must be zero-filled before its first use; every
- *   completed call leaves it ready for the next one (whatever must start at
- *   zero is back at zero). Calls that share one workspace must be ordered on
- *   one stream. A shape needs one when K is split for
- *   parallelism: small-N GEMVs (M <= 16), and GEMMs whose output has few
- *   tiles (fewer than half the device's compute units); the int32 partial sums meet in it
- *   (exact in any order) and the last K range to arrive stores the output.
+ *   NULL when that is 0); its contents on entry do not matter. A shape needs
+ *   one when its K is split: GEMVs (M <= 16) whose M x K int8 activations do
+ *   not fit one workgroup's LDS slice, and GEMMs with fewer than 128 output
+ *   tiles of 128 x 64. Each K range writes its int32 partial sums to a slice
+ *   of its own, and a second launch adds the slices in a fixed order (exact)
+ *   and applies the scales and the epilogue. Calls that share one workspace
+ *   must be ordered on one stream.
  * w_scale must be finite (BT_ERR_VALUE otherwise).
  * ------------------------------------------------------------------------- */
 size_t bt_matmul_workspace_bytes(int64_t M, int64_t N, int64_t K);
@@ -229,8 +229,8 @@ bt_status bt_repack_int8(const int8_t* w_dev, int64_t N, int64_t K, void* wdev,
                          hipStream_t stream);
 
 /* Workspace bt_int8_matmul needs for this shape (0 if none): shapes with too
- * few output tiles to fill the device split K, and the partial sums meet in
- * the workspace. Same rules as for bt_ternary_matmul's workspace. */
+ * few output tiles to fill the device split K, each K range writing its partial
+ * sums to a slice of the workspace. Same rules as for bt_ternary_matmul's. */
 size_t bt_int8_matmul_workspace_bytes(int64_t M, int64_t N, int64_t K);
 
 /* xq: device int8 M x K; xscale: device fp32 [M]; w8dev from bt_repack_int8;

@@ -96,11 +96,9 @@ namespace bt {
 // Work split of a GEMV. Each wave streams tiles_per_wave 16-row tiles over one
 // K chunk; a workgroup (4 waves) first stages its chunk of the M activation
 // rows (and a zero row) in LDS, so a chunk is at most
-// kGemvLdsBytes / (256 (M + 1)) steps. A single
-// call on a small matrix (e.g. 1536 rows) has too few tiles to keep 256
-// compute units streaming, so it also cuts K until about kTargetBlocks
-// workgroups exist (chunks of at least two steps). A grouped launch has
-// parallelism across problems and splits K only for the LDS slice.
+// kGemvLdsBytes / (256 (M + 1)) steps; K is split only for that. (Splitting
+// K further for parallelism was measured to lose: the cross-workgroup
+// synchronization it needs costs more than the extra workgroups gain.)
 void gemv_shape(int64_t M, int64_t N, int64_t K, bool grouped, GemvDesc* d) {
     memset(d, 0, sizeof(*d));
     d->M = int32_t(M);
@@ -113,13 +111,6 @@ void gemv_shape(int64_t M, int64_t N, int64_t K, bool grouped, GemvDesc* d) {
     // M activation rows plus one zero row per chunk
     const int64_t lds_steps = std::max<int64_t>(1, kGemvLdsBytes / ((M + 1) * kSuperK));
     int64_t chunks = ceil_div(d->steps, lds_steps);
-    if (!grouped) {
-        constexpr int64_t kTargetBlocks = 1024;
-        constexpr int64_t kMinStepsPerChunk = 2;
-        const int64_t want = std::min(ceil_div(kTargetBlocks, d->groups),
-                                      ceil_div(d->steps, kMinStepsPerChunk));
-        chunks = std::max(chunks, want);
-    }
     const int64_t spc = ceil_div(d->steps, chunks);
     chunks = ceil_div(d->steps, spc);
     d->chunks = int32_t(chunks);
@@ -130,6 +121,12 @@ void gemv_shape(int64_t M, int64_t N, int64_t K, bool grouped, GemvDesc* d) {
 
 size_t gemv_partial_bytes(const GemvDesc& d) {
     return (size_t(d.M) * size_t(d.tiles) * kTileN * sizeof(int32_t) + 255) & ~size_t(255);
+}
+
+size_t gemv_single_workspace_bytes(const GemvDesc& d) {
+    if (d.chunks <= 1) return 0;
+    return gemm_slice_bytes(d.M, d.N) * size_t(d.chunks) +
+           ((size_t(d.M) * 8 + 255) & ~size_t(255));
 }
 
 size_t gemv_workspace_bytes(const GemvDesc& d) {
@@ -173,7 +170,7 @@ extern "C" size_t bt_matmul_workspace_bytes(int64_t M, int64_t N, int64_t K) {
         return bt::gemm_workspace_bytes(bt::gemm_choice(M, N, K, false, true), M, N);
     bt::GemvDesc d;
     bt::gemv_shape(M, N, K, false, &d);
-    return bt::gemv_workspace_bytes(d);
+    return bt::gemv_single_workspace_bytes(d);
 }
 
 extern "C" size_t bt_int8_matmul_workspace_bytes(int64_t M, int64_t N, int64_t K) {

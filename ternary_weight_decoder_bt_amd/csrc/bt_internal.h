@@ -67,7 +67,9 @@ struct GemvDesc {
     int32_t steps_per_chunk;
     int32_t tiles_per_wave;
     int32_t lds_row;        // bytes per activation row in LDS (steps_per_chunk*256 + 16)
-    int32_t pad_;
+    int32_t slices;         // chunks > 1: 1 = each chunk stores its partial sums in its
+                            // own M x N slice of ws and a second launch adds them (single
+                            // calls); 0 = atomics into ws, last chunk finishes (plans)
     int64_t groups;         // workgroups per chunk = ceil(tiles / (4 * tiles_per_wave))
     int64_t block_begin;    // first workgroup of this problem in a grouped launch
     int64_t blocks;         // workgroups of this problem = groups * chunks
@@ -99,11 +101,12 @@ struct PlanHeader {
     int64_t total_blocks;
 };
 
-// Work split of a GEMV (single call: split K for parallelism and for the LDS
-// slice; grouped: only for the LDS slice). Also sizes its workspace.
+// Work split of a GEMV: K is split only where the activations do not fit one
+// workgroup's LDS slice.
 void gemv_shape(int64_t M, int64_t N, int64_t K, bool grouped, GemvDesc* d);
-size_t gemv_workspace_bytes(const GemvDesc& d);
+size_t gemv_workspace_bytes(const GemvDesc& d);          // plans: atomics + counters
 size_t gemv_partial_bytes(const GemvDesc& d);
+size_t gemv_single_workspace_bytes(const GemvDesc& d);   // single calls: slices + d, row sums
 
 // GEMM shape choice (M > 16), made from the shape alone so that the host can
 // size the workspace: the persistent kernel (128 x 256 tiles), the tiled

@@ -689,9 +689,22 @@ __device__ __forceinline__ int32_t gemv_row_sum(const GemvShared& sh, int m) {
 // workspace (int32 addition is exact in any order) and the last chunk to
 // arrive reads the total, clears the workspace and finishes the tile.
 __device__ __forceinline__ void gemv_finish(const GemvDesc& d, int64_t tile, v4i c, int lane,
-                                            const GemvShared& sh) {
+                                            const GemvShared& sh, int chunk) {
     const int kq = lane >> 4;
     const int64_t n = tile * bt::kTileN + (lane & 15);
+    if (d.chunks > 1 && d.slices) {
+        // this chunk's partial sums into its own slice; a second launch adds
+        // the slices and finishes (no cross-workgroup synchronization here)
+        const int64_t slice = ((int64_t(d.M) * d.N * 4 + 255) & ~int64_t(255)) / 4;
+        if (n < d.N) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int mm = 4 * kq + i;
+                if (mm < d.M) gst<int32_t>(d.ws + chunk * slice + int64_t(mm) * d.N + n, c[i]);
+            }
+        }
+        return;
+    }
     if (d.chunks > 1) {
         const int64_t ldw = int64_t(d.tiles) * bt::kTileN;
 #pragma unroll
@@ -931,7 +944,7 @@ __device__ __forceinline__ void gemv_block(const GemvDesc& d, int64_t local_bloc
         if (t >= d.tiles) return;
         cur = gemv_consume(b, min(kB, nsteps - bb * kB), abase + bb * kB * 256, cur);
         if (bb == nb - 1) {
-            gemv_finish(d, t, cur, lane, sh);
+            gemv_finish(d, t, cur, lane, sh, chunk);
             cur = v4i{0, 0, 0, 0};
         }
     };
@@ -1856,14 +1869,38 @@ extern "C" bt_status bt_rmsnorm_quantize(const float* x, const float* g, float e
 }
 
 // Fills the split-K workspace pointers of a single-call GEMV.
+// A single call whose activations need more than one LDS slice splits K:
+// the chunks' partial sums go to slices of the workspace, and after them the
+// fused path's scales and row sums when the caller does not keep them.
 static bt_status gemv_bind_workspace(GemvDesc& d, void* workspace, size_t workspace_bytes) {
-    const size_t need = bt::gemv_workspace_bytes(d);
+    const size_t need = bt::gemv_single_workspace_bytes(d);
     if (!need) return BT_OK;
     if (!workspace || workspace_bytes < need) return BT_ERR_WORKSPACE;
     if (!bt::aligned16(workspace)) return BT_ERR_ALIGN;
+    d.slices = 1;
     d.ws = static_cast<int32_t*>(workspace);
-    d.cnt = reinterpret_cast<uint32_t*>(static_cast<char*>(workspace) + bt::gemv_partial_bytes(d));
     return BT_OK;
+}
+
+// Second launch of a split single-call GEMV: adds the chunks' slices, then
+// the rescale and epilogue (the GEMM's split-K reduction, which shares the
+// slice layout).
+static bt_status gemv_reduce(const GemvDesc& d, hipStream_t stream) {
+    GemmArgs g;
+    memset(&g, 0, sizeof(g));
+    g.xscale = d.xscale;
+    g.xsum = d.xsum;
+    g.y = d.y;
+    g.acc = d.acc;
+    g.w_scale = d.w_scale;
+    g.M = d.M;
+    g.N = d.N;
+    g.K = d.K;
+    g.epi = d.epi;
+    g.splits = d.chunks;
+    g.ws = d.ws;
+    g.ws_slice = int64_t(bt::gemm_slice_bytes(d.M, d.N) / sizeof(int32_t));
+    return launch_splitk_reduce<false>(g, stream);
 }
 
 extern "C" bt_status bt_ternary_matmul_fused(int64_t M, int64_t N, int64_t K, const float* x,
@@ -1890,10 +1927,19 @@ extern "C" bt_status bt_ternary_matmul_fused(int64_t M, int64_t N, int64_t K, co
     d.y = y;
     d.acc = acc;
     d.w_scale = w_scale;
+    if (d.chunks > 1) {
+        // the second launch needs the scales and row sums: keep them in the
+        // workspace, after the slices, when the caller does not
+        char* scratch = reinterpret_cast<char*>(d.ws) + bt::gemm_slice_bytes(M, N) * d.chunks;
+        if (!d.xscale) d.xscale = reinterpret_cast<float*>(scratch);
+        if (!d.xsum) d.xsum = reinterpret_cast<int32_t*>(scratch + 4 * M);
+    }
     (void)hipGetLastError();
     hipLaunchKernelGGL(gemv_kernel<true>, dim3(unsigned(d.blocks)), dim3(64 * bt::kGemvWaves),
                        gemv_lds_bytes(d), stream, d);
-    return launched();
+    const bt_status st2 = launched();
+    if (st2 != BT_OK || d.chunks <= 1) return st2;
+    return gemv_reduce(d, stream);
 }
 
 // Checks an epilogue against the output it is applied to and converts it.
@@ -1947,7 +1993,9 @@ static bt_status matmul_impl(int64_t M, int64_t N, int64_t K, const int8_t* xq,
         (void)hipGetLastError();
         hipLaunchKernelGGL(gemv_kernel<false>, dim3(unsigned(d.blocks)), dim3(64 * bt::kGemvWaves),
                            gemv_lds_bytes(d), stream, d);
-        return launched();
+        const bt_status lst = launched();
+        if (lst != BT_OK || d.chunks <= 1) return lst;
+        return gemv_reduce(d, stream);
     }
     GemmArgs g;
     memset(&g, 0, sizeof(g));

@@ -65,11 +65,12 @@ def test_graph_replays_match_eager(dev):
                            for o, w, c in zip(two, ws, cases)])
     fplan = bt.MatmulPlan([dict(o, wdev=w, n=c["N"], w_scale=c["w_scale"], x=x)
                            for o, w, c, x in zip(fused, ws, cases, xs)])
-    sk = synth.small_problem(21, 3, 1536, 8960)
+    sk = synth.small_problem(21, 16, 1536, 8960)
     sk_w, sk_x = _weights(sk, dev), torch.from_numpy(sk["x"]).to(dev)
     sk_q = bt.quantize_act(sk_x)
-    sk_ws = bt.new_workspace(3, 1536, 8960, dev)
-    sk_y = torch.empty((3, 1536), dtype=torch.float32, device=dev)
+    sk_ws = bt.new_workspace(16, 1536, 8960, dev)
+    assert sk_ws is not None                      # 16 rows x 8960: K is split
+    sk_y = torch.empty((16, 1536), dtype=torch.float32, device=dev)
     gm = synth.small_problem(22, 200, 2048, 1536, "t3")
     gm_w, gm_x = _weights(gm, dev), torch.from_numpy(gm["x"]).to(dev)
     gm_q = [torch.empty((200, 1536), dtype=torch.int8, device=dev),
@@ -96,6 +97,7 @@ def test_graph_replays_match_eager(dev):
             o["acc"].fill_(-1)
             o["xq"].fill_(99)
         sk_y.fill_(float("nan"))
+        sk_ws.fill_(0x5A)                         # partial slices are overwritten
         gm_y.fill_(float("nan"))
         gm_q[0].fill_(99)
 
@@ -112,4 +114,3 @@ def test_graph_replays_match_eager(dev):
         for i, (a, b) in enumerate(zip(got, eager)):
             assert torch.equal(a.view(torch.uint8) if a.dtype == torch.float32 else a,
                                b.view(torch.uint8) if b.dtype == torch.float32 else b), (rep, i)
-    assert int(sk_ws.count_nonzero()) == 0

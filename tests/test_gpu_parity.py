@@ -301,17 +301,37 @@ def test_zero_row_in_batch_gives_zero_output(dev):
         assert (y.cpu().numpy()[1] == 0).all()
 
 
-def test_deterministic_and_workspace_left_clean(dev):
+def test_split_gemv_deterministic_with_poisoned_workspace(dev):
+    """M = 16 rows of K = 8960 do not fit one LDS slice, so K is split: the
+    chunks' partial sums go to workspace slices and a second launch adds them.
+    Two calls agree bit for bit with the oracle whatever the workspace held."""
     c = synth.small_problem(6, 16, 1536, 8960)
+    ref = oracle.forward_ref(c["x"], c["w"], c["w_scale"], "f64")
     wdev = load_weights(c["w"], dev)
     xq, xs, xsum = run_quantize(c["x"], dev)
     ws = bt.new_workspace(16, 1536, 8960, dev)
     assert ws is not None
-    y1, a1 = run_matmul(xq, xs, xsum, wdev, 1536, c["w_scale"], dev, workspace=ws)
-    y2, a2 = run_matmul(xq, xs, xsum, wdev, 1536, c["w_scale"], dev, workspace=ws)
-    torch.cuda.synchronize()
-    assert torch.equal(a1, a2) and torch.equal(y1.view(torch.int32), y2.view(torch.int32))
-    assert int(ws.count_nonzero()) == 0
+    for fill in (0x00, 0x7F):
+        ws.fill_(fill)
+        y, a = run_matmul(xq, xs, xsum, wdev, 1536, c["w_scale"], dev, workspace=ws)
+        torch.cuda.synchronize()
+        assert np.array_equal(a.cpu().numpy(), ref["acc"])
+        assert np.array_equal(y.cpu().numpy(), ref["y"])
+    # the fused path splits the same way and keeps its scales in the workspace
+    for keep in (True, False):
+        ws.fill_(0x3C)
+        out = {}
+        if keep:
+            out = dict(xq=torch.empty_like(xq), xscale=torch.empty_like(xs),
+                       xsum=torch.empty_like(xsum))
+        y, a = bt.ternary_matmul_fused(to_dev(c["x"], dev), wdev, 1536, c["w_scale"],
+                                       workspace=ws, want_acc=True, **out)
+        torch.cuda.synchronize()
+        assert np.array_equal(a.cpu().numpy(), ref["acc"])
+        assert np.array_equal(y.cpu().numpy(), ref["y"])
+        if keep:
+            assert np.array_equal(out["xscale"].cpu().numpy(), ref["d"])
+            assert np.array_equal(out["xsum"].cpu().numpy(), ref["qsum"])
 
 
 # ------------------------------------------------------------------ grouped

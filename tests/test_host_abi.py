@@ -122,7 +122,11 @@ def test_sizes():
     assert bt.matmul_workspace_bytes(150, 1536, 8960) == 7 * 150 * 1536 * 4
     # 2 x 16 tiles, 64 stages of 128: min(16, 16) = 16 ranges of 4
     assert L_i8_ws(150, 2048, 8192) == 16 * 150 * 2048 * 4
-    assert bt.matmul_workspace_bytes(1, 1536, 1536) > 0       # split K on a small matrix
+    # GEMV: K is split only where M x K activations exceed one LDS slice
+    assert bt.matmul_workspace_bytes(1, 1536, 1536) == 0
+    assert bt.matmul_workspace_bytes(1, 1536, 8960) == 0
+    # 16 x 8960 int8 rows: chunks of 9 steps -> 4 chunks; slices + scales/row sums
+    assert bt.matmul_workspace_bytes(16, 1536, 8960) == 4 * 16 * 1536 * 4 + 256
 
 
 def test_device_entry_points_validate_before_launch():
@@ -195,10 +199,10 @@ def test_device_entry_points_validate_before_launch():
     assert L.bt_ternary_matmul_epilogue(*eargs(C.byref(BtEpilogue(None, None, f, 0, 0)),
                                                scale=float("nan"))) == VALUE
     # a split-K GEMV without (enough) workspace
-    need = bt.matmul_workspace_bytes(1, 1536, 1536)
-    assert L.bt_ternary_matmul(*args(N=1536, K=1536)) == WORKSPACE
-    assert L.bt_ternary_matmul(*args(N=1536, K=1536, ws=f, wsb=need - 1)) == WORKSPACE
-    assert L.bt_ternary_matmul(*args(N=1536, K=1536, ws=f + 4, wsb=need)) == ALIGN
+    need = bt.matmul_workspace_bytes(16, 1536, 8960)
+    assert L.bt_ternary_matmul(*args(M=16, N=1536, K=8960)) == WORKSPACE
+    assert L.bt_ternary_matmul(*args(M=16, N=1536, K=8960, ws=f, wsb=need - 1)) == WORKSPACE
+    assert L.bt_ternary_matmul(*args(M=16, N=1536, K=8960, ws=f + 4, wsb=need)) == ALIGN
     # fused quantize + GEMV: x, wdev, y required; q outputs optional; M <= 16
     fa = lambda **kw: [kw.get("M", 1), kw.get("N", 16), kw.get("K", 128), kw.get("x", f),
                        kw.get("w", f), kw.get("scale", 0.5), kw.get("y", f), None,
@@ -207,7 +211,7 @@ def test_device_entry_points_validate_before_launch():
     assert L.bt_ternary_matmul_fused(*fa(M=17)) == SHAPE
     assert L.bt_ternary_matmul_fused(*fa(xq=f + 1)) == ALIGN
     assert L.bt_ternary_matmul_fused(*fa(scale=float("inf"))) == VALUE
-    assert L.bt_ternary_matmul_fused(*fa(N=1536, K=1536)) == WORKSPACE
+    assert L.bt_ternary_matmul_fused(*fa(M=16, N=1536, K=8960)) == WORKSPACE
 
 
 def test_plan_building_on_host():
