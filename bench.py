@@ -361,6 +361,175 @@ class LongPrefill:
         return bool(ok)
 
 
+# ------------------------------------------------- single-projection calls
+
+def _rotating_copies(torch, wdev, min_bytes: int = 600 << 20):
+    """Enough copies of one repacked weight tensor that cycling through them
+    streams more than the 256 MB on-package cache holds."""
+    n = max(2, -(-min_bytes // wdev.numel()))
+    return [wdev] + [wdev.clone() for _ in range(n - 1)]
+
+
+def _graph_us_per_call(torch, calls, reps: int = 5):
+    """Median time per call of the `calls` (a list of closures, one launch sequence
+    each), captured as one HIP graph and replayed `reps` times."""
+    g = capture_graph(torch, lambda: [c() for c in calls])
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    times = []
+    for _ in range(reps + 1):
+        e0.record()
+        g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        times.append(e0.elapsed_time(e1) / len(calls))
+    del g
+    return float(np.median(times[1:])) * 1e3
+
+
+def run_single_projections(torch, bt, dev):
+    """Single calls outside the grouped decode step:
+    - one GEMV, M=1, K=N=1536 (x ~ N(0,1) seed 0, weights seed 1, scale 0.02), fused and
+      two-launch;
+    - the batched-decode remainder sweep: gate_up (1536->17920) and down (8960->1536) at
+      M in {1,2,3,4,5,7,8,16}, GEMV on quantized activations;
+    - one-layer prefill, M=512, the four projection shapes (quantize + GEMM each).
+    Weights rotate over copies so they stream from HBM; calls replay from a HIP graph.
+    Parity of each first output is checked against the oracle."""
+    import oracle
+    out = {}
+
+    def close(got, want):
+        nz = want != 0
+        return bool((got[~nz] == 0).all() and
+                    (np.abs(got[nz] - want[nz]) <= 1e-6 * np.abs(want[nz])).all())
+
+    # ---- one GEMV, M=1, 1536 x 1536
+    c = synth.config0()
+    ref = oracle.forward_ref(c["x"], c["w"], c["w_scale"], "f64")
+    packed = torch.from_numpy(bt.pack_ternary(c["w"]).reshape(-1)).to(dev)
+    ws_ = _rotating_copies(torch, bt.repack_ternary(packed, c["N"], c["K"]))
+    x = torch.from_numpy(c["x"]).to(dev)
+    y = torch.empty((1, c["N"]), dtype=torch.float32, device=dev)
+    xq = torch.empty((1, c["K"]), dtype=torch.int8, device=dev)
+    xs = torch.empty(1, dtype=torch.float32, device=dev)
+    xsum = torch.empty(1, dtype=torch.int32, device=dev)
+    wb = bt.packed_bytes(c["N"], c["K"])
+    ok = True
+    bt.ternary_matmul_fused(x, ws_[0], c["N"], c["w_scale"], y=y, xq=xq, xscale=xs, xsum=xsum)
+    torch.cuda.synchronize()
+    ok &= close(y.cpu().numpy(), ref["y"]) and np.array_equal(xq.cpu().numpy(), ref["q"])
+    y.fill_(float("nan"))
+    bt.quantize_act(x, xq, xs, xsum)
+    bt.ternary_matmul(xq, xs, xsum, ws_[0], c["N"], c["w_scale"], y=y)
+    torch.cuda.synchronize()
+    ok &= close(y.cpu().numpy(), ref["y"])
+    fused_us = _graph_us_per_call(torch, [
+        (lambda w=w: bt.ternary_matmul_fused(x, w, c["N"], c["w_scale"], y=y)) for w in ws_])
+    gemv_us = _graph_us_per_call(torch, [
+        (lambda w=w: bt.ternary_matmul(xq, xs, xsum, w, c["N"], c["w_scale"], y=y)) for w in ws_])
+    two_us = _graph_us_per_call(torch, [
+        (lambda w=w: (bt.quantize_act(x, xq, xs, xsum),
+                      bt.ternary_matmul(xq, xs, xsum, w, c["N"], c["w_scale"], y=y)))
+        for w in ws_])
+    out["gemv_1536x1536_M1"] = {
+        "workload": "one ternary GEMV, M=1, K=N=1536, weights streamed from HBM "
+                    f"({len(ws_)} rotating copies), calls replayed from a HIP graph",
+        "weight_bytes": wb, "parity_ok": bool(ok),
+        "fused_us": round(fused_us, 3), "two_launch_us": round(two_us, 3),
+        "gemv_only_us": round(gemv_us, 3),
+        "gemv_only_weight_gb_per_s": round(wb / (gemv_us * 1e-6) / 1e9, 1),
+        "fused_weight_gb_per_s": round(wb / (fused_us * 1e-6) / 1e9, 1)}
+    log(f"single GEMV 1536x1536: fused {fused_us:.2f} us, two-launch {two_us:.2f} us, "
+        f"GEMV alone {gemv_us:.2f} us ({wb / (gemv_us * 1e-6) / 1e9:.0f} GB/s); parity {ok}")
+    del ws_, packed
+
+    # ---- batched-decode remainder sweep
+    sweep = {}
+    for name in ("gate_up", "down"):
+        c1 = synth.decode_remainder_problem(name, 1)
+        n, k = c1["N"], c1["K"]
+        packed = torch.from_numpy(bt.pack_ternary(c1["w"]).reshape(-1)).to(dev)
+        ws_ = _rotating_copies(torch, bt.repack_ternary(packed, n, k))
+        wb = bt.packed_bytes(n, k)
+        row = {}
+        for m in synth.REMAINDER_MS:
+            cm = synth.decode_remainder_problem(name, m)
+            x = torch.from_numpy(cm["x"]).to(dev)
+            q = bt.quantize_act(x)
+            y = torch.empty((m, n), dtype=torch.float32, device=dev)
+            wsp = bt.new_workspace(m, n, k, dev)
+            bt.ternary_matmul(*q, ws_[0], n, cm["w_scale"], y=y, workspace=wsp)
+            torch.cuda.synchronize()
+            cols = np.array([0, 1, n // 2, n - 1])
+            want = oracle.dequant_ref(oracle.matmul_ref(q[0].cpu().numpy(), cm["w"][cols], "f64"),
+                                      q[1].cpu().numpy(), cm["w_scale"])
+            good = close(y.cpu().numpy()[:, cols], want)
+            us = _graph_us_per_call(torch, [
+                (lambda w=w: bt.ternary_matmul(*q, w, n, cm["w_scale"], y=y, workspace=wsp))
+                for w in ws_])
+            alg = wb + m * k + 4 * m * n + 8 * m
+            row[f"M{m}"] = {"us": round(us, 3), "gb_per_s": round(alg / (us * 1e-6) / 1e9, 1),
+                            "pct_of_hbm_peak": round(100 * alg / (us * 1e-6) / 1e9 / HBM_PEAK_GBS,
+                                                     2),
+                            "parity_ok": good}
+        sweep[name] = row
+        log(f"remainder sweep {name}: " + ", ".join(
+            f"M={m} {row[f'M{m}']['us']:.1f}us/{row[f'M{m}']['gb_per_s']:.0f}GB/s"
+            for m in synth.REMAINDER_MS))
+        del ws_, packed
+    out["remainder_sweep"] = {
+        "workload": "gate_up 1536->17920 and down 8960->1536 at M in {1,2,3,4,5,7,8,16}, "
+                    "GEMV on quantized activations, weights streamed from HBM, calls replayed "
+                    "from a HIP graph; GB/s = (weights + activations + output) / time",
+        "shapes": sweep}
+
+    # ---- one-layer prefill, M=512
+    pre, tot_ops, tot_us, gemm_us_tot = {}, 0, 0.0, 0.0
+    for proj in range(len(synth.PROJECTIONS)):
+        cp = synth.prefill_problem(proj)
+        m, n, k = cp["M"], cp["N"], cp["K"]
+        packed = torch.from_numpy(bt.pack_ternary(cp["w"]).reshape(-1)).to(dev)
+        wdev = bt.repack_ternary(packed, n, k)
+        x = torch.from_numpy(cp["x"]).to(dev)
+        q = bt.quantize_act(x)
+        y = torch.empty((m, n), dtype=torch.float32, device=dev)
+        wsp = bt.new_workspace(m, n, k, dev)
+        bt.ternary_matmul(*q, wdev, n, cp["w_scale"], y=y, workspace=wsp)
+        torch.cuda.synchronize()
+        rows = np.array([0, 1, m // 2, m - 1])
+        qn = q[0].cpu().numpy()
+        want = oracle.dequant_ref(oracle.matmul_ref(qn[rows], cp["w"], "f64"),
+                                  q[1].cpu().numpy()[rows], cp["w_scale"])
+        good = close(y.cpu().numpy()[rows], want)
+        reps = 20
+        gemm_us = _graph_us_per_call(torch, [
+            (lambda: bt.ternary_matmul(*q, wdev, n, cp["w_scale"], y=y, workspace=wsp))] * reps)
+        both_us = _graph_us_per_call(torch, [
+            (lambda: (bt.quantize_act(x, *q),
+                      bt.ternary_matmul(*q, wdev, n, cp["w_scale"], y=y, workspace=wsp)))] * reps)
+        ops = 2 * m * n * k
+        tot_ops += ops
+        tot_us += both_us
+        gemm_us_tot += gemm_us
+        pre[cp["name"]] = {"M": m, "N": n, "K": k, "gemm_us": round(gemm_us, 2),
+                           "gemm_tops": round(ops / (gemm_us * 1e-6) / 1e12, 1),
+                           "quantize_plus_gemm_us": round(both_us, 2), "parity_ok": good}
+        del packed, wdev, x, q, y, wsp
+    out["prefill_M512_one_layer"] = {
+        "workload": "one layer's four projections at M=512 (weights P(-1,0,1) = 0.3/0.4/0.3, "
+                    "x ~ N(0,1)), quantize + GEMM each, replayed from a HIP graph "
+                    "(L2-warm: each call reuses one weight tensor)",
+        "shapes": pre, "ms_per_layer": round(tot_us * 1e-3, 4),
+        "tops": round(tot_ops / (tot_us * 1e-6) / 1e12, 1),
+        "gemm_only_tops": round(tot_ops / (gemm_us_tot * 1e-6) / 1e12, 1),
+        "pct_of_int8_peak": round(100 * tot_ops / (tot_us * 1e-6) / 1e12 / I8_PEAK_TOPS, 2)}
+    log(f"prefill M=512 one layer: {tot_us:.1f} us ({tot_ops / (tot_us * 1e-6) / 1e12:.0f} TOPS), "
+        f"GEMMs {gemm_us_tot:.1f} us; " + ", ".join(
+            f"{k_} {v['gemm_tops']:.0f}" for k_, v in pre.items()))
+    torch.cuda.empty_cache()
+    return out
+
+
 # ------------------------------------------------------------ CPU baseline
 
 # The tokenizer's ConvNeXt stages ("VibeVoice-ASR-BitNet Technical Report",
@@ -461,6 +630,7 @@ def main():
     ap.add_argument("--trials", type=int, default=5)
     ap.add_argument("--layers", type=int, default=synth.N_LAYERS)
     ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--no-singles", action="store_true")
     ap.add_argument("--prefill-steps", type=int, default=5)
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -634,6 +804,10 @@ def main():
         "ms_per_stack_one_launch_per_tensor_graph": round(rp["per_tensor_graph"], 4)}
     del ds
     torch.cuda.empty_cache()
+
+    # ---- single-projection calls (one GEMV, remainder sweep, one-layer prefill)
+    if not args.no_singles:
+        out["single_projections"] = run_single_projections(torch, bt, dev)
 
     # ---- long prefill (secondary)
     if not args.no_prefill:

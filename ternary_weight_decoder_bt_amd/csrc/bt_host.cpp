@@ -107,7 +107,6 @@ void gemv_shape(int64_t M, int64_t N, int64_t K, bool grouped, GemvDesc* d) {
     d->tiles = int32_t(ceil_div(N, kTileN));
     d->steps = int32_t(ceil_div(K, kSuperK));
     d->tiles_per_wave = grouped ? kGemvGroupedTilesPerWave : 1;
-    d->groups = ceil_div(d->tiles, int64_t(kGemvWaves) * d->tiles_per_wave);
     // M activation rows plus one zero row per chunk
     const int64_t lds_steps = std::max<int64_t>(1, kGemvLdsBytes / ((M + 1) * kSuperK));
     int64_t chunks = ceil_div(d->steps, lds_steps);
@@ -116,6 +115,17 @@ void gemv_shape(int64_t M, int64_t N, int64_t K, bool grouped, GemvDesc* d) {
     d->chunks = int32_t(chunks);
     d->steps_per_chunk = int32_t(spc);
     d->lds_row = int32_t(spc * kSuperK + 16);
+    // A single call with few tiles leaves most compute units idle and each wave
+    // streaming a long K range: split every tile's K range over 2 or 4 waves of
+    // its workgroup instead (partial sums meet in LDS), while each wave keeps
+    // at least one 256-element step.
+    d->waves_per_tile = 1;
+    if (!grouped) {
+        while (d->waves_per_tile < kGemvWaves && d->tiles * d->waves_per_tile < kGemvFillWaves &&
+               spc >= 2 * d->waves_per_tile)
+            d->waves_per_tile *= 2;
+    }
+    d->groups = ceil_div(d->tiles, int64_t(kGemvWaves / d->waves_per_tile) * d->tiles_per_wave);
     d->blocks = d->groups * chunks;
 }
 

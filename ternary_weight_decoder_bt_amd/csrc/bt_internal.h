@@ -35,6 +35,7 @@ inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 #endif
 constexpr int kGemvBatch = BT_GEMV_BATCH;
 constexpr int kGemvLdsBytes = 40960;
+constexpr int kGemvFillWaves = 1024;   // waves that keep every compute unit streaming
 constexpr int kGemvGroupedTilesPerWave = BT_GEMV_TILES_PER_WAVE;
 
 // Epilogue on the fp32 output (all optional): bias add, ReLU, per-output
@@ -70,6 +71,8 @@ struct GemvDesc {
     int32_t slices;         // chunks > 1: 1 = each chunk stores its partial sums in its
                             // own M x N slice of ws and a second launch adds them (single
                             // calls); 0 = atomics into ws, last chunk finishes (plans)
+    int32_t waves_per_tile; // 1, 2 or 4: a tile's K range within a chunk is split over
+                            // this many waves of one workgroup (tiles_per_wave is then 1)
     int64_t groups;         // workgroups per chunk = ceil(tiles / (4 * tiles_per_wave))
     int64_t block_begin;    // first workgroup of this problem in a grouped launch
     int64_t blocks;         // workgroups of this problem = groups * chunks

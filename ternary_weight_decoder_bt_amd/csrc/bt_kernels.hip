@@ -866,7 +866,7 @@ __device__ __forceinline__ void gemv_quantize_rows(const GemvDesc& d, const Fuse
     if (writer && d.xsum && tid < d.M) gst<int32_t>(d.xsum + tid, gemv_row_sum(sh, tid));
 }
 
-template <bool kFused>
+template <bool kFused, bool kWaveSplit>
 __device__ __forceinline__ void gemv_block(const GemvDesc& d, int64_t local_block, int8_t* lds,
                                            GemvShared& sh) {
     const int tid = threadIdx.x;
@@ -877,9 +877,19 @@ __device__ __forceinline__ void gemv_block(const GemvDesc& d, int64_t local_bloc
     const int s0 = chunk * d.steps_per_chunk;
     const int s1 = min(s0 + d.steps_per_chunk, d.steps);
     const int nsteps = s1 - s0;
-    const int nb = (nsteps + kB - 1) / kB;
+    // With waves_per_tile > 1, wave `wave` takes sub-range `sub` of its tile's
+    // steps [s0, s1) (possibly empty: its loads are then clamped repeats of a
+    // valid step, never consumed).
+    const int wpt = kWaveSplit ? d.waves_per_tile : 1;
+    const int sub = wave & (wpt - 1);
+    const int sps_w = (nsteps + wpt - 1) / wpt;
+    const int ws0 = min(s0 + sub * sps_w, s1);
+    const int ws1 = min(ws0 + sps_w, s1);
+    const int nsteps_w = ws1 - ws0;
+    const int nb = max(1, (nsteps_w + kB - 1) / kB);
     const int total = d.tiles_per_wave * nb;
-    const int64_t tile0 = g * (int64_t(bt::kGemvWaves) * d.tiles_per_wave) + wave;
+    const int tile_stride = bt::kGemvWaves / wpt;
+    const int64_t tile0 = g * (int64_t(tile_stride) * d.tiles_per_wave) + wave / wpt;
     const int64_t tile_bytes = int64_t(d.steps) * 1024;
 
     // Items are (tile, batch of kB steps). Two items are loaded back to back
@@ -889,8 +899,8 @@ __device__ __forceinline__ void gemv_block(const GemvDesc& d, int64_t local_bloc
     auto issue = [&](GemvBatch& b, int idx) {
         const int r = idx / nb;
         const int bb = idx - r * nb;
-        const int64_t t = min(tile0 + int64_t(bt::kGemvWaves) * r, int64_t(d.tiles) - 1);
-        gemv_issue(b, d.w + t * tile_bytes, s0 + bb * kB, s1 - 1, lane);
+        const int64_t t = min(tile0 + int64_t(tile_stride) * r, int64_t(d.tiles) - 1);
+        gemv_issue(b, d.w + t * tile_bytes, ws0 + bb * kB, ws1 - 1, lane);
     };
 
     // The first weight batches go out before the activations are staged, so
@@ -940,10 +950,11 @@ __device__ __forceinline__ void gemv_block(const GemvDesc& d, int64_t local_bloc
     auto consume = [&](const GemvBatch& b, int idx) {
         const int r = idx / nb;
         const int bb = idx - r * nb;
-        const int64_t t = tile0 + int64_t(bt::kGemvWaves) * r;
+        const int64_t t = tile0 + int64_t(tile_stride) * r;
         if (t >= d.tiles) return;
-        cur = gemv_consume(b, min(kB, nsteps - bb * kB), abase + bb * kB * 256, cur);
-        if (bb == nb - 1) {
+        cur = gemv_consume(b, min(kB, nsteps_w - bb * kB), abase + (ws0 - s0 + bb * kB) * 256,
+                           cur);
+        if (bb == nb - 1 && wpt == 1) {
             gemv_finish(d, t, cur, lane, sh, chunk);
             cur = v4i{0, 0, 0, 0};
         }
@@ -962,13 +973,26 @@ __device__ __forceinline__ void gemv_block(const GemvDesc& d, int64_t local_bloc
         __builtin_amdgcn_sched_barrier(0);
         if (idx + 1 < total) consume(b1, idx + 1);
     }
+    if (kWaveSplit && wpt > 1) {
+        // the sub-range sums of each tile meet in LDS (over the activations,
+        // which every wave has finished reading), then its first wave finishes
+        __syncthreads();
+        v4i* part = reinterpret_cast<v4i*>(lds);
+        part[wave * 64 + lane] = cur;
+        __syncthreads();
+        if (sub == 0 && tile0 < d.tiles) {
+            for (int s = 1; s < wpt; ++s) cur += part[(wave + s) * 64 + lane];
+            gemv_finish(d, tile0, cur, lane, sh, chunk);
+        }
+    }
 }
 
+// Single calls: waves_per_tile may split a tile's K range over the workgroup.
 template <bool kFused>
-__global__ __launch_bounds__(64 * bt::kGemvWaves) __attribute__((amdgpu_waves_per_eu(5))) void gemv_kernel(GemvDesc d) {
+__global__ __launch_bounds__(64 * bt::kGemvWaves) __attribute__((amdgpu_waves_per_eu(4))) void gemv_kernel(GemvDesc d) {
     extern __shared__ __attribute__((aligned(16))) int8_t gemv_lds[];
     __shared__ GemvShared sh;
-    gemv_block<kFused>(d, blockIdx.x, gemv_lds, sh);
+    gemv_block<kFused, true>(d, blockIdx.x, gemv_lds, sh);
 }
 
 template <bool kFused>
@@ -983,10 +1007,14 @@ __global__ __launch_bounds__(64 * bt::kGemvWaves) __attribute__((amdgpu_waves_pe
         if (descs[mid].block_begin <= b) lo = mid; else hi = mid - 1;
     }
     const GemvDesc d = descs[lo];
-    gemv_block<kFused>(d, b - d.block_begin, gemv_lds, sh);
+    gemv_block<kFused, false>(d, b - d.block_begin, gemv_lds, sh);
 }
 
-size_t gemv_lds_bytes(const GemvDesc& d) { return size_t(d.M + 1) * size_t(d.lds_row); }
+size_t gemv_lds_bytes(const GemvDesc& d) {
+    const size_t rows = size_t(d.M + 1) * size_t(d.lds_row);
+    // waves_per_tile > 1 reuses the activation space for the waves' partial sums
+    return d.waves_per_tile > 1 ? std::max(rows, size_t(bt::kGemvWaves) * 64 * 16) : rows;
+}
 
 // -------------------------------------------------------------------- GEMM
 //

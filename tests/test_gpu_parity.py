@@ -208,6 +208,24 @@ def test_gemv_split_k_and_edges(dev, m, n, k):
     check_full(synth.small_problem(3, m, n, k, "outlier"), dev)
 
 
+# Single calls with few 16-row tiles split each tile's K range over 2 or 4 waves
+# of a workgroup: 5 steps over 4 waves leaves one wave empty, 1152 and 640 end
+# in a 128-wide step, 625 tiles take 2 waves each, and 16 x 8960 also splits K
+# across workgroups.
+@pytest.mark.parametrize("m,n,k", [(1, 40, 1280), (3, 1000, 1152), (2, 33, 768),
+                                   (16, 10000, 640), (16, 1536, 8960), (5, 17, 1280)])
+@pytest.mark.parametrize("fused", [False, True])
+def test_gemv_wave_split_k(dev, m, n, k, fused):
+    c = synth.small_problem(31, m, n, k, "outlier")
+    if fused:
+        ref = oracle.forward_ref(c["x"], c["w"], c["w_scale"], "f64")
+        y, acc, _ = run_fused(c, dev)
+        assert_exact("acc", acc.cpu().numpy(), ref["acc"])
+        assert_rel("y", y.cpu().numpy(), ref["y"])
+    else:
+        check_full(c, dev)
+
+
 _REMAINDER_W = {}
 
 
