@@ -29,3 +29,4 @@ from .fused_ref import (  # noqa: F401
     epilogue_ref,
 )
 from .i8s_ref import I8_KMAX, i8s_matmul_ref, i8s_forward_ref  # noqa: F401,E402
+from .bitnet_ref import absmean_ref, ternarize_ref, ternarize_pack_ref  # noqa: F401,E402
