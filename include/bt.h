@@ -79,6 +79,33 @@ bt_status bt_pack_ternary(const int8_t* w, int64_t N, int64_t K, uint8_t* packed
 bt_status bt_unpack_ternary(const uint8_t* packed, int64_t N, int64_t K, int8_t* w);
 
 /* ---------------------------------------------------------------------------
+ * Offline ternarization (device, once per weight tensor, before packing).
+ *
+ * Technical report section 2.2.2: the weights are quantized to ternary
+ * following the BitNet approach of its reference [11] ("The era of 1-bit
+ * LLMs"): the absmean quantizer. Over the whole N x K tensor, with
+ * S = sum |w| taken in fp64 (any summation order):
+ *   gamma = fl32(S / (N*K)) (the division in fp64); delta = fl32(gamma + eps);
+ *   t = w / delta (IEEE fp32 division);
+ *   w~ = clamp(round_half_away_from_zero(t), -1, 1), i.e. +-1 where |t| >= 1/2.
+ * The codes are written in the canonical packed format above (as
+ * bt_pack_ternary would pack w~) and gamma, the per-tensor scale that
+ * multiplies them back, to *scale. delta == 0 (an all-zero tensor with
+ * eps == 0) gives all-zero weights and gamma = 0.
+ *
+ * w: device fp32 N x K, finite (not checked). packed: device,
+ * bt_packed_bytes(N,K) bytes, written. scale: device fp32 [1], written.
+ * eps: finite and >= 0 (BT_ERR_VALUE otherwise). workspace: device, at least
+ * bt_ternarize_workspace_bytes(N,K) bytes (per-workgroup partial sums; its
+ * contents on entry do not matter). None of the four buffers may overlap
+ * another (BT_ERR_VALUE). Two launches on `stream`; deterministic.
+ * ------------------------------------------------------------------------- */
+size_t bt_ternarize_workspace_bytes(int64_t N, int64_t K);
+bt_status bt_ternarize(const float* w, int64_t N, int64_t K, float eps, uint8_t* packed,
+                       float* scale, void* workspace, size_t workspace_bytes,
+                       hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
  * Device repack (once per weight tensor, at load time).
  *
  * Permutes the canonical bytes into the kernels' fragment order: 16-row tiles,

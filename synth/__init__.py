@@ -18,6 +18,8 @@ from .generators import (  # noqa: F401
     projection_rng,
     small_problem,
     device_student_t3,
+    fp_weights,
+    device_fp_weights,
     CFG_LONG,
     REMAINDER_MS,
 )

@@ -13,8 +13,8 @@ The single-GEMV workload uses ``default_rng(0)`` for activations and
 ``default_rng(1)`` for weights.
 
 Nothing here packs, quantizes or multiplies: the weights come out as int8
-values in {-1, 0, +1} (N rows of K, K contiguous) and the activations as fp32
-(M rows of K).
+values in {-1, 0, +1} (N rows of K, K contiguous), or as fp32 before
+ternarization, and the activations as fp32 (M rows of K).
 """
 
 from __future__ import annotations
@@ -34,7 +34,7 @@ PROJECTIONS = (
 STREAM_W, STREAM_X, STREAM_SCALE, STREAM_OUTLIER = 0, 1, 2, 3
 
 # Workload ids (the first SeedSequence word).
-CFG_SINGLE, CFG_DECODE, CFG_REMAINDER, CFG_PREFILL, CFG_LONG = 0, 1, 2, 3, 4
+CFG_SINGLE, CFG_DECODE, CFG_REMAINDER, CFG_PREFILL, CFG_LONG, CFG_FPW = 0, 1, 2, 3, 4, 5
 
 REMAINDER_MS = (1, 2, 3, 4, 5, 7, 8, 16)
 
@@ -139,6 +139,38 @@ def device_student_t3(m: int, k: int, cfg: int, layer: int, proj: int, device):
     for _ in range(3):
         chi += torch.randn((m, k), generator=g, device=device, dtype=torch.float32).square()
     return z / torch.sqrt(chi / 3)
+
+
+def fp_weights(seed: int, n: int, k: int, dist: str = "normal") -> np.ndarray:
+    """fp32 (n, k) full-precision weights before ternarization: N(0, s^2) with a
+    seeded s ~ U(0.01, 0.05) ("normal"), the same with 0.1% of entries x10
+    ("outlier"), or s * Student-t with 3 degrees of freedom ("t3")."""
+    rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence([CFG_FPW, seed, n, k])))
+    s = np.float32(rng.uniform(0.01, 0.05))
+    if dist == "normal":
+        w = rng.standard_normal((n, k), dtype=np.float32)
+    elif dist == "outlier":
+        w = rng.standard_normal((n, k), dtype=np.float32)
+        w[rng.random((n, k)) < 0.001] *= np.float32(10.0)
+    elif dist == "t3":
+        w = rng.standard_t(3, size=(n, k)).astype(np.float32)
+    else:
+        raise ValueError(dist)
+    return w * s
+
+
+def device_fp_weights(layer: int, proj: int, device):
+    """fp32 (N, K) weights of one decoder projection, N(0, s^2) with s ~ U(0.01, 0.05),
+    drawn on the GPU with torch (the stack's 5.2 GB would take long on the host)."""
+    import torch
+    _, k, n = PROJECTIONS[proj]
+    rng = projection_rng(CFG_FPW, layer, proj, STREAM_SCALE)
+    s = float(np.float32(rng.uniform(0.01, 0.05)))
+    seed = int(np.random.SeedSequence([CFG_FPW, layer, proj, STREAM_W]).generate_state(
+        1, np.uint64)[0] & np.uint64(2 ** 63 - 1))
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    return torch.randn((n, k), generator=g, device=device, dtype=torch.float32) * s
 
 
 def small_problem(seed: int, m: int, n: int, k: int, dist: str = "normal",

@@ -26,6 +26,8 @@ from .ops import (  # noqa: F401
     quantize_act,
     repack_int8,
     repack_ternary,
+    ternarize,
+    ternarize_workspace_bytes,
     repacked_bytes,
     rmsnorm_quantize,
     ternary_matmul,

@@ -24,6 +24,8 @@ SIGNATURES = {
     "bt_packed_bytes": (_sz, [_i64, _i64]),
     "bt_pack_ternary": (C.c_int, [_p, _i64, _i64, _p]),
     "bt_unpack_ternary": (C.c_int, [_p, _i64, _i64, _p]),
+    "bt_ternarize_workspace_bytes": (_sz, [_i64, _i64]),
+    "bt_ternarize": (C.c_int, [_p, _i64, _i64, _f, _p, _p, _p, _sz, _p]),
     "bt_repacked_bytes": (_sz, [_i64, _i64]),
     "bt_repack_ternary": (C.c_int, [_p, _i64, _i64, _p, _p]),
     "bt_quantize_act": (C.c_int, [_p, _i64, _i64, _p, _p, _p, _p]),

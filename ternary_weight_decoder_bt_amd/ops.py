@@ -89,6 +89,36 @@ def unpack_ternary(packed: np.ndarray, k: int) -> np.ndarray:
 
 # ------------------------------------------------------------------ device
 
+def ternarize_workspace_bytes(n: int, k: int) -> int:
+    return int(lib().bt_ternarize_workspace_bytes(n, k))
+
+
+def ternarize(w, eps: float = 0.0, packed=None, scale=None, workspace=None, stream=None):
+    """fp32 device W (N, K) -> (uint8 canonical packed bytes (N*K/4,), fp32 scale (1,))
+    via bt_ternarize (absmean ternarization, codes packed as bt_pack_ternary does)."""
+    torch = _torch()
+    _dev(w, torch.float32, None, "w")
+    if w.dim() != 2:
+        raise ValueError("w must be (N, K)")
+    n, k = w.shape
+    nbytes = packed_bytes(n, k)
+    if nbytes == 0:
+        raise ValueError(f"invalid weight shape N={n}, K={k} (K must be a multiple of 128)")
+    if packed is None:
+        packed = torch.empty(nbytes, dtype=torch.uint8, device=w.device)
+    if scale is None:
+        scale = torch.empty(1, dtype=torch.float32, device=w.device)
+    _dev(packed, torch.uint8, (nbytes,), "packed")
+    _dev(scale, torch.float32, (1,), "scale")
+    need = ternarize_workspace_bytes(n, k)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=w.device)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    check(lib().bt_ternarize(_ptr(w), n, k, float(eps), _ptr(packed), _ptr(scale),
+                             _ptr(workspace), ws_bytes, _stream(stream)), "bt_ternarize")
+    return packed, scale
+
+
 def repack_ternary(packed_dev, n: int, k: int, out=None, stream=None):
     """Canonical bytes on the device -> the kernels' tile layout (bt_repack_ternary)."""
     torch = _torch()

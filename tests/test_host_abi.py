@@ -136,6 +136,27 @@ def test_device_entry_points_validate_before_launch():
     assert L.bt_repack_ternary(None, 16, 128, f, None) == NULL
     assert L.bt_repack_ternary(f, 16, 100, f, None) == SHAPE
     assert L.bt_repack_ternary(f + 4, 16, 128, f, None) == ALIGN
+    # offline ternarization: w, packed, scale, workspace must be distinct buffers
+    G = 1 << 30
+    tz = lambda **kw: [kw.get("w", f), kw.get("N", 16), kw.get("K", 128), kw.get("eps", 0.0),
+                       kw.get("p", f + G), kw.get("s", f + 2 * G), kw.get("ws", f + 3 * G),
+                       kw.get("wsb", 256), None]
+    assert L.bt_ternarize_workspace_bytes(16, 128) == 256
+    assert L.bt_ternarize_workspace_bytes(1536, 1536) == 288 * 8 + 0  # 288 partials
+    assert L.bt_ternarize_workspace_bytes(17920, 1536) == 1024 * 8
+    assert L.bt_ternarize_workspace_bytes(16, 100) == 0
+    assert L.bt_ternarize(*tz(w=None)) == NULL
+    assert L.bt_ternarize(*tz(s=None)) == NULL
+    assert L.bt_ternarize(*tz(K=100)) == SHAPE
+    assert L.bt_ternarize(*tz(N=0)) == SHAPE
+    assert L.bt_ternarize(*tz(eps=-1.0)) == VALUE
+    assert L.bt_ternarize(*tz(eps=float("nan"))) == VALUE
+    assert L.bt_ternarize(*tz(p=f + G + 4)) == ALIGN
+    assert L.bt_ternarize(*tz(ws=None)) == WORKSPACE
+    assert L.bt_ternarize(*tz(wsb=255)) == WORKSPACE
+    assert L.bt_ternarize(*tz(p=f + 16 * 128)) == VALUE       # packed inside w (16x128 fp32)
+    assert L.bt_ternarize(*tz(s=f + G + 256)) == VALUE        # scale inside packed (512 B)
+    assert L.bt_ternarize(*tz(ws=f + G + 496)) == VALUE       # workspace overlaps packed
     # quantize
     assert L.bt_quantize_act(None, 1, 128, f, f, f, None) == NULL
     assert L.bt_quantize_act(f, 0, 128, f, f, f, None) == SHAPE
