@@ -1047,6 +1047,7 @@ struct GemmArgs {
     float w_scale;
     int32_t M, N, K, tiles, steps;   // steps: 256-wide stages (Kp / 256)
     int32_t m_tiles, n_tiles, per_xcd;
+    int32_t group_m;        // token-row bands per group of the tile order (tile_coords)
     EpiArgs epi;
     int32_t splits, sps;    // K ranges per tile and stages per range (1, all: no split)
     int32_t* ws;            // split K: one M x N int32 slice of partial sums per range
@@ -1054,6 +1055,21 @@ struct GemmArgs {
 };
 
 constexpr int kXcds = 8;
+
+// Output tile (mt, nt) of linear tile index L. Tiles are ordered in groups of
+// group_m token-row bands; inside a group they run down the bands first. The
+// tiles that run at the same time on one XCD (consecutive indices) then form
+// a compact block whose activation rows and weight tiles both stay in that
+// XCD's L2, instead of one band's row that sweeps every weight tile through it.
+__device__ __forceinline__ void tile_coords(const GemmArgs& g, int L, int& mt, int& nt) {
+    const int per_group = g.group_m * g.n_tiles;
+    const int grp = L / per_group;
+    const int first_m = grp * g.group_m;
+    const int gm = min(g.m_tiles - first_m, g.group_m);
+    const int r = L - grp * per_group;
+    mt = first_m + r % gm;
+    nt = r / gm;
+}
 
 __device__ __forceinline__ void lds_dma16(__amdgpu_buffer_rsrc_t r, int8_t* lds_wave_base,
                                           uint32_t voff, uint32_t soff) {
@@ -1172,8 +1188,8 @@ void gemm_kernel(GemmArgs g) {
     if (unit >= g.m_tiles * g.n_tiles * g.splits) return;
     const int tile_id = unit / g.splits;
     const int split = unit - tile_id * g.splits;
-    const int mt = tile_id / g.n_tiles;
-    const int nt = tile_id - mt * g.n_tiles;
+    int mt, nt;
+    tile_coords(g, tile_id, mt, nt);
 
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -1466,8 +1482,8 @@ void gemm_persistent_kernel(GemmArgs g) {
     // Buffers of a tile: its token rows and this wave's weight tiles. Rows
     // past M and weight tiles past N read as zero (range check).
     auto tile_rsrc = [&](int tile_id, __amdgpu_buffer_rsrc_t& ra, __amdgpu_buffer_rsrc_t& rw) {
-        const int mt = tile_id / g.n_tiles;
-        const int nt = tile_id - mt * g.n_tiles;
+        int mt, nt;
+        tile_coords(g, tile_id, mt, nt);
         const int64_t m0 = int64_t(mt) * BM;
         const int t0 = min(nt * (BN / bt::kTileN) + wave * TW, g.tiles - 1);
         ra = make_rsrc(g.xq + m0 * g.K, uint32_t(min(int64_t(BM), int64_t(g.M) - m0)) * uint32_t(g.K));
@@ -1551,8 +1567,8 @@ void gemm_persistent_kernel(GemmArgs g) {
         const int tile_id = first + k * per_wg;
         const bool has_next = k + 1 < count;
         tile_rsrc(has_next ? tile_id + per_wg : tile_id, ra_nxt, rw_nxt);
-        const int mt = tile_id / g.n_tiles;
-        const int nt = tile_id - mt * g.n_tiles;
+        int mt, nt;
+        tile_coords(g, tile_id, mt, nt);
         const int64_t m0 = int64_t(mt) * BM;
         const int n0 = nt * BN;
 
@@ -1661,6 +1677,18 @@ void gemm_persistent_kernel(GemmArgs g) {
 #endif
 
 
+#ifndef BT_GEMM_GROUPED
+#define BT_GEMM_GROUPED 1
+#endif
+
+// Token-row bands per tile group: as many as one XCD's share of the tiles
+// spans, so that share is one compact block of the output.
+int32_t gemm_group_m(int32_t m_tiles, int32_t n_tiles, int64_t tiles_per_xcd) {
+    if (!BT_GEMM_GROUPED) return 1;
+    const int64_t gm = bt::ceil_div(tiles_per_xcd, n_tiles);
+    return int32_t(std::max<int64_t>(1, std::min<int64_t>(m_tiles, gm)));
+}
+
 // Shape dispatch of the GEMM: the default tile, or a 128 x 128 tile (waves of
 // 64 x 64) when the default leaves fewer than two workgroups per compute unit
 // (e.g. 4096 x 1536 outputs).
@@ -1676,6 +1704,7 @@ bt_status launch_gemm(GemmArgs g, hipStream_t stream) {
     }
     const int64_t total = int64_t(g.m_tiles) * g.n_tiles * g.splits;
     g.per_xcd = int32_t(bt::ceil_div(total, kXcds));
+    g.group_m = gemm_group_m(g.m_tiles, g.n_tiles, bt::ceil_div(g.per_xcd, g.splits));
     const int64_t grid = int64_t(g.per_xcd) * kXcds;
     if (grid > (int64_t(1) << 31) - 1) return BT_ERR_SHAPE;
     (void)hipGetLastError();
@@ -1724,6 +1753,7 @@ bt_status launch_gemm_persistent(GemmArgs g, hipStream_t stream) {
     const int64_t total = int64_t(g.m_tiles) * g.n_tiles;
     if (total > (int64_t(1) << 31) - 1) return BT_ERR_SHAPE;
     g.per_xcd = int32_t(bt::ceil_div(total, kXcds));
+    g.group_m = gemm_group_m(g.m_tiles, g.n_tiles, g.per_xcd);
     // one workgroup per resident slot, a multiple of the XCD count, and no
     // more than there are tiles in an XCD's band
     const int64_t slots = int64_t(device_cus()) * BT_GEMM_P_WGS_PER_CU / kXcds;
