@@ -38,7 +38,11 @@ import synth  # noqa: E402
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 I8_PEAK_TOPS = 5000.0          # MI355X dense int8 MFMA, TOPS
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemv_decode_step_traffic.json")
-KERNEL_SRC = os.path.join(ROOT, "ternary_weight_decoder_bt_amd", "csrc", "bt_kernels.hip")
+GEMM_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_long_prefill_traffic.json")
+CSRC = os.path.join(ROOT, "ternary_weight_decoder_bt_amd", "csrc")
+# the sources a kernel family's counters depend on (its kernels, shared helpers, host dispatch)
+DECODE_SOURCES = ("bt_kernels.hip", "bt_device.h", "bt_internal.h", "bt_host.cpp")
+GEMM_SOURCES = ("bt_gemm.hip", "bt_device.h", "bt_internal.h", "bt_host.cpp")
 
 METRIC = "ternary GEMV HBM GB/s (% of peak) + decode-step tokens/s; prefill int8 TOPS"
 
@@ -47,22 +51,35 @@ def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
-def kernel_source_hash() -> str:
-    with open(KERNEL_SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+def source_hash(names) -> str:
+    h = hashlib.sha256()
+    for name in names:
+        with open(os.path.join(CSRC, name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
-def measured_traffic(kernel: str):
-    """HBM bytes per launch of `kernel` from the committed counter summary, or
-    None when the kernels changed since the counters were taken."""
+def _traffic_file(path, sources):
+    """A committed counter summary, or None when its sources changed since the
+    counters were taken."""
     try:
-        with open(TRAFFIC_FILE) as f:
+        with open(path) as f:
             t = json.load(f)
     except (OSError, ValueError):
         return None
-    if t.get("kernel_source_sha256_16") != kernel_source_hash():
-        return None
-    return t.get("kernels", {}).get(kernel, {}).get("hbm_bytes_per_launch")
+    return t if t.get("kernel_source_sha256_16") == source_hash(sources) else None
+
+
+def measured_traffic(kernel: str):
+    """HBM bytes per launch of the decode kernel `kernel` (or None)."""
+    t = _traffic_file(TRAFFIC_FILE, DECODE_SOURCES)
+    return None if t is None else t.get("kernels", {}).get(kernel, {}).get("hbm_bytes_per_launch")
+
+
+def measured_gemm_traffic():
+    """HBM bytes per long-prefill stack of GEMM launches (or None)."""
+    t = _traffic_file(GEMM_TRAFFIC_FILE, GEMM_SOURCES)
+    return None if t is None else t.get("hbm_bytes_per_stack")
 
 
 def capture_graph(torch, fn):
@@ -231,6 +248,7 @@ class LongPrefill:
         self.torch, self.bt = torch, bt
         self.probs = []
         self.ops = 0
+        self.alg_bytes = 0
         t0 = time.time()
         i = 0
         for layer in range(layers):
@@ -251,6 +269,8 @@ class LongPrefill:
                      "ws": bt.new_workspace(m, n, k, dev)}
                 self.probs.append(p)
                 self.ops += 2 * m * n * k
+                # int8 activations + 2-bit weights + fp32 output + scales and row sums
+                self.alg_bytes += m * k + n * k // 4 + 4 * m * n + 8 * m
         torch.cuda.synchronize()
         self.m = m
         log(f"long prefill ready: {len(self.probs)} projections, M={m}, "
@@ -934,7 +954,10 @@ def main():
             "roofline": {"bound": "mfma",
                          "kernel": "gemm_persistent_kernel (gate_up) + gemm_kernel (qkv, o, down)",
                          "achieved": round(gemm_tops, 2), "peak": I8_PEAK_TOPS,
-                         "unit": "TFLOP/s", "frac": round(gemm_tops / I8_PEAK_TOPS, 4)},
+                         "unit": "TFLOP/s", "frac": round(gemm_tops / I8_PEAK_TOPS, 4),
+                         "traffic": measured_gemm_traffic(),
+                         "traffic_unit": "HBM bytes per stack of 112 GEMM launches",
+                         "algorithmic_bytes_per_stack": lp.alg_bytes},
         }
         del lp
         torch.cuda.empty_cache()

@@ -14,7 +14,7 @@ LIB_NAME = "libbt.so"
 LIB_PATH = os.path.join(PKG_DIR, LIB_NAME)
 ARCH = "gfx950"
 
-SOURCES = ("bt_host.cpp", "bt_kernels.hip", "bt_ternarize.hip")
+SOURCES = ("bt_host.cpp", "bt_kernels.hip", "bt_gemm.hip", "bt_ternarize.hip")
 
 # -ffp-contract=off: the quantizer's rounding decision must see the rounded
 #   fp32 product x * (127 / a), never a fused multiply-add of it.

@@ -50,6 +50,24 @@ struct EpiArgs {
 
 // One GEMV problem as the kernel sees it. The single-matrix call passes it by
 // value; a grouped plan stores an array of them in device memory.
+// Arguments of the prefill GEMM launches (bt_gemm.hip).
+struct GemmArgs {
+    const int8_t* xq;
+    const float* xscale;
+    const int32_t* xsum;
+    const uint8_t* w;
+    float* y;
+    int32_t* acc;
+    float w_scale;
+    int32_t M, N, K, tiles, steps;   // steps: 256-wide stages (Kp / 256)
+    int32_t m_tiles, n_tiles, per_xcd;
+    int32_t group_m;        // token-row bands per group of the tile order (tile_coords)
+    EpiArgs epi;
+    int32_t splits, sps;    // K ranges per tile and stages per range (1, all: no split)
+    int32_t* ws;            // split K: one M x N int32 slice of partial sums per range
+    int64_t ws_slice;       // int32 elements from one slice to the next
+};
+
 struct GemvDesc {
     const float* x;         // fused quantization: fp32 activations (else null)
     int8_t* xq;             // unfused: input. fused: optional output (written once)
@@ -130,5 +148,12 @@ inline size_t gemm_slice_bytes(int64_t M, int64_t N) {
 }
 
 inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// bt_gemm.hip: the prefill GEMM for M > 16 (shape dispatch, split K and its
+// reduction launch), and that reduction alone for a split single-call GEMV
+// (same slice layout).
+bt_status gemm_dispatch(GemmArgs g, bool int8_weights, void* workspace, size_t workspace_bytes,
+                        hipStream_t stream);
+bt_status gemm_reduce_slices(const GemmArgs& g, hipStream_t stream);
 
 }  // namespace bt
