@@ -812,8 +812,9 @@ bt_status dispatch_gemm(GemmArgs g, bool int8_weights, void* workspace, size_t w
     }
     bt_status st;
     if (int8_weights) {
-        st = c.kind == 2 ? launch_gemm<64, 64, 2, 2, 128, 2, true>(g, stream)
-                         : launch_gemm<128, 64, 1, 4, 128, 2, true>(g, stream);
+        st = c.kind == 3   ? launch_gemm<32, 32, 2, 2, 128, 2, true>(g, stream)
+             : c.kind == 2 ? launch_gemm<64, 64, 2, 2, 128, 2, true>(g, stream)
+                           : launch_gemm<128, 64, 1, 4, 128, 2, true>(g, stream);
         if (st == BT_OK && g.splits > 1) st = launch_splitk_reduce<true>(g, stream);
         return st;
     }
@@ -821,8 +822,9 @@ bt_status dispatch_gemm(GemmArgs g, bool int8_weights, void* workspace, size_t w
     if (c.kind == 0)
         return launch_gemm_persistent<BT_GEMM_P_WA, 64, BT_GEMM_P_NW, 128, BT_GEMM_P_NS>(g, stream);
 #endif
-    st = c.kind == 2 ? launch_gemm<64, 64, 2, 2, 256, 2>(g, stream)
-                     : launch_gemm<128, 64, 1, 4, 128, 2>(g, stream);
+    st = c.kind == 3   ? launch_gemm<32, 32, 2, 2, 256, 2>(g, stream)
+         : c.kind == 2 ? launch_gemm<64, 64, 2, 2, 256, 2>(g, stream)
+                       : launch_gemm<128, 64, 1, 4, 128, 2>(g, stream);
     if (st == BT_OK && g.splits > 1) st = launch_splitk_reduce<false>(g, stream);
     return st;
 }

@@ -154,6 +154,12 @@ GemmChoice gemm_choice(int64_t M, int64_t N, int64_t K, bool int8_weights, bool 
     }
     c.kind = 2;
     c.tiles = ceil_div(M, 128) * ceil_div(N, 128);
+    // fewer 128 x 128 tiles than compute units (e.g. one layer at M = 512): 64 x 64
+    // tiles put four times as many workgroups to work (measured faster there)
+    if (c.tiles < kGemmSmallTiles) {
+        c.kind = 3;
+        c.tiles = ceil_div(M, 64) * ceil_div(N, 64);
+    }
     const int64_t nst = ceil_div(K, int8_weights ? 128 : 256);
     // split only below one tile per two compute units: every range stores an
     // M x N int32 slice and a second launch reads them all back, which costs

@@ -135,9 +135,10 @@ size_t gemv_single_workspace_bytes(const GemvDesc& d);   // single calls: slices
 // `splits` ranges of `sps` stages when there are too few tiles to fill the
 // device (partial sums meet in an int32 workspace).
 constexpr int kGemmSlots = 512;   // resident workgroups the split choice aims at
+constexpr int kGemmSmallTiles = 256;   // below this many 128 x 128 tiles, use 64 x 64 tiles
 struct GemmChoice {
-    int kind;        // 0 persistent, 1 tiled 128 x 256, 2 tiled 128 x 128
-    int splits;      // K ranges (kind 2), else 1
+    int kind;        // 0 persistent, 1 tiled 128 x 256, 2 tiled 128 x 128, 3 tiled 64 x 64
+    int splits;      // K ranges (kinds 2, 3), else 1
     int sps;         // stages per range (stage = 256-wide K for ternary, 128 for int8)
     int64_t tiles;   // output tiles of the chosen kind
 };

@@ -118,10 +118,11 @@ def test_sizes():
     assert bt.matmul_workspace_bytes(4096, 17920, 1536) == 0
     assert bt.matmul_workspace_bytes(4096, 1536, 8960) == 0   # 384 tiles: enough
     assert bt.matmul_workspace_bytes(17, 1536, 1536) == 0     # too short a K to split
-    # 2 x 12 tiles, 35 stages: min(ceil(512/24), 35//4) = 8 ranges of 5 -> 7 ranges
+    # 3 x 24 tiles of 64 x 64, 35 stages: min(ceil(512/72), 35//4) = 8 ranges of 5 -> 7 ranges
     assert bt.matmul_workspace_bytes(150, 1536, 8960) == 7 * 150 * 1536 * 4
-    # 2 x 16 tiles, 64 stages of 128: min(16, 16) = 16 ranges of 4
-    assert L_i8_ws(150, 2048, 8192) == 16 * 150 * 2048 * 4
+    # 64 x 64 tiles below 256 tiles of 128 x 128: 3 x 32 tiles, 64 stages of 128:
+    # min(ceil(512/96), 16) = 6 ranges of 11 -> 6 ranges
+    assert L_i8_ws(150, 2048, 8192) == 6 * 150 * 2048 * 4
     # GEMV: K is split only where M x K activations exceed one LDS slice
     assert bt.matmul_workspace_bytes(1, 1536, 1536) == 0
     assert bt.matmul_workspace_bytes(1, 1536, 8960) == 0
