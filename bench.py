@@ -711,6 +711,7 @@ def main():
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-singles", action="store_true")
     ap.add_argument("--no-ternarize", action="store_true")
+    ap.add_argument("--no-i8s", action="store_true")
     ap.add_argument("--prefill-steps", type=int, default=5)
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -963,7 +964,7 @@ def main():
         torch.cuda.empty_cache()
 
     # ---- I8_S (the tokenizer's INT8 GEMMs), secondary
-    if not args.no_prefill:
+    if not args.no_i8s:
         out["i8s"] = run_i8s_tokenizer_ffn(torch, bt, dev)
 
     if not args.no_cpu_baseline:

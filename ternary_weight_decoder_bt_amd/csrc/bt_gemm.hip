@@ -796,6 +796,136 @@ bt_status launch_splitk_reduce(const GemmArgs& g, hipStream_t stream) {
 
 // Runs the kernel gemm_choice picked for the shape; with split K, binds the
 // workspace (partial sums, then one counter per tile).
+// I8_S product for a small weight matrix and many tokens (the tokenizer's early
+// stages: N x K int8 of at most 64 KB, K <= 512, M up to hundreds of thousands).
+// Every workgroup first copies the whole repacked matrix, [tile][64-wide step]
+// in 1 KB pieces, into LDS. Each wave then streams blocks of 16 tokens: one
+// 16-byte activation fragment per lane and 64-wide step, prefetched a block
+// ahead, meets the 16-row weight tiles held in LDS, eight tiles per pass, and
+// the fp32 rows go out at once. Per token these shapes read K + 4 bytes and
+// write 4 N, so the output bytes bound them; the generic GEMM's 128-token
+// tiles with one K stage each spend their time in start-up and epilogue.
+template <int NK>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NK >= 8 ? 3 : 4))) void i8_stream_kernel(GemmArgs g) {
+    extern __shared__ __attribute__((aligned(16))) int8_t wl[];
+    constexpr uint32_t kNowhere = 0x80000000u;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int tiles = g.tiles;
+    // after the weights: each wave's 4 KB for turning 16 x 64 output blocks into rows
+    float* const ep = reinterpret_cast<float*>(wl + int64_t(tiles) * NK * 1024) + (tid >> 6) * 1024;
+    const int64_t steps64 = int64_t(g.steps) * 4;   // 64-wide steps per repacked tile
+    for (int i = tid; i < tiles * NK * 64; i += 256) {
+        const int tk = i >> 6;
+        const int t = tk / NK;
+        const int kk = tk - t * NK;
+        lds_st<v4u>(wl + int64_t(i) * 16,
+                    gld<v4u>(g.w + (int64_t(t) * steps64 + kk) * 1024 + (i & 63) * 16));
+    }
+    __syncthreads();
+
+    const int64_t nblocks = (int64_t(g.M) + 15) / 16;
+    const int64_t stride = int64_t(gridDim.x) * 4;
+    int64_t b = int64_t(blockIdx.x) * 4 + (tid >> 6);
+    // rows past M and K chunks past K read as zero (M * K < 2^31 is checked on the host)
+    const __amdgpu_buffer_rsrc_t ar = make_rsrc(g.xq, uint32_t(int64_t(g.M) * g.K));
+    const int ml = lane & 15;
+    const uint32_t kq = 16u * uint32_t(lane >> 4);
+    auto load_a = [&](v4u (&a)[NK], int64_t blk) {
+        const int64_t m = blk * 16 + ml;
+        const uint32_t base = m < g.M ? uint32_t(m) * uint32_t(g.K) : kNowhere;
+#pragma unroll
+        for (int kk = 0; kk < NK; ++kk) {
+            const uint32_t k = 64u * kk + kq;
+            a[kk] = buf_ld16u(ar, k < uint32_t(g.K) ? base + k : kNowhere, 0);
+        }
+    };
+    auto load_s = [&](int64_t blk) {
+        return gld<float>(g.xscale + min(blk * 16 + ml, int64_t(g.M) - 1));
+    };
+    v4u a_cur[NK], a_nxt[NK];
+    load_a(a_cur, b);
+    float s_cur = load_s(b);
+    const bool vec = (g.N & 3) == 0;
+    for (; b < nblocks; b += stride) {
+        load_a(a_nxt, b + stride);
+        const float s_nxt = load_s(b + stride);
+        const int64_t m = b * 16 + ml;
+        const float rs = s_cur * g.w_scale;
+        const bool full_rows = (b + 1) * 16 <= int64_t(g.M) && vec && !g.acc;
+        for (int p = 0; p < tiles; p += 4) {
+            v4i acc[4];
+#pragma unroll
+            for (int t = 0; t < 4; ++t) acc[t] = v4i{0, 0, 0, 0};
+#pragma unroll
+            for (int kk = 0; kk < NK; ++kk) {
+                const v4i af = __builtin_bit_cast(v4i, a_cur[kk]);
+#pragma unroll
+                for (int t = 0; t < 4; ++t)
+                    if (p + t < tiles)
+                        acc[t] = mfma16x16x64(
+                            lds_ld<v4i>(wl + (int64_t(p + t) * NK + kk) * 1024 + lane * 16), af,
+                            acc[t]);
+            }
+            // acc[t][r] = C[n = 16(p+t) + 4(l/16) + r][token m]
+            if (full_rows && 16 * (p + 4) <= g.N) {
+                // a whole 16 x 64 block: rows go out 256 contiguous bytes at a time
+                const EpiCols ec = epi_cols_load(g.epi, 16 * p, lane);
+                v4f v[4];
+#pragma unroll
+                for (int t = 0; t < 4; ++t)
+                    v[t] = v4f{float(acc[t].x) * rs, float(acc[t].y) * rs, float(acc[t].z) * rs,
+                               float(acc[t].w) * rs};
+                gemm_store_block_rows(v, ep, g.y, g.N, b * 16, 16 * p, lane, g.epi, ec);
+                continue;
+            }
+            if (m < g.M) {
+                float* yrow = g.y + m * g.N;
+                int32_t* arow = g.acc ? g.acc + m * g.N : nullptr;
+#pragma unroll
+                for (int t = 0; t < 4; ++t) {
+                    if (p + t >= tiles) continue;
+                    const int n = 16 * (p + t) + 4 * (lane >> 4);
+                    const v4i a = acc[t];
+                    v4f yv = {float(a.x) * rs, float(a.y) * rs, float(a.z) * rs, float(a.w) * rs};
+                    if (vec && n + 3 < g.N) {
+                        yv = epi_col4(g.epi, yv, n);
+                        if (g.epi.res) yv = gld<v4f>(g.epi.res + m * g.N + n) + yv;
+                        __builtin_nontemporal_store(yv, (BT_GLOBAL v4f*)(yrow + n));
+                        if (arow) __builtin_nontemporal_store(a, (BT_GLOBAL v4i*)(arow + n));
+                    } else {
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) {
+                            if (n + r < g.N) {
+                                float v = epi_col(g.epi, yv[r], n + r);
+                                if (g.epi.res) v = g.epi.res[m * g.N + n + r] + v;
+                                gst<float>(yrow + n + r, v);
+                                if (arow) gst<int32_t>(arow + n + r, a[r]);
+                            }
+                        }
+                    }
+                }
+            }
+        }
+#pragma unroll
+        for (int kk = 0; kk < NK; ++kk) a_cur[kk] = a_nxt[kk];
+        s_cur = s_nxt;
+    }
+}
+
+template <int NK>
+bt_status launch_i8_stream(GemmArgs g, hipStream_t stream) {
+    g.tiles = int32_t(bt::ceil_div(g.N, bt::kTileN));
+    const size_t lds = size_t(g.tiles) * NK * 1024 + 4 * 4096;
+    const int64_t nblocks = bt::ceil_div(g.M, 16);
+    const int64_t per_cu = std::max<int64_t>(1, std::min<int64_t>(6, int64_t(163840 / lds)));
+    const int64_t wgs = std::max<int64_t>(
+        1, std::min<int64_t>(bt::ceil_div(nblocks, 4), int64_t(device_cus()) * per_cu));
+    (void)hipGetLastError();
+    hipLaunchKernelGGL(i8_stream_kernel<NK>, dim3(unsigned(wgs)), dim3(256), lds, stream, g);
+    return hipGetLastError() == hipSuccess ? BT_OK : BT_ERR_DEVICE;
+}
+
 bt_status dispatch_gemm(GemmArgs g, bool int8_weights, void* workspace, size_t workspace_bytes,
                         hipStream_t stream) {
     const bt::GemmChoice c =
@@ -811,6 +941,13 @@ bt_status dispatch_gemm(GemmArgs g, bool int8_weights, void* workspace, size_t w
         g.ws_slice = int64_t(bt::gemm_slice_bytes(g.M, g.N) / sizeof(int32_t));
     }
     bt_status st;
+    if (int8_weights && c.kind == 4) {
+        const int nk = bt::i8_stream_steps(g.K);
+        return nk == 1 ? launch_i8_stream<1>(g, stream)
+             : nk == 2 ? launch_i8_stream<2>(g, stream)
+             : nk == 4 ? launch_i8_stream<4>(g, stream)
+                       : launch_i8_stream<8>(g, stream);
+    }
     if (int8_weights) {
         st = c.kind == 3   ? launch_gemm<32, 32, 2, 2, 128, 2, true>(g, stream)
              : c.kind == 2 ? launch_gemm<64, 64, 2, 2, 128, 2, true>(g, stream)

@@ -146,6 +146,13 @@ size_t gemv_workspace_bytes(const GemvDesc& d) {
 
 GemmChoice gemm_choice(int64_t M, int64_t N, int64_t K, bool int8_weights, bool persistent_ok) {
     GemmChoice c{1, 1, 0, 0};
+    // int8 weights of at most 64 KB with K <= 512: held whole in LDS, tokens streamed
+    if (int8_weights && K <= 512 && ceil_div(N, kTileN) * i8_stream_steps(K) <= 64 &&
+        M * K < (int64_t(1) << 31)) {
+        c.kind = 4;
+        c.tiles = ceil_div(M, 16);
+        return c;
+    }
     const int64_t wide = ceil_div(M, 128) * ceil_div(N, 256);
     if (wide >= kGemmSlots) {
         c.kind = persistent_ok && !int8_weights ? 0 : 1;

@@ -136,8 +136,15 @@ size_t gemv_single_workspace_bytes(const GemvDesc& d);   // single calls: slices
 // device (partial sums meet in an int32 workspace).
 constexpr int kGemmSlots = 512;   // resident workgroups the split choice aims at
 constexpr int kGemmSmallTiles = 256;   // below this many 128 x 128 tiles, use 64 x 64 tiles
+// 64-wide K steps the small-matrix I8_S kernel holds per weight tile: ceil(K/64)
+// rounded up to a power of two (1, 2, 4 or 8).
+inline int i8_stream_steps(int64_t K) {
+    const int64_t s = (K + 63) / 64;
+    return s <= 1 ? 1 : s <= 2 ? 2 : s <= 4 ? 4 : 8;
+}
 struct GemmChoice {
-    int kind;        // 0 persistent, 1 tiled 128 x 256, 2 tiled 128 x 128, 3 tiled 64 x 64
+    int kind;        // 0 persistent, 1 tiled 128 x 256, 2 tiled 128 x 128, 3 tiled 64 x 64,
+                     // 4 small int8 weight matrix held in LDS (i8_stream_kernel)
     int splits;      // K ranges (kinds 2, 3), else 1
     int sps;         // stages per range (stage = 256-wide K for ternary, 128 for int8)
     int64_t tiles;   // output tiles of the chosen kind

@@ -54,6 +54,7 @@ def run(x, w8, s, dev, **epi):
 
 
 @pytest.mark.parametrize("m,n,k", [(1000, 128, 32), (700, 32, 128), (300, 256, 64),
+                                   (33333, 128, 32), (20001, 64, 256), (1, 16, 32),
                                    (4096, 512, 128), (2000, 128, 512), (150, 8192, 2048),
                                    (150, 2048, 8192), (37, 130, 96), (5, 16, 32),
                                    (1200, 4096, 1024)])
@@ -75,7 +76,10 @@ def test_i8s_extreme_accumulator(dev):
     assert (acc[:, :16] == 127 * 128 * k).all() and (acc[:, 16:] == -127 * 127 * k).all()
 
 
-@pytest.mark.parametrize("m,n,k", [(6000, 2048, 512), (1200, 1024, 4096), (37, 130, 96)])
+# (4099, 512, 128), (2000, 128, 512), (37, 130, 96): weight matrices of at most 64 KB
+# with K <= 512, which the small-matrix kernel holds in LDS (N = 130: scalar stores)
+@pytest.mark.parametrize("m,n,k", [(6000, 2048, 512), (1200, 1024, 4096), (37, 130, 96),
+                                   (4099, 512, 128), (2000, 128, 512), (3001, 32, 32)])
 def test_i8s_fused_tokenizer_epilogues(dev, m, n, k):
     """mul_mat_add_relu (FFN up: bias + ReLU) and add_scaled (FFN down: layer
     scale + residual), the tokenizer's fused operators, on the I8_S product."""

@@ -123,6 +123,8 @@ def test_sizes():
     # 64 x 64 tiles below 256 tiles of 128 x 128: 3 x 32 tiles, 64 stages of 128:
     # min(ceil(512/96), 16) = 6 ranges of 11 -> 6 ranges
     assert L_i8_ws(150, 2048, 8192) == 6 * 150 * 2048 * 4
+    # int8 weights of at most 64 KB with K <= 512 are held in LDS: never split
+    assert L_i8_ws(480000, 128, 32) == 0 and L_i8_ws(30, 512, 128) == 0
     # GEMV: K is split only where M x K activations exceed one LDS slice
     assert bt.matmul_workspace_bytes(1, 1536, 1536) == 0
     assert bt.matmul_workspace_bytes(1, 1536, 8960) == 0
