@@ -806,7 +806,7 @@ bt_status launch_splitk_reduce(const GemmArgs& g, hipStream_t stream) {
 // write 4 N, so the output bytes bound them; the generic GEMM's 128-token
 // tiles with one K stage each spend their time in start-up and epilogue.
 template <int NK>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NK >= 8 ? 3 : 4))) void i8_stream_kernel(GemmArgs g) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NK >= 8 ? 2 : 4))) void i8_stream_kernel(GemmArgs g) {
     extern __shared__ __attribute__((aligned(16))) int8_t wl[];
     constexpr uint32_t kNowhere = 0x80000000u;
     const int tid = threadIdx.x;
