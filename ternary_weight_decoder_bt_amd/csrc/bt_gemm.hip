@@ -154,12 +154,24 @@ void gemm_kernel(GemmArgs g) {
     static_assert(WA % 16 == 0 && WW % 16 == 0, "wave tile");
     static_assert(NS >= 2 && (NS - 2) * kLoads < 64, "pipeline depth");
     static_assert(kDmaPerWave * 64 * NW == BM * CPR, "A stage must split evenly over waves");
-    __shared__ __attribute__((aligned(16))) int8_t As[NS * kStage];
+    // One LDS array per pipeline stage: the copy that fills one stage and the
+    // fragment reads of another then touch different objects, which lets the
+    // compiler see that a read need not wait for every copy still in flight
+    // (with one array it waits for all of them before each stage's reads).
+    static_assert(NS <= 4, "at most four stage buffers");
+    __shared__ __attribute__((aligned(16))) int8_t As0[kStage];
+    __shared__ __attribute__((aligned(16))) int8_t As1[kStage];
+    __shared__ __attribute__((aligned(16))) int8_t As2[NS > 2 ? kStage : 16];
+    __shared__ __attribute__((aligned(16))) int8_t As3[NS > 3 ? kStage : 16];
+    auto stage_buf = [&](int buf) -> int8_t* {
+        return buf == 0 ? As0 : buf == 1 ? As1 : buf == 2 ? As2 : As3;
+    };
     // After the main loop the stage buffers are idle (a barrier makes sure):
-    // the row-wise epilogue's blocks live in them.
+    // the row-wise epilogue's blocks live in the first one.
     constexpr bool kRowStores = WW == 64;   // row-wise epilogue through LDS
-    float* const Ep = reinterpret_cast<float*>(As);
-    static_assert(NS * kStage >= NW * 16 * 64 * 4, "epilogue blocks fit the stage buffers");
+    float* const Ep = reinterpret_cast<float*>(As0);
+    static_assert(!kRowStores || kStage >= NW * 16 * 64 * 4,
+                  "epilogue blocks fit the first stage buffer");
 
     // Swizzled LDS slot of logical chunk c of row r: the 16 rows an MFMA
     // fragment read serves at once land in 16 distinct 4-bank groups.
@@ -255,7 +267,7 @@ void gemm_kernel(GemmArgs g) {
         for (int j = 0; j < kDmaPerWave; ++j) {
             const uint32_t voff = (avoff[j & 3] + uint32_t(RPC * j) * uint32_t(g.K)) | pad |
                                   (ccol[j & 3] >= left ? kNowhere : 0u);
-            lds_dma16(arsrc, As + buf * kStage + (wave * kDmaPerWave + j) * 1024, voff, kcol);
+            lds_dma16(arsrc, stage_buf(buf) + (wave * kDmaPerWave + j) * 1024, voff, kcol);
         }
     };
 
@@ -269,7 +281,7 @@ void gemm_kernel(GemmArgs g) {
         for (int t = 0; t < TW; ++t) acc[i][t] = v4i{0, 0, 0, 0};
 
     // fragment reads: row (wm*WA + 16i + lane%16), logical chunk 4kk + lane/16
-    const int8_t* afrag = As + (wm * WA + (lane & 15)) * KS;
+    const int afrag = (wm * WA + (lane & 15)) * KS;
     int aslot[NK];
 #pragma unroll
     for (int kk = 0; kk < NK; ++kk) aslot[kk] = slot_of(lane & 15, 4 * kk + (lane >> 4)) * 16;
@@ -289,7 +301,7 @@ void gemm_kernel(GemmArgs g) {
         load_a(buf, sb + ls, pad);
     };
     auto consume = [&](int buf, const BVec (&bc)[TW]) {
-        const int8_t* abuf = afrag + buf * kStage;
+        const int8_t* abuf = stage_buf(buf) + afrag;
 #pragma unroll
         for (int kk = 0; kk < NK; ++kk) {
             v4i af[TA];
@@ -440,7 +452,18 @@ void gemm_persistent_kernel(GemmArgs g) {
     static_assert(WA % 16 == 0 && WW % 16 == 0, "wave tile");
     static_assert(NS >= 2 && (NS - 2) * kLoads < 64, "pipeline depth");
     static_assert(kDmaPerWave * 64 * NW == BM * CPR, "A stage must split evenly over waves");
-    __shared__ __attribute__((aligned(16))) int8_t As[NS * kStage];
+    // One LDS array per pipeline stage: the copy that fills one stage and the
+    // fragment reads of another then touch different objects, which lets the
+    // compiler see that a read need not wait for every copy still in flight
+    // (with one array it waits for all of them before each stage's reads).
+    static_assert(NS <= 4, "at most four stage buffers");
+    __shared__ __attribute__((aligned(16))) int8_t As0[kStage];
+    __shared__ __attribute__((aligned(16))) int8_t As1[kStage];
+    __shared__ __attribute__((aligned(16))) int8_t As2[NS > 2 ? kStage : 16];
+    __shared__ __attribute__((aligned(16))) int8_t As3[NS > 3 ? kStage : 16];
+    auto stage_buf = [&](int buf) -> int8_t* {
+        return buf == 0 ? As0 : buf == 1 ? As1 : buf == 2 ? As2 : As3;
+    };
     constexpr bool kRowStores = WW == 64;   // row-wise epilogue through LDS
     __shared__ __attribute__((aligned(16))) float Ep[kRowStores ? NW * 16 * 64 : 4];
 
@@ -510,7 +533,7 @@ void gemm_persistent_kernel(GemmArgs g) {
         for (int j = 0; j < kDmaPerWave; ++j) {
             const uint32_t voff = (avoff[j & 3] + uint32_t(RPC * j) * uint32_t(g.K)) | pad |
                                   (ahigh[j & 3] & tail);
-            lds_dma16(ra, As + buf * kStage + (wave * kDmaPerWave + j) * 1024, voff, kcol);
+            lds_dma16(ra, stage_buf(buf) + (wave * kDmaPerWave + j) * 1024, voff, kcol);
         }
     };
 
@@ -519,12 +542,12 @@ void gemm_persistent_kernel(GemmArgs g) {
     for (int i = 0; i < TA; ++i)
 #pragma unroll
         for (int t = 0; t < TW; ++t) acc[i][t] = v4i{0, 0, 0, 0};
-    const int8_t* afrag = As + (lane & 15) * KS;
+    const int afrag = (lane & 15) * KS;
     int aslot[NK];
 #pragma unroll
     for (int kk = 0; kk < NK; ++kk) aslot[kk] = slot_of(lane & 15, 4 * kk + (lane >> 4)) * 16;
     auto consume = [&](int buf, const BVec (&bc)[TW]) {
-        const int8_t* abuf = afrag + buf * kStage;
+        const int8_t* abuf = stage_buf(buf) + afrag;
 #pragma unroll
         for (int kk = 0; kk < NK; ++kk) {
             v4i af[TA];
