@@ -1008,6 +1008,7 @@ bt_status dispatch_gemm(GemmArgs g, bool int8_weights, void* workspace, size_t w
         return launch_gemm_persistent<BT_GEMM_P_WA, 64, BT_GEMM_P_NW, 128, BT_GEMM_P_NS>(g, stream);
 #endif
     st = c.kind == 3   ? launch_gemm<32, 32, 2, 2, 256, 2>(g, stream)
+         : c.kind == 5 ? launch_gemm<64, 48, 2, 2, 256, 2>(g, stream)
          : c.kind == 2 ? launch_gemm<64, 64, 2, 2, 256, 2>(g, stream)
                        : launch_gemm<128, 64, 1, 4, 128, 2>(g, stream);
     if (st == BT_OK && g.splits > 1) st = launch_splitk_reduce<false>(g, stream);

@@ -161,6 +161,16 @@ GemmChoice gemm_choice(int64_t M, int64_t N, int64_t K, bool int8_weights, bool 
     }
     c.kind = 2;
     c.tiles = ceil_div(M, 128) * ceil_div(N, 128);
+    // 128 x 96 tiles when they fill the resident workgroup slots in whole rounds
+    // clearly better (N = 1536 at M = 4096: 512 tiles instead of 384)
+    if (!int8_weights && c.tiles >= kGemmSmallTiles) {
+        const int64_t t96 = ceil_div(M, 128) * ceil_div(N, 96);
+        auto fill = [](int64_t t) { return double(t) / double(ceil_div(t, kGemmSlots) * kGemmSlots); };
+        if (fill(t96) > fill(c.tiles) + 0.05) {
+            c.kind = 5;
+            c.tiles = t96;
+        }
+    }
     // fewer 128 x 128 tiles than compute units (e.g. one layer at M = 512): 64 x 64
     // tiles put four times as many workgroups to work (measured faster there)
     if (c.tiles < kGemmSmallTiles) {

@@ -144,7 +144,8 @@ inline int i8_stream_steps(int64_t K) {
 }
 struct GemmChoice {
     int kind;        // 0 persistent, 1 tiled 128 x 256, 2 tiled 128 x 128, 3 tiled 64 x 64,
-                     // 4 small int8 weight matrix held in LDS (i8_stream_kernel)
+                     // 4 small int8 weight matrix held in LDS (i8_stream_kernel),
+                     // 5 tiled 128 x 96
     int splits;      // K ranges (kinds 2, 3), else 1
     int sps;         // stages per range (stage = 256-wide K for ternary, 128 for int8)
     int64_t tiles;   // output tiles of the chosen kind

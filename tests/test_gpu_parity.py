@@ -250,7 +250,9 @@ def test_gemm_shapes(dev, m, n, k):
 # workgroup, pipeline crossing tile boundaries), with ragged M, N a multiple
 # of 4 but not of the tile, N not a multiple of 4, and stage counts that are
 # and are not a multiple of the pipeline depth. Every output is compared.
-@pytest.mark.parametrize("m,n,k", [(4133, 4100, 384), (4100, 4099, 256), (4096, 8192, 640)])
+# (4000, 1530, 640): 128 x 96 tiles (512 of them against 384 of 128 x 128), ragged M, N, K
+@pytest.mark.parametrize("m,n,k", [(4133, 4100, 384), (4100, 4099, 256), (4096, 8192, 640),
+                                   (4000, 1530, 640)])
 def test_gemm_many_tiles_ragged(dev, m, n, k):
     check_full(synth.small_problem(5, m, n, k, "t3", (0.3, 0.4, 0.3)), dev)
 
