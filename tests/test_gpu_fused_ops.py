@@ -136,9 +136,10 @@ EPILOGUES = {
 }
 
 
+# (4000, 1530, 256): 128 x 96 tiles (direct stores), ragged M and N
 @pytest.mark.parametrize("m,n,k", [(1, 200, 384), (5, 1536, 1536), (16, 130, 8960),
                                    (40, 200, 384), (300, 1536, 1536), (4133, 4100, 384),
-                                   (4096, 1540, 256)])
+                                   (4096, 1540, 256), (4000, 1530, 256)])
 @pytest.mark.parametrize("kind", list(EPILOGUES))
 def test_matmul_epilogues(dev, m, n, k, kind):
     """GEMV (M <= 16), GEMM full and ragged tiles, with each epilogue; y against
@@ -168,7 +169,7 @@ def test_matmul_epilogues(dev, m, n, k, kind):
         assert not np.signbit(got).any()          # ReLU gives +0, never -0
 
 
-@pytest.mark.parametrize("m,n,k", [(3, 200, 384), (4096, 2048, 256)])
+@pytest.mark.parametrize("m,n,k", [(3, 200, 384), (4096, 2048, 256), (4000, 1536, 256)])
 def test_matmul_residual_in_place(dev, m, n, k):
     """residual = y: out = y_old + layer_scale * relu(y + bias), written over y_old."""
     c = synth.small_problem(31, m, n, k, "normal")
