@@ -666,6 +666,97 @@ def run_i8s_tokenizer_ffn(torch, bt, dev, reps: int = 10):
             "gb_per_s": round(tot_bytes / (tot_ms * 1e-3) / 1e9, 1)}
 
 
+def run_ceilings(torch, dev):
+    """What the part itself reaches, for the rooflines' denominators: the
+    v_mfma_i32_16x16x64_i8 issue rate (operands in registers, eight
+    independent chains per wave, 2 and 4 waves per SIMD) with the shader
+    clock it ran at, and a plain streaming read by size (each read takes a
+    fresh window of a 2 GiB buffer, so no size is served from the 256 MB
+    last-level cache; launches are back to back, so the smallest sizes
+    include the gap between launches)."""
+    from ternary_weight_decoder_bt_amd import ceilings as cl
+    stream = torch.cuda.current_stream().cuda_stream
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    wall_khz = cl.wall_clock_khz(dev.index or 0)
+    clocks = torch.zeros(4, dtype=torch.int64, device=dev)
+    iters = 16384
+    mfma = {}
+    for waves_per_simd in (2, 4):
+        blocks = cus * waves_per_simd   # 4 waves per workgroup, one per SIMD
+        out = torch.empty(blocks * 256, dtype=torch.int32, device=dev)
+        cl.mfma_i8_issue(blocks, iters, 1, 1, out, clocks, stream)   # warm-up
+        times, ghz = [], []
+        for _ in range(5):
+            out.fill_(0)
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            cl.mfma_i8_issue(blocks, iters, 1, 1, out, clocks, stream)
+            b.record()
+            torch.cuda.synchronize()
+            times.append(a.elapsed_time(b))
+            c = clocks.cpu().tolist()
+            if wall_khz > 0 and c[3] > c[1]:
+                ghz.append((c[2] - c[0]) / ((c[3] - c[1]) / (wall_khz * 1e3)) / 1e9)
+        ok = bool((out == cl.expected_issue_sum(iters, 1, 1)).all().item())
+        ms = float(np.median(times))
+        ops = blocks * 4 * iters * 8 * 2 * 16 * 16 * 64
+        tops = ops / (ms * 1e-3) / 1e12
+        clk = float(np.median(ghz)) if ghz else None
+        mfma[f"{waves_per_simd}_waves_per_simd"] = {
+            "tops": round(tops, 1), "ms": round(ms, 4), "checksum_ok": ok,
+            "shader_clock_ghz": None if clk is None else round(clk, 3),
+            "ops_per_cu_per_cycle": None if not clk else round(tops * 1e12 / cus / (clk * 1e9), 1)}
+    best = max(mfma.values(), key=lambda v: v["tops"])
+    per_cycle = best["ops_per_cu_per_cycle"]
+    res = {"compute_units": cus, "wall_clock_khz": wall_khz,
+           "mfma_i32_16x16x64_i8": mfma,
+           "int8_peak_tops_measured": best["tops"],
+           "int8_peak_tops_derived_at_2p4ghz": None if not per_cycle
+           else round(per_cycle * cus * 2.4e9 / 1e12, 1),
+           "int8_peak_tops_published": I8_PEAK_TOPS}
+
+    buf_bytes = 2 << 30
+    buf = torch.empty(buf_bytes // 4, dtype=torch.int32, device=dev)
+    buf.random_()
+    reads = []
+    max_blocks = cus * 8
+    xor_out = torch.empty(max_blocks * 16, dtype=torch.int32, device=dev)
+    for mb in (1, 4, 16, 64, 256, 1024, 2048):
+        nbytes = mb << 20
+        blocks = max(1, min(max_blocks, nbytes // (256 * 16 * 8)))
+        windows = buf_bytes // nbytes
+        reps = max(3, min(64, (512 << 20) // nbytes))
+        base = buf.data_ptr()
+        cl.stream_read(base, nbytes, blocks, xor_out, stream)   # warm-up
+        trials = []
+        w = 1
+        for _ in range(3):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            for _ in range(reps):
+                cl.stream_read(base + (w % windows) * nbytes, nbytes, blocks, xor_out, stream)
+                w += 1
+            b.record()
+            torch.cuda.synchronize()
+            trials.append(a.elapsed_time(b) / reps)
+        ms = float(np.median(trials))
+        reads.append({"mb": mb, "gb_per_s": round(nbytes / (ms * 1e-3) / 1e9, 1),
+                      "us_per_read": round(ms * 1e3, 2), "workgroups": blocks,
+                      "fresh_windows": windows > 1})
+    # the kernel read every byte: XOR of its outputs == XOR of the first 1 MiB
+    cl.stream_read(base, 1 << 20, 64, xor_out, stream)
+    torch.cuda.synchronize()
+    got = np.bitwise_xor.reduce(xor_out[:64 * 16].cpu().numpy().view(np.uint32).reshape(-1, 4))
+    want = np.bitwise_xor.reduce(buf[: (1 << 20) // 4].cpu().numpy().view(np.uint32).reshape(-1, 4))
+    res["stream_read"] = reads
+    res["stream_read_checksum_ok"] = bool(np.array_equal(got, want))
+    res["stream_read_peak_gb_per_s"] = max(r["gb_per_s"] for r in reads)
+    res["hbm_peak_gb_per_s_published"] = HBM_PEAK_GBS
+    del buf
+    torch.cuda.empty_cache()
+    return res
+
+
 def cpu_baseline(seconds: float):
     """The oracle as it stands (quantize, exact fp64-BLAS integer matmul,
     rescale) over the whole decode step, repeated until `seconds` (at least
@@ -715,6 +806,8 @@ def main():
     ap.add_argument("--prefill-steps", type=int, default=5)
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-ceilings", action="store_true",
+                    help="skip the matrix-core issue-rate and streaming-read measurements")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy (5 times), to scale the "
                          "FETCH_SIZE / WRITE_SIZE counters of a profiler run")
@@ -966,6 +1059,13 @@ def main():
     # ---- I8_S (the tokenizer's INT8 GEMMs), secondary
     if not args.no_i8s:
         out["i8s"] = run_i8s_tokenizer_ffn(torch, bt, dev)
+
+    if not args.no_ceilings:
+        out["ceilings"] = run_ceilings(torch, dev)
+        c = out["ceilings"]
+        log(f"ceilings: int8 MFMA {c['int8_peak_tops_measured']} TOPS measured "
+            f"({c['int8_peak_tops_derived_at_2p4ghz']} at 2.4 GHz), streaming read "
+            f"{c['stream_read_peak_gb_per_s']} GB/s")
 
     if not args.no_cpu_baseline:
         log("timing the CPU oracle")

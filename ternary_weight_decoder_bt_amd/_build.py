@@ -1,4 +1,5 @@
-"""Build libbt.so in-tree with hipcc for gfx950 (MI355X)."""
+"""Build libbt.so (the matmul path) and libbt_ceilings.so (hardware ceiling
+measurements) in-tree with hipcc for gfx950 (MI355X)."""
 
 from __future__ import annotations
 
@@ -15,6 +16,8 @@ LIB_PATH = os.path.join(PKG_DIR, LIB_NAME)
 ARCH = "gfx950"
 
 SOURCES = ("bt_host.cpp", "bt_kernels.hip", "bt_gemm.hip", "bt_ternarize.hip")
+CEILINGS_LIB_PATH = os.path.join(PKG_DIR, "libbt_ceilings.so")
+CEILINGS_SOURCES = ("bt_ceilings.hip",)
 
 # -ffp-contract=off: the quantizer's rounding decision must see the rounded
 #   fp32 product x * (127 / a), never a fused multiply-add of it.
@@ -40,10 +43,17 @@ def hipcc() -> str:
 
 
 def build(verbose: bool = False) -> str:
-    """Compile every source into libbt.so next to this file; returns its path."""
-    tmp = LIB_PATH + ".tmp"
+    """Compile libbt.so and libbt_ceilings.so next to this file; returns the
+    path of libbt.so."""
+    _compile(SOURCES, LIB_PATH, verbose)
+    _compile(CEILINGS_SOURCES, CEILINGS_LIB_PATH, verbose)
+    return LIB_PATH
+
+
+def _compile(sources, lib_path: str, verbose: bool) -> None:
+    tmp = lib_path + ".tmp"
     cmd = [hipcc(), *FLAGS, "-I", INCLUDE, "-I", CSRC,
-           *[os.path.join(CSRC, s) for s in SOURCES], "-o", tmp]
+           *[os.path.join(CSRC, s) for s in sources], "-o", tmp]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if verbose or res.returncode != 0:
         print(" ".join(cmd))
@@ -52,8 +62,7 @@ def build(verbose: bool = False) -> str:
         print("\n".join(l for l in res.stderr.splitlines() if "packed-fp32-ops" not in l))
     if res.returncode != 0:
         raise RuntimeError(f"hipcc failed with status {res.returncode}")
-    os.replace(tmp, LIB_PATH)
-    return LIB_PATH
+    os.replace(tmp, lib_path)
 
 
 if __name__ == "__main__":
