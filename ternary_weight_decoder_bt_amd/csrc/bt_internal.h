@@ -130,12 +130,13 @@ size_t gemv_partial_bytes(const GemvDesc& d);
 size_t gemv_single_workspace_bytes(const GemvDesc& d);   // single calls: slices + d, row sums
 
 // GEMM shape choice (M > 16), made from the shape alone so that the host can
-// size the workspace: the persistent kernel (128 x 256 tiles), the tiled
-// kernel with 128 x 256 tiles, or with 128 x 128 tiles and K split into
-// `splits` ranges of `sps` stages when there are too few tiles to fill the
-// device (partial sums meet in an int32 workspace).
+// size the workspace: the persistent kernel (128 x 256 tiles) when there are
+// at least as many such tiles as resident workgroup slots, else the tiled
+// kernel with the tile shape of least estimated time (128 x 128, 128 x 96 or
+// 64 x 64), with K split into `splits` ranges of `sps` stages when there are
+// fewer tiles than compute units (partial sums meet in an int32 workspace).
 constexpr int kGemmSlots = 512;   // resident workgroups the split choice aims at
-constexpr int kGemmSmallTiles = 256;   // below this many 128 x 128 tiles, use 64 x 64 tiles
+constexpr int kGemmSmallTiles = 256;   // int8: below this many 128 x 128 tiles, use 64 x 64 tiles
 // 64-wide K steps the small-matrix I8_S kernel holds per weight tile: ceil(K/64)
 // rounded up to a power of two (1, 2, 4 or 8).
 inline int i8_stream_steps(int64_t K) {
@@ -146,7 +147,7 @@ struct GemmChoice {
     int kind;        // 0 persistent, 1 tiled 128 x 256, 2 tiled 128 x 128, 3 tiled 64 x 64,
                      // 4 small int8 weight matrix held in LDS (i8_stream_kernel),
                      // 5 tiled 128 x 96
-    int splits;      // K ranges (kinds 2, 3), else 1
+    int splits;      // K ranges (kinds 2, 3, 5), else 1
     int sps;         // stages per range (stage = 256-wide K for ternary, 128 for int8)
     int64_t tiles;   // output tiles of the chosen kind
 };

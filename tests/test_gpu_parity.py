@@ -250,9 +250,10 @@ def test_gemm_shapes(dev, m, n, k):
 # workgroup, pipeline crossing tile boundaries), with ragged M, N a multiple
 # of 4 but not of the tile, N not a multiple of 4, and stage counts that are
 # and are not a multiple of the pipeline depth. Every output is compared.
-# (4000, 1530, 640): 128 x 96 tiles (512 of them against 384 of 128 x 128), ragged M, N, K
+# (4000, 1530, 640): 128 x 96 tiles (512 of them against 384 of 128 x 128), ragged M, N, K;
+# (2000, 2000, 640): 128 x 128 tiles (256, one per compute unit), ragged M, N, K
 @pytest.mark.parametrize("m,n,k", [(4133, 4100, 384), (4100, 4099, 256), (4096, 8192, 640),
-                                   (4000, 1530, 640)])
+                                   (4000, 1530, 640), (2000, 2000, 640)])
 def test_gemm_many_tiles_ragged(dev, m, n, k):
     check_full(synth.small_problem(5, m, n, k, "t3", (0.3, 0.4, 0.3)), dev)
 
@@ -485,7 +486,10 @@ def test_grouped_mixed_m_with_lds_split(dev, fused):
     assert int(plan.workspace.count_nonzero()) == 0
 
 
-@pytest.mark.parametrize("m,n,k", [(150, 1536, 8960), (130, 1540, 8960), (17, 130, 2048)])
+# 64 x 64 tiles in 3, 3, 2 and 2 ranges; (1500, 1530, 8960): 128 x 96 tiles in 2 ranges;
+# (1700, 1900, 2560): 128 x 128 tiles in 2 ranges
+@pytest.mark.parametrize("m,n,k", [(150, 1536, 8960), (130, 1540, 8960), (17, 130, 2048),
+                                   (512, 1536, 8960), (1500, 1530, 8960), (1700, 1900, 2560)])
 def test_gemm_split_k_exact_and_workspace_clean(dev, m, n, k):
     """Few output tiles and a long K: K is split and the int32 partial sums meet
     in the workspace; the result is the oracle's, bit for bit, on two calls in a

@@ -113,13 +113,18 @@ def test_sizes():
                      [(1536, 2048), (1536, 1536), (1536, 17920), (8960, 1536)])
     assert total == 327_548_928
     # GEMM: none when the output has enough tiles; split K (one M x N int32
-    # slice of partial sums per K range) when it has fewer tiles than half the
-    # compute units and a long K
+    # slice of partial sums per K range) when it has fewer tiles than compute
+    # units and a long K
     assert bt.matmul_workspace_bytes(4096, 17920, 1536) == 0
-    assert bt.matmul_workspace_bytes(4096, 1536, 8960) == 0   # 384 tiles: enough
+    assert bt.matmul_workspace_bytes(4096, 1536, 8960) == 0   # 512 tiles of 128 x 96
+    assert bt.matmul_workspace_bytes(2048, 1536, 8960) == 0   # 256 tiles: one per CU
     assert bt.matmul_workspace_bytes(17, 1536, 1536) == 0     # too short a K to split
-    # 3 x 24 tiles of 64 x 64, 35 stages: min(ceil(512/72), 35//4) = 8 ranges of 5 -> 7 ranges
-    assert bt.matmul_workspace_bytes(150, 1536, 8960) == 7 * 150 * 1536 * 4
+    # 3 x 24 tiles of 64 x 64, 35 stages: max(2, ceil(192/72)) = 3 ranges of 12
+    assert bt.matmul_workspace_bytes(150, 1536, 8960) == 3 * 150 * 1536 * 4
+    # 4 x 24 tiles of 64 x 64 at M = 512 ... 8 x 24: 2 ranges
+    assert bt.matmul_workspace_bytes(512, 1536, 8960) == 2 * 512 * 1536 * 4
+    # 12 x 16 tiles of 128 x 96: 2 ranges
+    assert bt.matmul_workspace_bytes(1536, 1536, 8960) == 2 * 1536 * 1536 * 4
     # 64 x 64 tiles below 256 tiles of 128 x 128: 3 x 32 tiles, 64 stages of 128:
     # min(ceil(512/96), 16) = 6 ranges of 11 -> 6 ranges
     assert L_i8_ws(150, 2048, 8192) == 6 * 150 * 2048 * 4
