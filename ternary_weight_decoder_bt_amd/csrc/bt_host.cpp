@@ -159,50 +159,42 @@ GemmChoice gemm_choice(int64_t M, int64_t N, int64_t K, bool int8_weights, bool 
         c.tiles = wide;
         return c;
     }
+    // The tile shape with the least estimated time: the rounds of the resident
+    // workgroup slots its tiles need (a last round, or a whole launch, of at
+    // most one workgroup per compute unit takes about two thirds of the time
+    // of one with two), times the tile's area over its measured relative
+    // efficiency (64 x 64: 0.6, 128 x 96: 0.89, 128 x 128: 1; int8 weights have
+    // no 128 x 96 kernel). Measured at M = 150 ... 6144 on the decoder's and
+    // the tokenizer's shapes, it picks the fastest shape, or one within 5% of
+    // it, in every case.
+    struct Cand { int kind; int64_t bm, bn; double eff; };
+    const Cand cands[3] = {{2, 128, 128, 1.0}, {5, 128, 96, 0.89}, {3, 64, 64, 0.6}};
+    double best = 0.0;
+    for (const Cand& k : cands) {
+        if (int8_weights && k.kind == 5) continue;
+        const int64_t t = ceil_div(M, k.bm) * ceil_div(N, k.bn);
+        const int64_t full = t / kGemmSlots, rem = t % kGemmSlots;
+        const double rounds =
+            double(full) + (rem == 0 ? 0.0 : rem <= kGemmSlots / 2 ? 0.66 : 1.0);
+        const double est = rounds * double(k.bm * k.bn) / k.eff;
+        if (c.tiles == 0 || est < best) {
+            best = est;
+            c.kind = k.kind;
+            c.tiles = t;
+        }
+    }
+    // Fewer tiles than compute units: split K into ranges that fill the
+    // compute units about once more, of at most 16 stages each where K is
+    // long, within one round of slots. The ranges' slices cost (splits + 1)
+    // M x N int32 of traffic, so the split is taken for a small output or a
+    // long K only. Measured: 12-30% faster at M = 150 ... 512 with K = 8192,
+    // 8960; a split of a 6000 x 512 output over K = 2048 was 30% slower.
     const int64_t nst = ceil_div(K, int8_weights ? 128 : 256);
     int64_t splits = 1;
-    if (int8_weights) {
-        c.kind = 2;
-        c.tiles = ceil_div(M, 128) * ceil_div(N, 128);
-        // fewer 128 x 128 tiles than compute units: 64 x 64 tiles put four
-        // times as many workgroups to work
-        if (c.tiles < kGemmSmallTiles) {
-            c.kind = 3;
-            c.tiles = ceil_div(M, 64) * ceil_div(N, 64);
-        }
-        // split only below one tile per two compute units: every range stores
-        // an M x N int32 slice and a second launch reads them all back
-        if (c.tiles < kGemmSlots / 4 && nst >= 8)
-            splits = std::min<int64_t>(ceil_div(kGemmSlots, c.tiles), nst / 4);
-    } else {
-        // The tile shape with the least estimated time: the rounds of the
-        // resident workgroup slots its tiles need (a last round, or a whole
-        // launch, of at most one workgroup per compute unit takes about two
-        // thirds of the time of one with two), times the tile's area over its
-        // measured relative efficiency (64 x 64: 0.6, 128 x 96: 0.89,
-        // 128 x 128: 1). Measured at M = 512 ... 6144 on the decoder's shapes:
-        // it picks the fastest shape, or one within 5% of it, in every case.
-        struct Cand { int kind; int64_t bm, bn; double eff; };
-        const Cand cands[3] = {{2, 128, 128, 1.0}, {5, 128, 96, 0.89}, {3, 64, 64, 0.6}};
-        double best = 0.0;
-        for (const Cand& k : cands) {
-            const int64_t t = ceil_div(M, k.bm) * ceil_div(N, k.bn);
-            const int64_t full = t / kGemmSlots, rem = t % kGemmSlots;
-            const double rounds =
-                double(full) + (rem == 0 ? 0.0 : rem <= kGemmSlots / 2 ? 0.66 : 1.0);
-            const double est = rounds * double(k.bm * k.bn) / k.eff;
-            if (c.tiles == 0 || est < best) {
-                best = est;
-                c.kind = k.kind;
-                c.tiles = t;
-            }
-        }
-        // Fewer tiles than compute units and a long K: split K so the ranges
-        // fill the compute units about once more (measured with K = 8960: 12-20%
-        // faster at M = 150, 256, 512, and than more ranges; 3% at M = 1536;
-        // with exactly one tile per compute unit, M = 2048, a split was slower)
-        if (c.tiles < kGemmSlots / 2 && nst >= 8)
-            splits = std::min<int64_t>(std::max<int64_t>(2, ceil_div(192, c.tiles)), nst / 4);
+    if (c.tiles < kGemmSlots / 2 && nst >= 8) {
+        int64_t s = std::max({int64_t(2), ceil_div(192, c.tiles), ceil_div(nst, 16)});
+        s = std::min({s, int64_t(kGemmSlots) / c.tiles, nst / 4});
+        if (s >= 2 && (M * N <= (int64_t(1) << 20) || K >= 1000 * (s + 1))) splits = s;
     }
     const int64_t sps = ceil_div(nst, std::max<int64_t>(splits, 1));
     c.sps = int(sps);

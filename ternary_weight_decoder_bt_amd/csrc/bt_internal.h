@@ -135,8 +135,7 @@ size_t gemv_single_workspace_bytes(const GemvDesc& d);   // single calls: slices
 // kernel with the tile shape of least estimated time (128 x 128, 128 x 96 or
 // 64 x 64), with K split into `splits` ranges of `sps` stages when there are
 // fewer tiles than compute units (partial sums meet in an int32 workspace).
-constexpr int kGemmSlots = 512;   // resident workgroups the split choice aims at
-constexpr int kGemmSmallTiles = 256;   // int8: below this many 128 x 128 tiles, use 64 x 64 tiles
+constexpr int kGemmSlots = 512;   // resident workgroups (two per compute unit)
 // 64-wide K steps the small-matrix I8_S kernel holds per weight tile: ceil(K/64)
 // rounded up to a power of two (1, 2, 4 or 8).
 inline int i8_stream_steps(int64_t K) {

@@ -57,7 +57,7 @@ def run(x, w8, s, dev, **epi):
                                    (33333, 128, 32), (20001, 64, 256), (1, 16, 32),
                                    (4096, 512, 128), (2000, 128, 512), (150, 8192, 2048),
                                    (150, 2048, 8192), (37, 130, 96), (5, 16, 32),
-                                   (1200, 4096, 1024)])
+                                   (1200, 4096, 1024), (6000, 512, 2048)])
 def test_i8s_matmul_shapes(dev, m, n, k):
     x, w8, s = case(40 + k, m, n, k)
     ref = oracle.i8s_forward_ref(x, w8, s)

@@ -487,9 +487,9 @@ def test_grouped_mixed_m_with_lds_split(dev, fused):
 
 
 # 64 x 64 tiles in 3, 3, 2 and 2 ranges; (1500, 1530, 8960): 128 x 96 tiles in 2 ranges;
-# (1700, 1900, 2560): 128 x 128 tiles in 2 ranges
+# (1700, 1900, 8960): 128 x 128 tiles in 2 ranges
 @pytest.mark.parametrize("m,n,k", [(150, 1536, 8960), (130, 1540, 8960), (17, 130, 2048),
-                                   (512, 1536, 8960), (1500, 1530, 8960), (1700, 1900, 2560)])
+                                   (512, 1536, 8960), (1500, 1530, 8960), (1700, 1900, 8960)])
 def test_gemm_split_k_exact_and_workspace_clean(dev, m, n, k):
     """Few output tiles and a long K: K is split and the int32 partial sums meet
     in the workspace; the result is the oracle's, bit for bit, on two calls in a

@@ -125,9 +125,12 @@ def test_sizes():
     assert bt.matmul_workspace_bytes(512, 1536, 8960) == 2 * 512 * 1536 * 4
     # 12 x 16 tiles of 128 x 96: 2 ranges
     assert bt.matmul_workspace_bytes(1536, 1536, 8960) == 2 * 1536 * 1536 * 4
-    # 64 x 64 tiles below 256 tiles of 128 x 128: 3 x 32 tiles, 64 stages of 128:
-    # min(ceil(512/96), 16) = 6 ranges of 11 -> 6 ranges
-    assert L_i8_ws(150, 2048, 8192) == 6 * 150 * 2048 * 4
+    # 14 x 15 tiles of 128 x 128 with K = 2560: the slices would cost more than the split gains
+    assert bt.matmul_workspace_bytes(1700, 1900, 2560) == 0
+    # int8: 3 x 32 tiles of 64 x 64, 64 stages of 128: ranges of at most 16 stages -> 4
+    assert L_i8_ws(150, 2048, 8192) == 4 * 150 * 2048 * 4
+    # a 6000 x 512 output over K = 2048: the slices would cost more than the split gains
+    assert L_i8_ws(6000, 512, 2048) == 0
     # int8 weights of at most 64 KB with K <= 512 are held in LDS: never split
     assert L_i8_ws(480000, 128, 32) == 0 and L_i8_ws(30, 512, 128) == 0
     # GEMV: K is split only where M x K activations exceed one LDS slice
