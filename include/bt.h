@@ -185,11 +185,12 @@ bt_status bt_rmsnorm_quantize(const float* x, const float* g, float eps, int64_t
  * workspace: device, at least bt_matmul_workspace_bytes(M,N,K) bytes (may be
  *   NULL when that is 0); its contents on entry do not matter. A shape needs
  *   one when its K is split: GEMVs (M <= 16) whose M x K int8 activations do
- *   not fit one workgroup's LDS slice, and GEMMs with fewer than 128 output
- *   tiles of 128 x 64. Each K range writes its int32 partial sums to a slice
- *   of its own, and a second launch adds the slices in a fixed order (exact)
- *   and applies the scales and the epilogue. Calls that share one workspace
- *   must be ordered on one stream.
+ *   not fit one workgroup's LDS slice, and GEMMs with fewer output tiles than
+ *   compute units and a K long enough for the split to pay (the library's
+ *   choice, made from M, N, K alone). Each K range writes its int32 partial
+ *   sums to a slice of its own, and a second launch adds the slices in a fixed
+ *   order (exact) and applies the scales and the epilogue. Calls that share
+ *   one workspace must be ordered on one stream.
  * w_scale must be finite (BT_ERR_VALUE otherwise).
  * ------------------------------------------------------------------------- */
 size_t bt_matmul_workspace_bytes(int64_t M, int64_t N, int64_t K);
