@@ -779,6 +779,43 @@ def cpu_baseline(seconds: float):
         passes.append(time.perf_counter() - t0)
         total += passes[-1]
     t = float(np.median(passes))
+    # the same on one core, over one layer (the four projections), and the
+    # oracle's unpacking of that layer's canonical 2-bit bytes, timed apart
+    layer = probs[:len(synth.PROJECTIONS)]
+    layer_bytes = sum(c["N"] * c["K"] // 4 for c in layer)
+    one_core = None
+    try:
+        from threadpoolctl import threadpool_limits
+        with threadpool_limits(limits=1):
+            ts = []
+            for _ in range(3):
+                t0 = time.perf_counter()
+                for c in layer:
+                    oracle.forward_ref(c["x"], c["w"], c["w_scale"], "f64")
+                ts.append(time.perf_counter() - t0)
+        one_core = {"value": round(layer_bytes / float(np.median(ts)) / 1e9, 4), "unit": "GB/s",
+                    "cores": 1, "sample": "layer 0's four projections, median of 3 passes"}
+    except Exception:  # noqa: BLE001
+        pass
+    packed = [oracle.pack_ref(c["w"]) for c in layer]
+    ts = []
+    for _ in range(3):
+        t0 = time.perf_counter()
+        for c, pk in zip(layer, packed):
+            oracle.unpack_ref(pk, c["K"])
+        ts.append(time.perf_counter() - t0)
+    unpack = {"value": round(layer_bytes / float(np.median(ts)) / 1e9, 4),
+              "unit": "GB/s of packed bytes", "cores": 1,
+              "sample": "oracle.unpack_ref over layer 0's four projections, median of 3 passes"}
+    cpu_model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    cpu_model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
     return {"value": round(w_bytes / t / 1e9, 4), "unit": "GB/s", "cores": threads,
             "kind": "oracle",
             "sample": f"the whole decode step (28 layers x 4 projections, M=1), {len(passes)} "
@@ -787,7 +824,10 @@ def cpu_baseline(seconds: float):
                       f"to int8; value = packed weight bytes / pass time",
             "tokens_per_s": round(1.0 / t, 3),
             "host_cpus": os.cpu_count(),
-            "affinity_cpus": len(os.sched_getaffinity(0))}
+            "affinity_cpus": len(os.sched_getaffinity(0)),
+            "cpu_model": cpu_model,
+            "one_core": one_core,
+            "unpack": unpack}
 
 
 # --------------------------------------------------------------------- main
