@@ -618,6 +618,34 @@ VAE_STAGES = ((32, 480000), (64, 240000), (128, 120000), (256, 30000), (512, 600
               (1024, 1200), (2048, 150))
 
 
+def run_remainder_for_counters(torch, bt, dev, reps: int):
+    """The remainder sweep's points (gate_up, then down, each M in order), each
+    launched `reps` times eagerly on rotating weight copies, for a counter pass
+    of the profiler: every call's GEMV launches in order, so the n-th group of
+    `reps` gemv_kernel dispatches is the n-th point (a split call adds one
+    reduce launch, named otherwise). Prints the point order as JSON."""
+    points = []
+    for name in ("gate_up", "down"):
+        c1 = synth.decode_remainder_problem(name, 1)
+        n, k = c1["N"], c1["K"]
+        packed = torch.from_numpy(bt.pack_ternary(c1["w"]).reshape(-1)).to(dev)
+        ws_ = _rotating_copies(torch, bt.repack_ternary(packed, n, k))
+        for m in synth.REMAINDER_MS:
+            cm = synth.decode_remainder_problem(name, m)
+            q = bt.quantize_act(torch.from_numpy(cm["x"]).to(dev))
+            y = torch.empty((m, n), dtype=torch.float32, device=dev)
+            wsp = bt.new_workspace(m, n, k, dev)
+            torch.cuda.synchronize()
+            for i in range(reps):
+                bt.ternary_matmul(*q, ws_[(7 * i + 1) % len(ws_)], n, cm["w_scale"], y=y,
+                                  workspace=wsp)
+            torch.cuda.synchronize()
+            points.append({"shape": name, "M": m, "N": n, "K": k,
+                           "alg_bytes": bt.packed_bytes(n, k) + m * k + 4 * m * n + 8 * m})
+        del ws_, packed
+    print(json.dumps({"remainder_points": points, "reps": reps}), flush=True)
+
+
 def run_i8s_tokenizer_ffn(torch, bt, dev, reps: int = 10):
     """Time the I8_S GEMMs of the tokenizer's FFN layers (synthetic int8 codes and
     weights). Returns {stage: {...}} and the aggregate."""
@@ -848,6 +876,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-ceilings", action="store_true",
                     help="skip the matrix-core issue-rate and streaming-read measurements")
+    ap.add_argument("--remainder-counters", type=int, default=0, metavar="R",
+                    help="only launch each remainder-sweep point R times eagerly (for a "
+                         "profiler counter pass) and print the point order")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy (5 times), to scale the "
                          "FETCH_SIZE / WRITE_SIZE counters of a profiler run")
@@ -871,7 +902,7 @@ def main():
         return
 
     packed_prefill = None
-    if not args.no_prefill:
+    if not args.no_prefill and not args.remainder_counters:
         t0 = time.time()
         packed_prefill = pack_long_prefill_weights(args.layers)
         log(f"long-prefill weights drawn and packed on the host in {time.time() - t0:.1f}s")
@@ -884,6 +915,9 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
     dev = torch.device("cuda:0")
+    if args.remainder_counters > 0:
+        run_remainder_for_counters(torch, bt, dev, args.remainder_counters)
+        return
 
     # ---- decode step (headline)
     ds = DecodeStep(torch, bt, dev, args.layers)
