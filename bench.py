@@ -200,6 +200,65 @@ class DecodeStep:
         if ev is not None:
             ev[1].record()
 
+    def batched(self, m: int, steps: int, trials: int):
+        """The same decode step for a batch of m tokens (m <= 16): the 112
+        projections with m-row activations (seeded as the single-token step),
+        the two weight sets alternating; quantization fused into the grouped
+        GEMV, and as two launches (grouped quantize, grouped GEMV). Returns
+        ({way: median ms per step}, parity of sampled projections)."""
+        torch, bt = self.torch, self.bt
+        import oracle
+        dev = self.wsets[0][0].device
+        fitems, qitems, gitems = [], [], []
+        for (layer, proj, _m, n, k), it in zip(self.shapes, self.items):
+            x = torch.from_numpy(synth.decode_problem(layer, proj, m, with_weights=False)["x"])
+            x = x.to(dev)
+            y = torch.full((m, n), float("nan"), device=dev)
+            xq = torch.empty((m, k), dtype=torch.int8, device=dev)
+            xs = torch.empty(m, dtype=torch.float32, device=dev)
+            xsum = torch.empty(m, dtype=torch.int32, device=dev)
+            fitems.append({"x": x, "n": n, "w_scale": it["w_scale"], "y": y})
+            qitems.append((x, xq, xs, xsum))
+            gitems.append({"xq": xq, "xscale": xs, "xsum": xsum, "n": n,
+                           "w_scale": it["w_scale"], "y": y})
+        fplans = [bt.MatmulPlan([dict(it, wdev=w) for it, w in zip(fitems, ws)])
+                  for ws in self.wsets]
+        qplan = bt.QuantPlan(qitems)
+        gplans = [bt.MatmulPlan([dict(it, wdev=w) for it, w in zip(gitems, ws)])
+                  for ws in self.wsets]
+        ways = {"fused": lambda i: fplans[i & 1].launch(),
+                "two_launch": lambda i: (qplan.launch(), gplans[i & 1].launch())}
+        ok = True
+        for fn in ways.values():
+            for it in fitems:
+                it["y"].fill_(float("nan"))
+            fn(0)
+            torch.cuda.synchronize()
+            for idx in (0, 2, 3, len(fitems) - 1):
+                layer, proj, _m, n, k = self.shapes[idx]
+                c = synth.decode_problem(layer, proj, m)
+                ref = oracle.forward_ref(c["x"], c["w"], c["w_scale"], "f64")
+                y = fitems[idx]["y"].cpu().numpy()
+                nz = ref["y"] != 0
+                ok &= bool((y[~nz] == 0).all())
+                ok &= bool((np.abs(y[nz] - ref["y"][nz]) <= 1e-6 * np.abs(ref["y"][nz])).all())
+        for fn in ways.values():
+            for i in range(10):
+                fn(i)
+        torch.cuda.synchronize()
+        times = {w: [] for w in ways}
+        for _ in range(trials):
+            for w, fn in ways.items():
+                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                a.record()
+                for i in range(steps):
+                    fn(i)
+                b.record()
+                torch.cuda.synchronize()
+                times[w].append(a.elapsed_time(b) / steps)
+        del fplans, gplans, qplan
+        return {w: float(np.median(v)) for w, v in times.items()}, bool(ok)
+
     def clear_outputs(self):
         for it in self.items:
             it["y"].fill_(float("nan"))
@@ -1037,6 +1096,22 @@ def main():
                                             round(med["gemv_two_launch_b2b"], 5)},
         "timing": f"median of {args.trials} interleaved trials of {args.steps} steps per variant",
     }
+    # ---- the same step for a batch of 16 tokens (batched decode)
+    b_ms, b_ok = ds.batched(16, max(1, args.steps // 2), args.trials)
+    b_best = min(b_ms, key=b_ms.get)
+    out["decode_step_M16"] = {
+        "workload": "the same 112-projection decode step for a batch of 16 tokens (grouped "
+                    "launches; down's 16 x 8960 activations split over K ranges that meet "
+                    "through atomics in the workspace)",
+        "ms_per_step": {w: round(v, 5) for w, v in b_ms.items()}, "best": b_best,
+        "tokens_per_s": round(16e3 / b_ms[b_best], 1),
+        "weight_gb_per_s": round(ds.w_bytes / (b_ms[b_best] * 1e-3) / 1e9, 1),
+        "pct_of_hbm_peak": round(100 * ds.w_bytes / (b_ms[b_best] * 1e-3) / 1e9 / HBM_PEAK_GBS, 2),
+        "parity_ok": b_ok}
+    log("decode step, M=16: " + ", ".join(
+        f"{w} {v * 1e3:.1f} us ({ds.w_bytes / (v * 1e-3) / 1e9:.0f} GB/s of weights)"
+        for w, v in b_ms.items()) + f"; parity {b_ok}")
+
     # ---- the one-time device repack, timed on its own (not part of a step)
     rp = ds.time_repack()
     rp_bytes = 2 * ds.w_bytes   # read canonical + write tile layout (same size at these shapes)

@@ -593,7 +593,15 @@ __device__ __forceinline__ int32_t gemv_row_sum(const GemvShared& sh, int m) {
 
 // Epilogue of one tile. With K split into chunks, partial sums meet in the
 // workspace (int32 addition is exact in any order) and the last chunk to
-// arrive reads the total, clears the workspace and finishes the tile.
+// arrive reads the total, clears the workspace and finishes the tile. Every
+// access to the shared words (partial sums and arrival counters) is an atomic,
+// performed where all compute units and XCDs see it; a chunk waits until its
+// additions have completed before it counts itself in, and the last chunk
+// reads the totals with atomics after its count came back. No fence is needed:
+// a device-scope fence would add a write-back and invalidation of the L2 for
+// plain stores, which none of this uses, and costs more than the whole
+// product for a 16-token batch (measured: the down projection 16.5 -> 1.4 us
+// per layer without it).
 __device__ __forceinline__ void gemv_finish(const GemvDesc& d, int64_t tile, v4i c, int lane,
                                             const GemvShared& sh, int chunk) {
     const int kq = lane >> 4;
@@ -618,12 +626,15 @@ __device__ __forceinline__ void gemv_finish(const GemvDesc& d, int64_t tile, v4i
             const int mm = 4 * kq + i;
             if (mm < d.M) atomicAdd(d.ws + mm * ldw + n, c[i]);
         }
-        __threadfence();
+        // the additions complete (are performed) before the count goes out
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_s_waitcnt(0);
+        asm volatile("" ::: "memory");
         uint32_t prev = 0;
         if (lane == 0) prev = atomicAdd(d.cnt + tile, 1u);
         prev = __shfl(prev, 0, 64);
         if (prev != uint32_t(d.chunks - 1)) return;
-        __threadfence();
+        asm volatile("" ::: "memory");
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int mm = 4 * kq + i;

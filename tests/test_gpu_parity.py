@@ -486,6 +486,34 @@ def test_grouped_mixed_m_with_lds_split(dev, fused):
     assert int(plan.workspace.count_nonzero()) == 0
 
 
+@pytest.mark.parametrize("fused", [False, True])
+def test_grouped_batched_decode_split_repeated(dev, fused):
+    """A 16-token batch through four layers' projections in one plan: every
+    down projection (16 x 8960 activations) is split over K ranges whose
+    partial sums meet through atomics, the last range to arrive finishing the
+    tile. Thirty launches in a row, each checked exactly (acc, q) and within
+    the tolerance (y) against the oracle, and the workspace left clean: an
+    ordering mistake between a range's additions and its arrival count would
+    show as a wrong sum in some launch."""
+    cases = [synth.decode_problem(layer, proj, 16) for layer in (0, 5, 11, 27)
+             for proj in range(4)]
+    items, refs = _grouped_items(cases, dev, fused)
+    plan = bt.MatmulPlan(items)
+    assert plan.workspace is not None
+    down = [i for i, c in enumerate(cases) if c["K"] == 8960]
+    for rep in range(30):
+        for i in down:
+            items[i]["y"].fill_(float("nan"))
+            items[i]["acc"].fill_(POISON_I32)
+        plan.launch()
+        torch.cuda.synchronize()
+        for i in down:
+            assert_exact(f"acc[{i}] launch {rep}", items[i]["acc"].cpu().numpy(), refs[i]["acc"])
+            assert_rel(f"y[{i}] launch {rep}", items[i]["y"].cpu().numpy(), refs[i]["y"])
+    _check_grouped(items, refs)
+    assert int(plan.workspace.count_nonzero()) == 0
+
+
 # 64 x 64 tiles in 3, 3, 2 and 2 ranges; (1500, 1530, 8960): 128 x 96 tiles in 2 ranges;
 # (1700, 1900, 8960): 128 x 128 tiles in 2 ranges
 @pytest.mark.parametrize("m,n,k", [(150, 1536, 8960), (130, 1540, 8960), (17, 130, 2048),
