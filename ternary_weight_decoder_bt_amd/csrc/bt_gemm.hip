@@ -9,20 +9,21 @@
 // (WA*WGM) x (WW*WGN) tile of y (token rows x weight rows); each wave owns a
 // WA x WW sub-tile held as (WA/16) x (WW/16) MFMA accumulators.
 //
-// K advances in 256-wide stages. The workgroup's activation rows for a stage
-// (BM x 256 int8) are copied from global memory straight into one of two LDS
-// buffers (buffer_load ... lds: no staging registers), while the other
+// K advances in stages (256 wide in the tiled ternary kernels, 128 in the
+// persistent one and for int8 weights). The workgroup's activation rows for a
+// stage (BM x KS int8) are copied from global memory straight into one of NS
+// LDS buffers (buffer_load ... lds: no staging registers), while another
 // buffer feeds the matrix cores. Rows past M, and columns past K, read as
-// zero through the buffer bounds. In LDS a row's sixteen 16-byte chunks are
-// stored XOR-swizzled (chunk c of row r at slot c ^ (r % 16)), so the 16 rows
-// an MFMA fragment read touches fall in 16 different bank groups. Each wave
-// keeps its WW/16 weight tiles' packed words for the next stage in registers
-// (one 128-bit load per tile and lane) and unpacks each 16-element word right
-// before the WA/16 MFMAs that use it.
+// zero through the buffer bounds. In LDS a row's 16-byte chunks are stored
+// XOR-swizzled, so the 16 rows an MFMA fragment read touches fall in 16
+// different bank groups. Each wave keeps its WW/16 weight tiles' packed words
+// for the coming stages in registers (one load per tile and lane) and unpacks
+// each 16-element word right before the WA/16 MFMAs that use it.
 //
 // Workgroup order: consecutive workgroup ids go to different XCDs, so ids are
-// remapped to give each XCD a contiguous band of output tiles (whole rows of
-// tiles along N): the activation rows of a band stay in that XCD's L2.
+// remapped to give each XCD a compact block of output tiles (a group of
+// token-row bands, walked down the bands first): its activation rows and
+// weight tiles stay in that XCD's L2.
 
 #include <hip/hip_runtime.h>
 
@@ -691,26 +692,6 @@ void gemm_persistent_kernel(GemmArgs g) {
     wait_vmcnt<0>();
 }
 
-#ifndef BT_GEMM_WA
-#define BT_GEMM_WA 128
-#endif
-#ifndef BT_GEMM_WW
-#define BT_GEMM_WW 64
-#endif
-#ifndef BT_GEMM_WGM
-#define BT_GEMM_WGM 1
-#endif
-#ifndef BT_GEMM_WGN
-#define BT_GEMM_WGN 4
-#endif
-#ifndef BT_GEMM_KS
-#define BT_GEMM_KS 128
-#endif
-#ifndef BT_GEMM_NS
-#define BT_GEMM_NS 2
-#endif
-
-
 #ifndef BT_GEMM_GROUPED
 #define BT_GEMM_GROUPED 1
 #endif
@@ -723,9 +704,9 @@ int32_t gemm_group_m(int32_t m_tiles, int32_t n_tiles, int64_t tiles_per_xcd) {
     return int32_t(std::max<int64_t>(1, std::min<int64_t>(m_tiles, gm)));
 }
 
-// Shape dispatch of the GEMM: the default tile, or a 128 x 128 tile (waves of
-// 64 x 64) when the default leaves fewer than two workgroups per compute unit
-// (e.g. 4096 x 1536 outputs).
+// Launch of the tiled GEMM for one tile shape (the shape itself is chosen on
+// the host, gemm_choice): one workgroup per (tile, K range), numbered so that
+// an XCD's workgroups take one compact block of tiles.
 template <int WA, int WW, int WGM, int WGN, int KS, int NS, bool kW8 = false>
 bt_status launch_gemm(GemmArgs g, hipStream_t stream) {
     constexpr int BM = WA * WGM;
@@ -842,14 +823,12 @@ bt_status launch_splitk_reduce(const GemmArgs& g, hipStream_t stream) {
     return hipGetLastError() == hipSuccess ? BT_OK : BT_ERR_DEVICE;
 }
 
-// Runs the kernel gemm_choice picked for the shape; with split K, binds the
-// workspace (partial sums, then one counter per tile).
 // I8_S product for a small weight matrix and many tokens (the tokenizer's early
 // stages: N x K int8 of at most 64 KB, K <= 512, M up to hundreds of thousands).
 // Every workgroup first copies the whole repacked matrix, [tile][64-wide step]
 // in 1 KB pieces, into LDS. Each wave then streams blocks of 16 tokens: one
 // 16-byte activation fragment per lane and 64-wide step, prefetched a block
-// ahead, meets the 16-row weight tiles held in LDS, eight tiles per pass, and
+// ahead, meets the 16-row weight tiles held in LDS, four tiles per pass, and
 // the fp32 rows go out at once. Per token these shapes read K + 4 bytes and
 // write 4 N, so the output bytes bound them; the generic GEMM's 128-token
 // tiles with one K stage each spend their time in start-up and epilogue.
@@ -974,6 +953,8 @@ bt_status launch_i8_stream(GemmArgs g, hipStream_t stream) {
     return hipGetLastError() == hipSuccess ? BT_OK : BT_ERR_DEVICE;
 }
 
+// Runs the kernel gemm_choice picked for the shape; with split K, each range
+// writes its own slice of the workspace and a second launch adds the slices.
 bt_status dispatch_gemm(GemmArgs g, bool int8_weights, void* workspace, size_t workspace_bytes,
                         hipStream_t stream) {
     const bt::GemmChoice c =
