@@ -1,6 +1,6 @@
 """Every launch goes to the stream it is given. The whole path (repack,
 quantize, GEMV and GEMM with a K split and its reduce launch, the grouped plan
-with its atomics, the I8_S product, ternarization) runs on a side stream while
+with its atomics, the I8_S product) runs on a side stream while
 the current stream is left alone; only that side stream is synchronized before
 the results are read, and they must be the oracle's. A launch on another stream
 would race with the side stream's producers (the inputs are written on the side
