@@ -53,11 +53,14 @@ def run(x, w8, s, dev, **epi):
     return xq.cpu().numpy(), y.cpu().numpy(), acc.cpu().numpy()
 
 
+# (999, 112, 384) and (1500, 48, 160): the small-matrix kernel with steps past K (eight
+# 64-wide steps held for six real ones; a step half inside K)
 @pytest.mark.parametrize("m,n,k", [(1000, 128, 32), (700, 32, 128), (300, 256, 64),
                                    (33333, 128, 32), (20001, 64, 256), (1, 16, 32),
                                    (4096, 512, 128), (2000, 128, 512), (150, 8192, 2048),
                                    (150, 2048, 8192), (37, 130, 96), (5, 16, 32),
-                                   (1200, 4096, 1024), (6000, 512, 2048)])
+                                   (1200, 4096, 1024), (6000, 512, 2048),
+                                   (999, 112, 384), (1500, 48, 160)])
 def test_i8s_matmul_shapes(dev, m, n, k):
     x, w8, s = case(40 + k, m, n, k)
     ref = oracle.i8s_forward_ref(x, w8, s)
