@@ -469,6 +469,40 @@ def test_grouped_fused_decode_layers(dev, fused):
 
 
 @pytest.mark.parametrize("fused", [False, True])
+def test_grouped_new_activations_each_launch(dev, fused):
+    """How a decoder uses a plan: built once, then each step writes new
+    activations into the same buffers and launches it again. Four launches,
+    every output poisoned before each and checked against the oracle for that
+    step's rows; the third step's first projection gets an all-zero row (d = 0,
+    q = 0) between live ones, so no launch may lean on what an earlier one left."""
+    cases = [synth.decode_problem(layer, proj, m) for layer, m in ((0, 1), (27, 3))
+             for proj in range(4)]
+    items, _ = _grouped_items(cases, dev, fused)
+    plan = bt.MatmulPlan(items)
+    for step in range(4):
+        refs = []
+        for i, (c, it) in enumerate(zip(cases, items)):
+            m, k = c["x"].shape
+            rng = np.random.default_rng(1000 * step + i)
+            x = rng.standard_normal((m, k)).astype(np.float32)
+            if step == 2 and i == 0:
+                x[0] = 0.0
+            it["y"].fill_(float("nan"))
+            it["acc"].fill_(POISON_I32)
+            if fused:
+                it["x"].copy_(to_dev(x, dev))
+                it["xq"].fill_(99)
+                it["xscale"].fill_(float("nan"))
+                it["xsum"].fill_(POISON_I32)
+            else:
+                bt.quantize_act(to_dev(x, dev), it["xq"], it["xscale"], it["xsum"])
+            refs.append(oracle.forward_ref(x, c["w"], c["w_scale"], "f64"))
+        plan.launch()
+        torch.cuda.synchronize()
+        _check_grouped(items, refs)
+
+
+@pytest.mark.parametrize("fused", [False, True])
 def test_grouped_mixed_m_with_lds_split(dev, fused):
     # M = 16 rows of K = 8960 do not fit one LDS slice, so that projection is
     # split along K inside the grouped launch and uses the plan's workspace
