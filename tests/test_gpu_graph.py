@@ -3,7 +3,8 @@ exactly the eager results (the kernels take the caller's stream and issue no
 memset, allocation or host synchronization, so they are capturable).
 
 Each replay is preceded by eager work on the same buffers (outputs poisoned
-with NaN, an eager launch into other buffers) and a synchronization.
+with NaN, an eager launch into other buffers) and a synchronization. The last
+replays follow new activations written into the captured input buffers.
 """
 
 import numpy as np
@@ -114,3 +115,25 @@ def test_graph_replays_match_eager(dev):
         for i, (a, b) in enumerate(zip(got, eager)):
             assert torch.equal(a.view(torch.uint8) if a.dtype == torch.float32 else a,
                                b.view(torch.uint8) if b.dtype == torch.float32 else b), (rep, i)
+
+    # New activations written into the captured input buffers: a replay must
+    # follow them, as a decoder's step-by-step replays do. The eager launches
+    # on the same new inputs give the expected bytes.
+    def same(a, b):
+        return torch.equal(a.view(torch.uint8) if a.dtype == torch.float32 else a,
+                           b.view(torch.uint8) if b.dtype == torch.float32 else b)
+
+    rng = np.random.default_rng(23)
+    for rep in range(2):
+        for x in xs + [gm_x]:
+            x.copy_(torch.from_numpy(rng.standard_normal(tuple(x.shape)).astype(np.float32)))
+        work()
+        want = snapshot()
+        poison()
+        torch.cuda.synchronize()
+        g.replay()
+        got = snapshot()
+        for i, (a, b) in enumerate(zip(got, want)):
+            assert same(a, b), ("new inputs", rep, i)
+        # the decode outputs did change with the inputs
+        assert not same(want[3], eager[3]) and not same(want[-4], eager[-4])
