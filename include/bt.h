@@ -42,7 +42,8 @@ extern "C" {
 typedef enum bt_status {
     BT_OK = 0,
     BT_ERR_NULL = 1,       /* a required pointer is NULL                            */
-    BT_ERR_SHAPE = 2,      /* M, N or K < 1, K % 128 != 0, or a size that overflows */
+    BT_ERR_SHAPE = 2,      /* M, N or K < 1, K % 128 != 0, K > BT_MAX_K, or a size
+                              that overflows                                         */
     BT_ERR_VALUE = 3,      /* a weight outside {-1,0,1}, a 2-bit code 3, a bad scale */
     BT_ERR_ALIGN = 4,      /* a device pointer not 16-byte aligned                   */
     BT_ERR_DEVICE = 5,     /* the HIP runtime reported an error                      */
@@ -54,6 +55,11 @@ typedef enum bt_status {
 #define BT_GROUP_K 128
 /* Largest token count served by the GEMV path; larger M uses the MFMA GEMM. */
 #define BT_GEMV_MAX_M 16
+/* Largest K of the ternary format and matmul (a multiple of BT_GROUP_K).
+ * |acc| <= 127 * K then stays below 2^24: every accumulator is exact in int32
+ * and converts to fp32 exactly, and the kernels' 32-bit buffer offsets (128
+ * token rows of K int8 per tile) cannot wrap. Larger K is BT_ERR_SHAPE. */
+#define BT_MAX_K 131072
 
 /* Human-readable name of a status code (static string, never NULL). */
 const char* bt_status_string(bt_status status);
@@ -68,7 +74,8 @@ const char* bt_status_string(bt_status status);
  * the elements 128g + 32s + b at bits 2s..2s+1, s = 0..3.
  * ------------------------------------------------------------------------- */
 
-/* N*K/4 (one eighth of the FP16 matrix), or 0 if N < 1, K < 1 or K % 128 != 0. */
+/* N*K/4 (one eighth of the FP16 matrix), or 0 if N < 1, K < 1, K % 128 != 0 or
+ * K > BT_MAX_K. */
 size_t bt_packed_bytes(int64_t N, int64_t K);
 
 /* Pack w (host, N x K int8, values in {-1,0,1}) into packed (host, N*K/4 bytes).

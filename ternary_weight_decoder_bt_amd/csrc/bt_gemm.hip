@@ -736,14 +736,9 @@ void gemm_persistent_kernel(GemmArgs g) {
     wait_vmcnt<0>();
 }
 
-#ifndef BT_GEMM_GROUPED
-#define BT_GEMM_GROUPED 1
-#endif
-
 // Token-row bands per tile group: as many as one XCD's share of the tiles
 // spans, so that share is one compact block of the output.
 int32_t gemm_group_m(int32_t m_tiles, int32_t n_tiles, int64_t tiles_per_xcd) {
-    if (!BT_GEMM_GROUPED) return 1;
     const int64_t gm = bt::ceil_div(tiles_per_xcd, n_tiles);
     return int32_t(std::max<int64_t>(1, std::min<int64_t>(m_tiles, gm)));
 }
@@ -772,35 +767,23 @@ bt_status launch_gemm(GemmArgs g, hipStream_t stream) {
     return hipGetLastError() == hipSuccess ? BT_OK : BT_ERR_DEVICE;
 }
 
-#ifndef BT_GEMM_PERSISTENT
-#define BT_GEMM_PERSISTENT 1
-#endif
-#ifndef BT_GEMM_P_WA
-#define BT_GEMM_P_WA 128
-#endif
-#ifndef BT_GEMM_P_NW
-#define BT_GEMM_P_NW 4
-#endif
-#ifndef BT_GEMM_P_NS
-#define BT_GEMM_P_NS 3
-#endif
-#ifndef BT_GEMM_P_WGS_PER_CU
-#define BT_GEMM_P_WGS_PER_CU 2
-#endif
+// The persistent kernel's shape: waves of 128 tokens x 64 weight rows, four
+// side by side (tiles of 128 x 256), a 3-stage pipeline, two workgroups per
+// compute unit.
+constexpr int kPersistWA = 128;
+constexpr int kPersistNW = 4;
+constexpr int kPersistNS = 3;
+constexpr int kPersistWgsPerCu = 2;
 
-// Compute units of the current device, read once per device.
+// Compute units of the current device (queried on every call: the host keeps
+// no state between calls).
 int device_cus() {
-    static int cus[64] = {0};
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-    if (cus[dev] == 0) {
-        int n = 0;
-        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-            n <= 0)
-            n = 256;
-        cus[dev] = n;
-    }
-    return cus[dev];
+    int dev = 0, n = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        n <= 0)
+        return 256;
+    return n;
 }
 
 template <int WA, int WW, int NW, int KS, int NS>
@@ -815,7 +798,7 @@ bt_status launch_gemm_persistent(GemmArgs g, hipStream_t stream) {
     g.group_m = gemm_group_m(g.m_tiles, g.n_tiles, g.per_xcd);
     // one workgroup per resident slot, a multiple of the XCD count, and no
     // more than there are tiles in an XCD's band
-    const int64_t slots = int64_t(device_cus()) * BT_GEMM_P_WGS_PER_CU / kXcds;
+    const int64_t slots = int64_t(device_cus()) * kPersistWgsPerCu / kXcds;
     const int64_t per_xcd_wgs = std::max<int64_t>(1, std::min<int64_t>(slots, g.per_xcd));
     (void)hipGetLastError();
     hipLaunchKernelGGL((gemm_persistent_kernel<WA, WW, NW, KS, NS>),
@@ -1002,7 +985,7 @@ bt_status launch_i8_stream(GemmArgs g, hipStream_t stream) {
 bt_status dispatch_gemm(GemmArgs g, bool int8_weights, void* workspace, size_t workspace_bytes,
                         hipStream_t stream) {
     const bt::GemmChoice c =
-        bt::gemm_choice(g.M, g.N, g.K, int8_weights, BT_GEMM_PERSISTENT && !epi_any(g.epi));
+        bt::gemm_choice(g.M, g.N, g.K, int8_weights, !epi_any(g.epi));
     g.splits = 1;
     if (c.splits > 1) {
         const size_t need = bt::gemm_workspace_bytes(c, g.M, g.N);
@@ -1028,10 +1011,8 @@ bt_status dispatch_gemm(GemmArgs g, bool int8_weights, void* workspace, size_t w
         if (st == BT_OK && g.splits > 1) st = launch_splitk_reduce<true>(g, stream);
         return st;
     }
-#if BT_GEMM_PERSISTENT
     if (c.kind == 0)
-        return launch_gemm_persistent<BT_GEMM_P_WA, 64, BT_GEMM_P_NW, 128, BT_GEMM_P_NS>(g, stream);
-#endif
+        return launch_gemm_persistent<kPersistWA, 64, kPersistNW, 128, kPersistNS>(g, stream);
     st = c.kind == 3   ? launch_gemm<32, 32, 2, 2, 256, 2>(g, stream)
          : c.kind == 5 ? launch_gemm<64, 48, 2, 2, 256, 2>(g, stream)
          : c.kind == 2 ? launch_gemm<64, 64, 2, 2, 256, 2>(g, stream)

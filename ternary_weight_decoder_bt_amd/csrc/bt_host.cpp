@@ -16,7 +16,7 @@ extern "C" const char* bt_status_string(bt_status s) {
     switch (s) {
         case BT_OK: return "ok";
         case BT_ERR_NULL: return "a required pointer is NULL";
-        case BT_ERR_SHAPE: return "invalid shape (M, N, K >= 1 and K % 128 == 0 required)";
+        case BT_ERR_SHAPE: return "invalid shape (M, N, K >= 1, K % 128 == 0 and K <= 131072 required)";
         case BT_ERR_VALUE: return "invalid value (weight outside {-1,0,1}, code 3, or non-finite scale)";
         case BT_ERR_ALIGN: return "device pointer not 16-byte aligned";
         case BT_ERR_DEVICE: return "HIP runtime error";
@@ -28,7 +28,7 @@ extern "C" const char* bt_status_string(bt_status s) {
 static bool valid_nk(int64_t N, int64_t K) {
     if (N < 1 || K < 1 || K % BT_GROUP_K) return false;
     // every byte count and int32 index the kernels form must fit
-    if (N > (int64_t(1) << 30) || K > (int64_t(1) << 30)) return false;
+    if (N > (int64_t(1) << 30) || K > bt::kMaxK) return false;
     const int64_t padded = ceil_div(N, bt::kTileN) * bt::kTileN;
     return padded <= std::numeric_limits<int64_t>::max() / (K + bt::kSuperK);
 }

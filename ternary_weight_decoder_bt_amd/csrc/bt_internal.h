@@ -22,21 +22,18 @@ constexpr uint32_t kPlanMagicRepack = 0x4254504bu;      // "KPTB"
 
 inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
+// Largest K of the ternary matmul: |acc| <= 127 * K stays below 2^24, so
+// every accumulator is exact in int32 and converts to fp32 exactly, and every
+// byte offset the kernels form inside one tile's buffer (at most 128 rows of
+// K int8, or 4 * K weight bytes per 16-row tile) fits their 32-bit offsets.
+constexpr int64_t kMaxK = BT_MAX_K;
+
 // GEMV tuning: weight steps (1 KB per wave) loaded per batch, and the LDS
 // slice that holds one workgroup's int8 activations (M rows x its K range).
-#ifndef BT_GEMV_BATCH
-#define BT_GEMV_BATCH 6
-#endif
-#ifndef BT_GEMV_NONTEMPORAL
-#define BT_GEMV_NONTEMPORAL 1
-#endif
-#ifndef BT_GEMV_TILES_PER_WAVE
-#define BT_GEMV_TILES_PER_WAVE 2
-#endif
-constexpr int kGemvBatch = BT_GEMV_BATCH;
+constexpr int kGemvBatch = 6;
 constexpr int kGemvLdsBytes = 40960;
 constexpr int kGemvFillWaves = 1024;   // waves that keep every compute unit streaming
-constexpr int kGemvGroupedTilesPerWave = BT_GEMV_TILES_PER_WAVE;
+constexpr int kGemvGroupedTilesPerWave = 2;
 
 // Epilogue on the fp32 output (all optional): bias add, ReLU, per-output
 // layer scale, residual add, in that order.

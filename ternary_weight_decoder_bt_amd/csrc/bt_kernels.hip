@@ -101,10 +101,7 @@ __device__ __forceinline__ void repack_store(const RepackIn& in, uint8_t* __rest
     *reinterpret_cast<uint4*>(out + blk * 1024 + lane * 16) = uint4{w[0], w[1], w[2], w[3]};
 }
 
-#ifndef BT_REPACK_PER_WAVE
-#define BT_REPACK_PER_WAVE 8
-#endif
-constexpr int kRepackPerWave = BT_REPACK_PER_WAVE;   // output blocks a wave handles per pass
+constexpr int kRepackPerWave = 8;   // output blocks a wave handles per pass
 
 __global__ __launch_bounds__(256) void repack_kernel(const uint8_t* __restrict__ packed, int32_t N,
                                                      int32_t K, int32_t steps, int64_t blocks,
@@ -557,11 +554,7 @@ __device__ __forceinline__ void gemv_issue(GemvBatch& b, const uint8_t* wt, int 
 #pragma unroll
     for (int u = 0; u < kB; ++u) {
         const int st = min(sb + u, last);
-#if BT_GEMV_NONTEMPORAL
         b.w[u] = gld_stream<v4u>(wt + int64_t(st) * 1024 + lane * 16);
-#else
-        b.w[u] = gld<v4u>(wt + int64_t(st) * 1024 + lane * 16);
-#endif
     }
 }
 

@@ -246,6 +246,42 @@ def test_device_entry_points_validate_before_launch():
     assert L.bt_ternary_matmul_fused(*fa(M=16, N=1536, K=8960)) == WORKSPACE
 
 
+def test_k_bound_of_the_ternary_path():
+    """K is capped at BT_MAX_K = 131072: |acc| <= 127 K stays below 2^24 (exact in
+    int32 and in fp32), and the kernels' 32-bit offsets over 128 token rows of K
+    bytes cannot wrap. Beyond it every size query is 0 and every call BT_ERR_SHAPE."""
+    L = bt.lib()
+    f = FAKE
+    kmax = 131072
+    assert 127 * kmax < 2 ** 24
+    assert 128 * (kmax + 128) < 2 ** 31
+    assert L.bt_packed_bytes(16, kmax) == 16 * kmax // 4
+    assert L.bt_repacked_bytes(16, kmax) == 16 * kmax // 4
+    for k in (kmax + 128, 1 << 24, 1 << 30):
+        assert L.bt_packed_bytes(16, k) == 0
+        assert L.bt_repacked_bytes(16, k) == 0
+        assert L.bt_matmul_workspace_bytes(1, 16, k) == 0
+        assert L.bt_matmul_workspace_bytes(4096, 16, k) == 0
+        assert L.bt_repack_ternary(f, 16, k, f, None) == SHAPE
+        for m in (1, 16, 17, 4096):
+            assert L.bt_ternary_matmul(m, 16, k, f, f, f, f, 0.5, f, None, f, 1 << 40,
+                                       None) == SHAPE
+            assert L.bt_ternary_matmul_epilogue(m, 16, k, f, f, f, f, 0.5, None, f, None, f,
+                                                1 << 40, None) == SHAPE
+        assert L.bt_ternary_matmul_fused(1, 16, k, f, f, 0.5, f, None, None, None, None, f,
+                                         1 << 40, None) == SHAPE
+        d = (BtMatmulDesc * 1)(BtMatmulDesc(1, 16, k, f, f, f, f, 0.5, f, None, None))
+        host = np.zeros(L.bt_matmul_plan_bytes(1), np.uint8)
+        assert L.bt_matmul_plan_build(d, 1, None, 0, host.ctypes.data, host.nbytes) == SHAPE
+        r = (BtRepackDesc * 1)(BtRepackDesc(f, f, 16, k))
+        host = np.zeros(L.bt_repack_plan_bytes(1), np.uint8)
+        assert L.bt_repack_plan_build(r, 1, host.ctypes.data, host.nbytes) == SHAPE
+    # the host format follows the same bound
+    w = np.zeros((1, kmax + 128), np.int8)
+    out = np.zeros((kmax + 128) // 4, np.uint8)
+    assert L.bt_pack_ternary(w.ctypes.data, 1, kmax + 128, out.ctypes.data) == SHAPE
+
+
 def test_plan_building_on_host():
     L = bt.lib()
     f = FAKE
