@@ -1169,13 +1169,14 @@ def main():
                           "copy_bytes_written_per_launch": dst.numel() * 4, "launches": 5}))
         return
 
+    # torch before the library: libbt.so binds to the HIP runtime torch loads
+    import torch
+
     packed_prefill = None
     if not args.no_prefill and not args.remainder_counters and not args.chain_only:
         t0 = time.time()
         packed_prefill = pack_long_prefill_weights(args.layers)
         log(f"long-prefill weights drawn and packed on the host in {time.time() - t0:.1f}s")
-
-    import torch
 
     import ternary_weight_decoder_bt_amd as bt
     bt.lib()

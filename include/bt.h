@@ -219,6 +219,25 @@ bt_status bt_ternary_matmul(int64_t M, int64_t N, int64_t K, const int8_t* xq,
                             float w_scale, float* y, int32_t* acc, void* workspace,
                             size_t workspace_bytes, hipStream_t stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * operation and arguments as bt_ternary_matmul without the workspace. Where
+ * the shape splits K, the partial sums go to a fixed array of
+ * BT_NOALLOC_SCRATCH_BYTES inside the library; every GPU the library runs on
+ * holds its own copy of it until the process ends, and its address is looked
+ * up (hipGetSymbolAddress, once per device) on the first call that needs it.
+ * The call itself allocates nothing (no hipMalloc, hipFree or allocating
+ * library routine). A shape whose bt_matmul_workspace_bytes(M,N,K) exceeds
+ * BT_NOALLOC_SCRATCH_BYTES returns BT_ERR_WORKSPACE before anything is
+ * launched. The array's contents on entry do not matter (each K range writes
+ * its whole slice before it is read), but all calls on one GPU share it:
+ * calls that may run at the same time on one GPU (unordered streams) race,
+ * so order them on one stream or with events. */
+#define BT_NOALLOC_SCRATCH_BYTES (16u << 20)
+bt_status bt_ternary_matmul_noalloc(int64_t M, int64_t N, int64_t K, const int8_t* xq,
+                                    const float* xscale, const int32_t* xsum, const void* wdev,
+                                    float w_scale, float* y, int32_t* acc, hipStream_t stream);
+
 /* The fused epilogues of the technical report's section 2.4.1 on the output
  * ("mul_mat_add_relu": matrix multiply + bias + ReLU; "add_scaled": residual
  * addition with layer-scale multiplication). With y the plain output above,

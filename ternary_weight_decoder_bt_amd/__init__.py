@@ -32,5 +32,6 @@ from .ops import (  # noqa: F401
     rmsnorm_quantize,
     ternary_matmul,
     ternary_matmul_fused,
+    ternary_matmul_noalloc,
     unpack_ternary,
 )

@@ -32,6 +32,7 @@ SIGNATURES = {
     "bt_rmsnorm_quantize": (C.c_int, [_p, _p, _f, _i64, _i64, _p, _p, _p, _p]),
     "bt_matmul_workspace_bytes": (_sz, [_i64, _i64, _i64]),
     "bt_ternary_matmul": (C.c_int, [_i64, _i64, _i64, _p, _p, _p, _p, _f, _p, _p, _p, _sz, _p]),
+    "bt_ternary_matmul_noalloc": (C.c_int, [_i64, _i64, _i64, _p, _p, _p, _p, _f, _p, _p, _p]),
     "bt_ternary_matmul_epilogue": (C.c_int, [_i64, _i64, _i64, _p, _p, _p, _p, _f, _p, _p, _p,
                                              _p, _sz, _p]),
     "bt_ternary_matmul_fused": (C.c_int, [_i64, _i64, _i64, _p, _p, _f, _p, _p, _p, _p, _p, _p,
@@ -94,6 +95,11 @@ def lib() -> C.CDLL:
             raise ImportError(
                 f"{LIB_PATH} is not built; build it with `python -c \"import __graft_entry__ as g; "
                 "g.build()\"` (hipcc, gfx950). There is no fallback implementation.")
+        # libbt.so needs libamdhip64.so.7, which torch also ships. Loading torch
+        # first makes the library bind to the HIP runtime torch's streams and
+        # memory come from; loaded the other way round, a process would carry two
+        # runtimes and every launch on a torch stream would fail.
+        import torch  # noqa: F401
         handle = C.CDLL(LIB_PATH)
         for name, (res, args) in SIGNATURES.items():
             fn = getattr(handle, name)

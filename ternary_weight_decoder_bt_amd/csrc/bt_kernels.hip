@@ -34,6 +34,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <mutex>
 #include <type_traits>
 
 #include "bt_device.h"
@@ -1107,16 +1108,25 @@ static bt_status epilogue_args(const bt_epilogue* epi, int64_t M, int64_t N, con
     return BT_OK;
 }
 
-static bt_status matmul_impl(int64_t M, int64_t N, int64_t K, const int8_t* xq,
-                             const float* xscale, const int32_t* xsum, const void* wdev,
-                             float w_scale, const bt_epilogue* epi, float* y, int32_t* acc,
-                             void* workspace, size_t workspace_bytes, hipStream_t stream) {
+// Argument checks of bt_ternary_matmul (everything but the workspace).
+static bt_status matmul_check(int64_t M, int64_t N, int64_t K, const int8_t* xq,
+                              const float* xscale, const int32_t* xsum, const void* wdev,
+                              float w_scale, const float* y, const int32_t* acc) {
     if (!xq || !xscale || !xsum || !wdev || !y) return BT_ERR_NULL;
     if (M < 1 || M > (int64_t(1) << 31) - 1 || !nk_ok(N, K)) return BT_ERR_SHAPE;
     if (!bt::aligned16(xq) || !bt::aligned16(xscale) || !bt::aligned16(xsum) ||
         !bt::aligned16(wdev) || !bt::aligned16(y) || (acc && !bt::aligned16(acc)))
         return BT_ERR_ALIGN;
     if (!isfinite(w_scale)) return BT_ERR_VALUE;
+    return BT_OK;
+}
+
+static bt_status matmul_impl(int64_t M, int64_t N, int64_t K, const int8_t* xq,
+                             const float* xscale, const int32_t* xsum, const void* wdev,
+                             float w_scale, const bt_epilogue* epi, float* y, int32_t* acc,
+                             void* workspace, size_t workspace_bytes, hipStream_t stream) {
+    const bt_status cst = matmul_check(M, N, K, xq, xscale, xsum, wdev, w_scale, y, acc);
+    if (cst != BT_OK) return cst;
     EpiArgs e;
     const bt_status est = epilogue_args(epi, M, N, y, &e);
     if (est != BT_OK) return est;
@@ -1174,6 +1184,66 @@ extern "C" bt_status bt_ternary_matmul_epilogue(int64_t M, int64_t N, int64_t K,
                                                 hipStream_t stream) {
     return matmul_impl(M, N, K, xq, xscale, xsum, wdev, w_scale, epi, y, acc, workspace,
                        workspace_bytes, stream);
+}
+
+// ------------------------------------------- allocation-free matmul entry point
+//
+// For callers that cannot allocate (code under graph capture, serving loops,
+// harnesses that forbid it): bt_ternary_matmul with the split-K workspace
+// taken from a fixed device array of this library instead of the caller.
+// Each GPU holds its own copy of the array (from the library's load until the
+// process ends); its address on a device is looked up once, with that device
+// current, and kept. Nothing in it has to start at zero: every K range writes
+// its whole partial-sum slice before the reduction launch reads it, so the
+// previous call's contents do no harm. Calls that overlap in time on one GPU
+// (different streams without ordering) share the array and race.
+constexpr size_t kScratchBytes = BT_NOALLOC_SCRATCH_BYTES;
+constexpr int kScratchDevices = 64;
+
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+namespace {
+
+struct ScratchSlot {
+    std::once_flag once;
+    void* ptr = nullptr;
+    hipError_t err = hipSuccess;
+};
+ScratchSlot scratch_slots[kScratchDevices];
+
+// The device address of `scratch` on the current device.
+bt_status scratch_address(void** out) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kScratchDevices)
+        return BT_ERR_DEVICE;
+    ScratchSlot& slot = scratch_slots[dev];
+    std::call_once(slot.once, [&slot] {
+        void* p = nullptr;
+        slot.err = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        slot.ptr = p;
+    });
+    if (slot.err != hipSuccess || !slot.ptr) return BT_ERR_DEVICE;
+    *out = slot.ptr;
+    return BT_OK;
+}
+
+}  // namespace
+
+extern "C" bt_status bt_ternary_matmul_noalloc(int64_t M, int64_t N, int64_t K, const int8_t* xq,
+                                               const float* xscale, const int32_t* xsum,
+                                               const void* wdev, float w_scale, float* y,
+                                               int32_t* acc, hipStream_t stream) {
+    const bt_status cst = matmul_check(M, N, K, xq, xscale, xsum, wdev, w_scale, y, acc);
+    if (cst != BT_OK) return cst;
+    const size_t need = bt_matmul_workspace_bytes(M, N, K);
+    if (need > kScratchBytes) return BT_ERR_WORKSPACE;
+    void* ws = nullptr;
+    if (need) {
+        const bt_status st = scratch_address(&ws);
+        if (st != BT_OK) return st;
+    }
+    return matmul_impl(M, N, K, xq, xscale, xsum, wdev, w_scale, nullptr, y, acc, ws,
+                       ws ? kScratchBytes : 0, stream);
 }
 
 // ------------------------------------------------------------------ I8_S

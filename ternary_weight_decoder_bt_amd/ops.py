@@ -227,6 +227,26 @@ def ternary_matmul(xq, xscale, xsum, wdev, n: int, w_scale: float, y=None, acc=N
     return (y, acc) if (want_acc or acc is not None) else y
 
 
+def ternary_matmul_noalloc(xq, xscale, xsum, wdev, n: int, w_scale: float, y, acc=None,
+                           stream=None):
+    """bt_ternary_matmul_noalloc: the same product with the split-K partial sums in
+    the library's own device array (no workspace argument, nothing allocated by the
+    call). y (and acc, if given) must be preallocated by the caller."""
+    torch = _torch()
+    _dev(xq, torch.int8, None, "xq")
+    m, k = xq.shape
+    _dev(xscale, torch.float32, (m,), "xscale")
+    _dev(xsum, torch.int32, (m,), "xsum")
+    _dev(wdev, torch.uint8, (repacked_bytes(n, k),), "wdev")
+    _dev(y, torch.float32, (m, n), "y")
+    if acc is not None:
+        _dev(acc, torch.int32, (m, n), "acc")
+    check(lib().bt_ternary_matmul_noalloc(m, n, k, _ptr(xq), _ptr(xscale), _ptr(xsum),
+                                          _ptr(wdev), float(w_scale), _ptr(y), _ptr(acc),
+                                          _stream(stream)), "bt_ternary_matmul_noalloc")
+    return (y, acc) if acc is not None else y
+
+
 def ternary_matmul_fused(x, wdev, n: int, w_scale: float, y=None, acc=None, xq=None,
                          xscale=None, xsum=None, workspace=None, want_acc=False, stream=None):
     """Quantize x and multiply in one launch (bt_ternary_matmul_fused, M <= 16).
@@ -416,6 +436,7 @@ class MatmulPlan(_Plan):
 __all__ = [
     "BtError", "GROUP_K", "GEMV_MAX_M", "packed_bytes", "repacked_bytes",
     "matmul_workspace_bytes", "int8_repacked_bytes", "repack_int8", "int8_matmul", "int8_matmul_workspace_bytes", "pack_ternary", "unpack_ternary", "repack_ternary",
-    "quantize_act", "rmsnorm_quantize", "new_workspace", "ternary_matmul", "ternary_matmul_fused", "RepackPlan",
+    "quantize_act", "rmsnorm_quantize", "new_workspace", "ternary_matmul", "ternary_matmul_noalloc",
+    "ternary_matmul_fused", "RepackPlan",
     "QuantPlan", "MatmulPlan",
 ]

@@ -282,6 +282,32 @@ def test_k_bound_of_the_ternary_path():
     assert L.bt_pack_ternary(w.ctypes.data, 1, kmax + 128, out.ctypes.data) == SHAPE
 
 
+def test_noalloc_entry_point_validates_before_launch():
+    """bt_ternary_matmul_noalloc: bt_ternary_matmul's checks, and BT_ERR_WORKSPACE for a
+    shape whose split-K partial sums would not fit the library's 16 MiB array (all
+    returned before any runtime call, so they run without a GPU)."""
+    L = bt.lib()
+    f = FAKE
+    na = lambda **kw: [kw.get("M", 1), kw.get("N", 16), kw.get("K", 128), kw.get("xq", f),
+                       kw.get("xs", f), kw.get("xsum", f), kw.get("w", f),
+                       kw.get("scale", 0.5), kw.get("y", f), kw.get("acc", None), None]
+    assert L.bt_ternary_matmul_noalloc(*na(xq=None)) == NULL
+    assert L.bt_ternary_matmul_noalloc(*na(xsum=None)) == NULL
+    assert L.bt_ternary_matmul_noalloc(*na(y=None)) == NULL
+    assert L.bt_ternary_matmul_noalloc(*na(K=130)) == SHAPE
+    assert L.bt_ternary_matmul_noalloc(*na(K=131072 + 128)) == SHAPE
+    assert L.bt_ternary_matmul_noalloc(*na(M=0)) == SHAPE
+    assert L.bt_ternary_matmul_noalloc(*na(w=f + 8)) == ALIGN
+    assert L.bt_ternary_matmul_noalloc(*na(acc=f + 4)) == ALIGN
+    assert L.bt_ternary_matmul_noalloc(*na(scale=float("nan"))) == VALUE
+    limit = 16 << 20
+    assert bt.matmul_workspace_bytes(2054, 1024, 8960) > limit
+    assert L.bt_ternary_matmul_noalloc(*na(M=2054, N=1024, K=8960)) == WORKSPACE
+    # the decoder's split shapes fit
+    for m, n, k in ((16, 1536, 8960), (512, 1536, 8960), (150, 1536, 8960)):
+        assert 0 < bt.matmul_workspace_bytes(m, n, k) <= limit
+
+
 def test_plan_building_on_host():
     L = bt.lib()
     f = FAKE
