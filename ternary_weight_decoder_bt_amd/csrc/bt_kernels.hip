@@ -659,21 +659,26 @@ __device__ __forceinline__ void gemv_finish(const GemvDesc& d, int64_t tile, v4i
 // token row (the row sum of q and the scale need all of it), keeps its own K
 // chunk in LDS, and the first workgroup of the problem also writes q, d and
 // the row sums out when asked to. The arithmetic is quantize_row's exactly.
-// Rows up to kFusedRegs*1024 elements are read once into registers; token 0
-// is read before the first weight loads go out, so its data is not queued
-// behind them. Longer rows are read twice (absmax, then quantize).
-constexpr int kFusedRegs = 2;   // float4 per thread: K <= 2048 in one read
+// Rows up to R*1024 elements (R float4 per thread) are read once into
+// registers; token 0 is read before the first weight loads go out, so its
+// data is not queued behind them (a wave's vector loads return in order).
+// Longer rows are read twice (absmax, then quantize). Grouped launches hold
+// R = 2 (K <= 2048); single calls take R = 9 for rows up to 9216 elements.
+constexpr int kFusedRegs = 2;       // grouped launches: K <= 2048 in one read
+constexpr int kFusedRegsLong = 9;   // single calls with 2048 < K <= 9216
 constexpr int kGemvThreads = 64 * bt::kGemvWaves;
 
+template <int R>
 struct FusedRow {
-    v4f v[kFusedRegs];
+    v4f v[R];
 };
 
-__device__ __forceinline__ void gemv_load_row(FusedRow& r, const GemvDesc& d, int m) {
+template <int R>
+__device__ __forceinline__ void gemv_load_row(FusedRow<R>& r, const GemvDesc& d, int m) {
     const int64_t K4 = d.K >> 2;
     const float* xr = d.x + int64_t(m) * d.K;
 #pragma unroll
-    for (int j = 0; j < kFusedRegs; ++j) {
+    for (int j = 0; j < R; ++j) {
         // clamped, branch-free: lanes past the row re-read its last float4
         // and their values are never used
         const int64_t i = min(int64_t(threadIdx.x) + int64_t(j) * kGemvThreads, K4 - 1);
@@ -694,7 +699,8 @@ __device__ __forceinline__ int gemv_quant_store(v4f v, float inv, int64_t k, int
 
 // One short row held in registers: a barrier joins the four wave maxima; the
 // row sum is left as four wave parts that the caller's barrier publishes.
-__device__ __forceinline__ void gemv_quant_short_row(const FusedRow& r, int m, const GemvDesc& d,
+template <int R>
+__device__ __forceinline__ void gemv_quant_short_row(const FusedRow<R>& r, int m, const GemvDesc& d,
                                                      bool writer, int64_t kbeg, int64_t kend,
                                                      int8_t* lds, GemvShared& sh) {
     const int tid = threadIdx.x;
@@ -702,7 +708,7 @@ __device__ __forceinline__ void gemv_quant_short_row(const FusedRow& r, int m, c
     const int64_t K4 = d.K >> 2;
     float amax = 0.0f;
 #pragma unroll
-    for (int j = 0; j < kFusedRegs; ++j) {
+    for (int j = 0; j < R; ++j) {
         const int64_t i = tid + int64_t(j) * kGemvThreads;
         if (i < K4)
             amax = fmaxf(amax, fmaxf(fmaxf(fabsf(r.v[j].x), fabsf(r.v[j].y)),
@@ -719,7 +725,7 @@ __device__ __forceinline__ void gemv_quant_short_row(const FusedRow& r, int m, c
     if (dead) inv = 0.0f;
     int s = 0;
 #pragma unroll
-    for (int j = 0; j < kFusedRegs; ++j) {
+    for (int j = 0; j < R; ++j) {
         const int64_t i = tid + int64_t(j) * kGemvThreads;
         if (i < K4) s += gemv_quant_store(r.v[j], inv, 4 * i, m, writer, d, kbeg, kend, lds);
     }
@@ -735,16 +741,17 @@ __device__ __forceinline__ void gemv_quant_short_row(const FusedRow& r, int m, c
 // All token rows. `r0` holds token 0 when the rows are short. Ends with the
 // barrier that publishes q, d and the row-sum parts; the writer then stores
 // the row sums.
-__device__ __forceinline__ void gemv_quantize_rows(const GemvDesc& d, const FusedRow& r0,
+template <int R>
+__device__ __forceinline__ void gemv_quantize_rows(const GemvDesc& d, const FusedRow<R>& r0,
                                                    bool writer, int64_t kbeg, int64_t kend,
                                                    int8_t* lds, GemvShared& sh) {
     const int tid = threadIdx.x;
     constexpr int T = kGemvThreads;
     const int64_t K4 = d.K >> 2;   // K % 128 == 0
-    if (K4 <= int64_t(kFusedRegs) * T) {
+    if (K4 <= int64_t(R) * T) {
         gemv_quant_short_row(r0, 0, d, writer, kbeg, kend, lds, sh);
         for (int m = 1; m < d.M; ++m) {
-            FusedRow r;
+            FusedRow<R> r;
             gemv_load_row(r, d, m);
             gemv_quant_short_row(r, m, d, writer, kbeg, kend, lds, sh);
         }
@@ -777,7 +784,14 @@ __device__ __forceinline__ void gemv_quantize_rows(const GemvDesc& d, const Fuse
     if (writer && d.xsum && tid < d.M) gst<int32_t>(d.xsum + tid, gemv_row_sum(sh, tid));
 }
 
-template <bool kFused, bool kWaveSplit>
+// Activation pieces (16 bytes of one token row) a thread of a single call
+// loads into registers before the weight loads go out: with the weights first,
+// every staging load would wait for them (in-order return) and each further
+// round of staging loads would add a round trip. Four cover a whole row of up
+// to 16384 elements.
+constexpr int kEarlyPieces = 4;
+
+template <bool kFused, bool kWaveSplit, int R>
 __device__ __forceinline__ void gemv_block(const GemvDesc& d, int64_t local_block, int8_t* lds,
                                            GemvShared& sh) {
     const int tid = threadIdx.x;
@@ -818,17 +832,40 @@ __device__ __forceinline__ void gemv_block(const GemvDesc& d, int64_t local_bloc
     // their latency overlaps the staging. Fused: token 0's activations go out
     // first, and the second batch waits until the rows are quantized (the
     // registers it needs hold the activations until then).
-    FusedRow r0;
-    if (kFused) gemv_load_row(r0, d, 0);
-    GemvBatch b0, b1;
-    issue(b0, 0);
-    if (!kFused) issue(b1, min(1, total - 1));
-
     // Stage this chunk of the M token rows in LDS rows 0..M-1 (zero past K)
     // and a zero row M, which the lanes of tokens >= M read instead.
     const int64_t kbeg = int64_t(s0) * bt::kSuperK;
     const int64_t kend = int64_t(s1) * bt::kSuperK;
     const int pieces = nsteps * (bt::kSuperK / 16);
+    const int real_pieces = d.M * pieces;
+    // single calls: the first pieces of the unfused activations go out before
+    // the weights (addresses clamped into the row, so the loads are
+    // unconditional; a piece past the rows or past K is stored as zero)
+    constexpr bool kEarly = kWaveSplit && !kFused;
+    v4i early[kEarly ? kEarlyPieces : 1];
+    float early_d = 0.0f;
+    int32_t early_qs = 0;
+    if constexpr (kEarly) {
+#pragma unroll
+        for (int j = 0; j < kEarlyPieces; ++j) {
+            const int i = min(tid + j * kGemvThreads, real_pieces - 1);
+            const int m = i / pieces;
+            const int64_t col = min(int64_t(i - m * pieces) * 16, int64_t(d.K) - kbeg - 16);
+            early[j] = gld<v4i>(d.xq + int64_t(m) * d.K + kbeg + col);
+        }
+        // the epilogue's per-token scale and row sum, too
+        early_d = gld<float>(d.xscale + min(tid, d.M - 1));
+        early_qs = gld<int32_t>(d.xsum + min(tid, d.M - 1));
+        // keep these loads ahead of the weights' (the compiler may not sink them)
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    FusedRow<R> r0;
+    if (kFused) gemv_load_row(r0, d, 0);
+    GemvBatch b0, b1;
+    issue(b0, 0);
+    if (!kFused) issue(b1, min(1, total - 1));
+    if constexpr (kEarly) __builtin_amdgcn_sched_barrier(0);
+
     if (kFused) {
         for (int i = tid; i < (d.M + 1) * pieces; i += 64 * bt::kGemvWaves) {
             const int m = i / pieces;
@@ -838,7 +875,24 @@ __device__ __forceinline__ void gemv_block(const GemvDesc& d, int64_t local_bloc
         gemv_quantize_rows(d, r0, chunk == 0 && g == 0, kbeg, kend, lds, sh);
         issue(b1, min(1, total - 1));
     } else {
-        for (int i = tid; i < (d.M + 1) * pieces; i += 64 * bt::kGemvWaves) {
+        int first = 0;
+        if constexpr (kEarly) {
+#pragma unroll
+            for (int j = 0; j < kEarlyPieces; ++j) {
+                const int i = tid + j * kGemvThreads;
+                if (i < real_pieces) {
+                    const int m = i / pieces;
+                    const int col = (i - m * pieces) * 16;
+                    lds_st<v4i>(lds + m * d.lds_row + col,
+                                kbeg + col < d.K ? early[j] : v4i{0, 0, 0, 0});
+                }
+            }
+            first = kEarlyPieces * kGemvThreads;
+            for (int i = tid; i < pieces; i += kGemvThreads)   // the zero row M
+                lds_st<v4i>(lds + d.M * d.lds_row + i * 16, v4i{0, 0, 0, 0});
+        }
+        const int staged = kEarly ? real_pieces : (d.M + 1) * pieces;
+        for (int i = first + tid; i < staged; i += kGemvThreads) {
             const int m = i / pieces;
             const int col = (i - m * pieces) * 16;
             v4i v = {0, 0, 0, 0};
@@ -847,8 +901,8 @@ __device__ __forceinline__ void gemv_block(const GemvDesc& d, int64_t local_bloc
         }
         // the epilogue's per-token scale and row sum, read once
         if (tid < d.M) {
-            sh.d[tid] = gld<float>(d.xscale + tid);
-            sh.qs[0][tid] = gld<int32_t>(d.xsum + tid);
+            sh.d[tid] = kEarly ? early_d : gld<float>(d.xscale + tid);
+            sh.qs[0][tid] = kEarly ? early_qs : gld<int32_t>(d.xsum + tid);
 #pragma unroll
             for (int w = 1; w < bt::kGemvWaves; ++w) sh.qs[w][tid] = 0;
         }
@@ -898,12 +952,13 @@ __device__ __forceinline__ void gemv_block(const GemvDesc& d, int64_t local_bloc
     }
 }
 
-// Single calls: waves_per_tile may split a tile's K range over the workgroup.
-template <bool kFused>
-__global__ __launch_bounds__(64 * bt::kGemvWaves) __attribute__((amdgpu_waves_per_eu(4))) void gemv_kernel(GemvDesc d) {
+// Single calls: waves_per_tile may split a tile's K range over the workgroup;
+// R float4 per thread hold a fused call's token row.
+template <bool kFused, int R = kFusedRegs>
+__global__ __launch_bounds__(64 * bt::kGemvWaves) __attribute__((amdgpu_waves_per_eu(R > kFusedRegs ? 2 : 4))) void gemv_kernel(GemvDesc d) {
     extern __shared__ __attribute__((aligned(16))) int8_t gemv_lds[];
     __shared__ GemvShared sh;
-    gemv_block<kFused, true>(d, blockIdx.x, gemv_lds, sh);
+    gemv_block<kFused, true, R>(d, blockIdx.x, gemv_lds, sh);
 }
 
 template <bool kFused>
@@ -918,7 +973,7 @@ __global__ __launch_bounds__(64 * bt::kGemvWaves) __attribute__((amdgpu_waves_pe
         if (descs[mid].block_begin <= b) lo = mid; else hi = mid - 1;
     }
     const GemvDesc d = descs[lo];
-    gemv_block<kFused, false>(d, b - d.block_begin, gemv_lds, sh);
+    gemv_block<kFused, false, kFusedRegs>(d, b - d.block_begin, gemv_lds, sh);
 }
 
 size_t gemv_lds_bytes(const GemvDesc& d) {
@@ -1079,8 +1134,12 @@ extern "C" bt_status bt_ternary_matmul_fused(int64_t M, int64_t N, int64_t K, co
         if (!d.xsum) d.xsum = reinterpret_cast<int32_t*>(scratch + 4 * M);
     }
     (void)hipGetLastError();
-    hipLaunchKernelGGL(gemv_kernel<true>, dim3(unsigned(d.blocks)), dim3(64 * bt::kGemvWaves),
-                       gemv_lds_bytes(d), stream, d);
+    if (K > 4 * kFusedRegs * kGemvThreads && K <= 4 * kFusedRegsLong * kGemvThreads)
+        hipLaunchKernelGGL((gemv_kernel<true, kFusedRegsLong>), dim3(unsigned(d.blocks)),
+                           dim3(64 * bt::kGemvWaves), gemv_lds_bytes(d), stream, d);
+    else
+        hipLaunchKernelGGL((gemv_kernel<true, kFusedRegs>), dim3(unsigned(d.blocks)),
+                           dim3(64 * bt::kGemvWaves), gemv_lds_bytes(d), stream, d);
     const bt_status st2 = launched();
     if (st2 != BT_OK || d.chunks <= 1) return st2;
     return gemv_reduce(d, stream);
