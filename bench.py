@@ -351,6 +351,40 @@ class LongPrefill:
         log(f"long prefill ready: {len(self.probs)} projections, M={m}, "
             f"setup {time.time() - t0:.1f}s")
 
+    def build_grouped(self):
+        """The same stack as two grouped launches: one quantization plan over the
+        112 inputs, one GEMM plan over the 112 projections (each projection's
+        workgroups walk its own output tiles), into separate output buffers."""
+        torch, bt = self.torch, self.bt
+        self.gitems = []
+        for p in self.probs:
+            m, k, n = self.m, p["k"], p["n"]
+            self.gitems.append({
+                "x": p["x"], "xq": torch.empty((m, k), dtype=torch.int8, device=p["x"].device),
+                "xscale": torch.empty(m, dtype=torch.float32, device=p["x"].device),
+                "xsum": torch.empty(m, dtype=torch.int32, device=p["x"].device),
+                "y": torch.empty((m, n), dtype=torch.float32, device=p["x"].device),
+                "wdev": p["wdev"], "n": n, "w_scale": p["s"]})
+        self.gqplan = bt.QuantPlan([(g["x"], g["xq"], g["xscale"], g["xsum"])
+                                    for g in self.gitems])
+        self.ggplan = bt.MatmulPlan([{k_: g[k_] for k_ in ("xq", "xscale", "xsum", "y", "wdev",
+                                                          "n", "w_scale")}
+                                     for g in self.gitems])
+
+    def step_grouped(self):
+        self.gqplan.launch()
+        self.ggplan.launch()
+
+    def grouped_matches(self):
+        """Every output of the grouped stack equals the per-projection stack's bit for
+        bit (q, d, row sums and y; compared on the GPU)."""
+        torch = self.torch
+        ok = True
+        for p, g in zip(self.probs, self.gitems):
+            ok &= bool(torch.equal(p["xq"], g["xq"]) and torch.equal(p["xs"], g["xscale"]) and
+                       torch.equal(p["xsum"], g["xsum"]) and torch.equal(p["y"], g["y"]))
+        return ok
+
     def step(self):
         bt = self.bt
         for p in self.probs:
@@ -1389,6 +1423,30 @@ def main():
         gemm_ms = g0.elapsed_time(g1) / args.prefill_steps
         tops = lp.ops / (ms * 1e-3) / 1e12
         gemm_tops = lp.ops / (gemm_ms * 1e-3) / 1e12
+        # the grouped stack: one quantization launch, one GEMM launch
+        lp.build_grouped()
+        g_gstack = capture_graph(torch, lp.step_grouped)
+        g_ggemm = capture_graph(torch, lp.ggplan.launch)
+        for g_ in lp.gitems:
+            g_["y"].fill_(float("nan"))
+        g_gstack.replay()
+        torch.cuda.synchronize()
+        grouped_ok = lp.grouped_matches()
+        times = {}
+        for name, gr in (("stack", g_gstack), ("gemm", g_ggemm), ("per_projection_stack", g_stack)):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            a.record()
+            for i in range(args.prefill_steps):
+                gr.replay()
+            b.record()
+            torch.cuda.synchronize()
+            times[name] = a.elapsed_time(b) / args.prefill_steps
+        g_ms, gg_ms = times["stack"], times["gemm"]
+        log(f"prefill grouped: {g_ms:.3f} ms/stack ({lp.ops / (g_ms * 1e-3) / 1e12:.0f} TOPS), "
+            f"GEMM launch {gg_ms:.3f} ms ({lp.ops / (gg_ms * 1e-3) / 1e12:.0f} TOPS); "
+            f"matches per-projection: {grouped_ok}")
+        del g_gstack, g_ggemm
         shapes = lp.time_shapes()
         prologues = lp.time_activation_prologues()
         epilogues = lp.time_epilogues()
@@ -1409,6 +1467,18 @@ def main():
                               "4 columns of each (every output of all 112 projections is "
                               "compared by tests/test_gpu_long_prefill_full.py)",
             "steps": args.prefill_steps,
+            "grouped": {
+                "workload": "the same stack as one grouped quantization launch over the 112 "
+                            "inputs and one grouped GEMM launch over the 112 projections (the "
+                            "projections are independent here, as in the grouped decode step)",
+                "ms_per_stack": round(g_ms, 4), "tops": round(lp.ops / (g_ms * 1e-3) / 1e12, 2),
+                "pct_of_int8_peak": round(100 * lp.ops / (g_ms * 1e-3) / 1e12 / I8_PEAK_TOPS, 2),
+                "gemm_ms": round(gg_ms, 4),
+                "gemm_tops": round(lp.ops / (gg_ms * 1e-3) / 1e12, 2),
+                "gemm_pct_of_int8_peak": round(100 * lp.ops / (gg_ms * 1e-3) / 1e12 /
+                                               I8_PEAK_TOPS, 2),
+                "matches_per_projection_bitwise": grouped_ok,
+                "per_projection_ms_same_trial": round(times["per_projection_stack"], 4)},
             "gemm_tops_per_shape": {k: round(v[1], 1) for k, v in shapes.items()},
             "gemm_us_per_shape": {k: round(v[0] * 1e3, 2) for k, v in shapes.items()},
             "gemm_epilogues": {k: {"us": round(v[0] * 1e3, 2), "tops": round(v[1], 1)}

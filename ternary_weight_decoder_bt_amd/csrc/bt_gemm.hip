@@ -41,7 +41,7 @@ namespace {
 
 using bt::GemmArgs;
 
-constexpr int kXcds = 8;
+using bt::kXcds;
 
 // Scheduling hint for the code just before it: interleave its kLoads vector
 // loads with the MFMAs, one load followed by G MFMAs (the LDS copies and the
@@ -503,9 +503,14 @@ void gemm_kernel(GemmArgs g) {
 // of one tile overlaps the loads of the next. Stages per tile are padded to a
 // multiple of NS with stages that read zeros (a buffer's range check turns
 // their loads into no-ops), which keeps every stage's wait count constant.
+//
+// The body serves two launches: one problem over the whole grid
+// (gemm_persistent_kernel), or many independent problems in one grid
+// (gemm_persistent_grouped_kernel), where each problem owns `per_wg`
+// workgroup slots in every XCD and a workgroup walks only its problem's tiles.
+// `slot` is the workgroup's slot among its problem's slots of one XCD.
 template <int WA, int WW, int NW, int KS, int NS>
-__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
-void gemm_persistent_kernel(GemmArgs g) {
+__device__ __forceinline__ void gemm_persistent_body(const GemmArgs& g, int slot, int per_wg) {
     constexpr int BM = WA;
     constexpr int BN = WW * NW;
     constexpr int TA = WA / 16;
@@ -540,11 +545,10 @@ void gemm_persistent_kernel(GemmArgs g) {
 
     // this workgroup's tiles: first, first + per_wg, ... below hi
     const int xcd = blockIdx.x % kXcds;
-    const int per_wg = int(gridDim.x) / kXcds;
     const int total = g.m_tiles * g.n_tiles;
     const int lo = xcd * g.per_xcd;
     const int hi = min(lo + g.per_xcd, total);
-    const int first = lo + int(blockIdx.x) / kXcds;
+    const int first = lo + slot;
     if (first >= hi) return;
     const int count = (hi - first + per_wg - 1) / per_wg;
 
@@ -736,11 +740,30 @@ void gemm_persistent_kernel(GemmArgs g) {
     wait_vmcnt<0>();
 }
 
-// Token-row bands per tile group: as many as one XCD's share of the tiles
-// spans, so that share is one compact block of the output.
-int32_t gemm_group_m(int32_t m_tiles, int32_t n_tiles, int64_t tiles_per_xcd) {
-    const int64_t gm = bt::ceil_div(tiles_per_xcd, n_tiles);
-    return int32_t(std::max<int64_t>(1, std::min<int64_t>(m_tiles, gm)));
+template <int WA, int WW, int NW, int KS, int NS>
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void gemm_persistent_kernel(GemmArgs g) {
+    gemm_persistent_body<WA, WW, NW, KS, NS>(g, int(blockIdx.x) / kXcds,
+                                             int(gridDim.x) / kXcds);
+}
+
+// Many problems in one launch: the problem owning slot blockIdx.x / 8 (one
+// lane per descriptor compares its first slot, a ballot counts them), then
+// that problem's persistent walk. Descriptors are ordered by first slot.
+template <int WA, int WW, int NW, int KS, int NS>
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void gemm_persistent_grouped_kernel(const GemmArgs* __restrict__ descs, int32_t count) {
+    const int slot = int(blockIdx.x) / kXcds;
+    const int lane = threadIdx.x & 63;
+    int p = -1;
+    for (int base = 0; base < count; base += 64) {
+        const int i = base + lane;
+        const int begin = i < count ? descs[i].slot_begin : INT32_MAX;
+        p += int(__popcll(__ballot(begin <= slot)));
+    }
+    p = __builtin_amdgcn_readfirstlane(p);
+    const GemmArgs g = descs[p];
+    gemm_persistent_body<WA, WW, NW, KS, NS>(g, slot - g.slot_begin, g.slots);
 }
 
 // Launch of the tiled GEMM for one tile shape (the shape itself is chosen on
@@ -758,7 +781,7 @@ bt_status launch_gemm(GemmArgs g, hipStream_t stream) {
     }
     const int64_t total = int64_t(g.m_tiles) * g.n_tiles * g.splits;
     g.per_xcd = int32_t(bt::ceil_div(total, kXcds));
-    g.group_m = gemm_group_m(g.m_tiles, g.n_tiles, bt::ceil_div(g.per_xcd, g.splits));
+    g.group_m = bt::gemm_group_m(g.m_tiles, g.n_tiles, bt::ceil_div(g.per_xcd, g.splits));
     const int64_t grid = int64_t(g.per_xcd) * kXcds;
     if (grid > (int64_t(1) << 31) - 1) return BT_ERR_SHAPE;
     (void)hipGetLastError();
@@ -770,8 +793,8 @@ bt_status launch_gemm(GemmArgs g, hipStream_t stream) {
 // The persistent kernel's shape: waves of 128 tokens x 64 weight rows, four
 // side by side (tiles of 128 x 256), a 3-stage pipeline, two workgroups per
 // compute unit.
-constexpr int kPersistWA = 128;
-constexpr int kPersistNW = 4;
+constexpr int kPersistWA = bt::kPersistBM;
+constexpr int kPersistNW = bt::kPersistBN / 64;
 constexpr int kPersistNS = 3;
 constexpr int kPersistWgsPerCu = 2;
 
@@ -795,7 +818,7 @@ bt_status launch_gemm_persistent(GemmArgs g, hipStream_t stream) {
     const int64_t total = int64_t(g.m_tiles) * g.n_tiles;
     if (total > (int64_t(1) << 31) - 1) return BT_ERR_SHAPE;
     g.per_xcd = int32_t(bt::ceil_div(total, kXcds));
-    g.group_m = gemm_group_m(g.m_tiles, g.n_tiles, g.per_xcd);
+    g.group_m = bt::gemm_group_m(g.m_tiles, g.n_tiles, g.per_xcd);
     // one workgroup per resident slot, a multiple of the XCD count, and no
     // more than there are tiles in an XCD's band
     const int64_t slots = int64_t(device_cus()) * kPersistWgsPerCu / kXcds;
@@ -803,6 +826,20 @@ bt_status launch_gemm_persistent(GemmArgs g, hipStream_t stream) {
     (void)hipGetLastError();
     hipLaunchKernelGGL((gemm_persistent_kernel<WA, WW, NW, KS, NS>),
                        dim3(unsigned(per_xcd_wgs * kXcds)), dim3(64 * NW), 0, stream, g);
+    return hipGetLastError() == hipSuccess ? BT_OK : BT_ERR_DEVICE;
+}
+
+// A grouped GEMM plan (bt_matmul_plan_build with M > 16): the host copy sizes
+// the grid (every problem's slots, in every XCD), the device copy feeds the
+// kernel.
+bt_status launch_gemm_grouped(const bt::PlanHeader* hdr, const GemmArgs* dev_descs,
+                              hipStream_t stream) {
+    const int64_t grid = hdr->total_blocks * kXcds;
+    if (grid < 1 || grid > (int64_t(1) << 31) - 1) return BT_ERR_SHAPE;
+    (void)hipGetLastError();
+    hipLaunchKernelGGL((gemm_persistent_grouped_kernel<kPersistWA, 64, kPersistNW, 128, kPersistNS>),
+                       dim3(unsigned(grid)), dim3(64 * kPersistNW), 0, stream, dev_descs,
+                       hdr->count);
     return hipGetLastError() == hipSuccess ? BT_OK : BT_ERR_DEVICE;
 }
 
@@ -1032,6 +1069,12 @@ bt_status gemm_dispatch(GemmArgs g, bool int8_weights, void* workspace, size_t w
 
 bt_status gemm_reduce_slices(const GemmArgs& g, hipStream_t stream) {
     return launch_splitk_reduce<false>(g, stream);
+}
+
+bt_status gemm_grouped_launch(const PlanHeader* hdr, const void* plan_dev, hipStream_t stream) {
+    const auto* descs = reinterpret_cast<const GemmArgs*>(static_cast<const char*>(plan_dev) +
+                                                          sizeof(PlanHeader));
+    return launch_gemm_grouped(hdr, descs, stream);
 }
 
 }  // namespace bt

@@ -278,7 +278,6 @@ extern "C" bt_status bt_quant_plan_build(const bt_quant_desc* descs, int32_t cou
     if (plan_bytes < bt_quant_plan_bytes(count)) return BT_ERR_WORKSPACE;
     auto* hdr = static_cast<bt::PlanHeader*>(plan_host);
     auto* out = reinterpret_cast<bt::QuantDesc*>(hdr + 1);
-    int64_t rows = 0;
     for (int32_t i = 0; i < count; ++i) {
         const bt_quant_desc& q = descs[i];
         if (!q.x || !q.xq || !q.xscale || !q.xsum) return BT_ERR_NULL;
@@ -288,21 +287,100 @@ extern "C" bt_status bt_quant_plan_build(const bt_quant_desc* descs, int32_t cou
             !bt::aligned16(q.xsum))
             return BT_ERR_ALIGN;
     }
+    int64_t blocks = 0;
     for (int32_t i = 0; i < count; ++i) {
         const bt_quant_desc& q = descs[i];
-        out[i] = bt::QuantDesc{q.x, q.xq, q.xscale, q.xsum, q.M, q.K, rows};
-        rows += q.M;
+        out[i] = bt::QuantDesc{q.x, q.xq, q.xscale, q.xsum, q.M, q.K, blocks};
+        blocks += bt::quant_wave_rows(q.K) ? ceil_div(q.M, bt::kQuantThreads / 64) : q.M;
     }
-    if (rows > int64_t(1) << 31) return BT_ERR_SHAPE;
+    if (blocks > (int64_t(1) << 31) - 1) return BT_ERR_SHAPE;
     hdr->magic = bt::kPlanMagicQuant;
     hdr->count = count;
-    hdr->total_blocks = rows;
+    hdr->total_blocks = blocks;
     return BT_OK;
 }
+
+static_assert(sizeof(bt::GemmArgs) <= sizeof(bt::GemvDesc), "a plan entry holds either kind");
 
 extern "C" size_t bt_matmul_plan_bytes(int32_t count) {
     if (count < 1) return 0;
     return sizeof(bt::PlanHeader) + size_t(count) * sizeof(bt::GemvDesc);
+}
+
+// A projection of a grouped GEMM plan (M > BT_GEMV_MAX_M): quantized inputs
+// only (quantization is not fused into the GEMM).
+static bt_status check_gemm_desc(const bt_matmul_desc& m) {
+    if (!m.wdev || !m.y || !m.xq || !m.xscale || !m.xsum) return BT_ERR_NULL;
+    if (m.M <= BT_GEMV_MAX_M || m.M > (int64_t(1) << 31) - 1 || !valid_nk(m.N, m.K))
+        return BT_ERR_SHAPE;
+    if (!bt::aligned16(m.xq) || !bt::aligned16(m.xscale) || !bt::aligned16(m.xsum) ||
+        !bt::aligned16(m.wdev) || !bt::aligned16(m.y) || (m.acc && !bt::aligned16(m.acc)))
+        return BT_ERR_ALIGN;
+    if (m.x) return BT_ERR_VALUE;
+    if (!std::isfinite(m.w_scale)) return BT_ERR_VALUE;
+    return BT_OK;
+}
+
+// Grouped GEMM plan: every projection runs the persistent GEMM's walk over its
+// own 128 x 256 output tiles on workgroup slots of its own, in every XCD.
+// The slots of one XCD are shared out in proportion to each projection's work
+// (tiles x 128-wide K stages), at least one each and no more than it has
+// tiles in one XCD, over max(64, 2P) slots per XCD for P projections (beyond
+// the 64 resident ones the dispatcher starts them as earlier ones finish).
+// Projections whose workgroups walk the longest runs come first in the grid.
+static bt_status build_gemm_plan(const bt_matmul_desc* descs, int32_t count, void* plan_host) {
+    auto* hdr = static_cast<bt::PlanHeader*>(plan_host);
+    auto* out = reinterpret_cast<bt::GemmArgs*>(hdr + 1);
+    double total_work = 0.0;
+    for (int32_t i = 0; i < count; ++i) {
+        const bt_matmul_desc& m = descs[i];
+        bt::GemmArgs g;
+        memset(&g, 0, sizeof(g));
+        g.xq = m.xq;
+        g.xscale = m.xscale;
+        g.xsum = m.xsum;
+        g.w = static_cast<const uint8_t*>(m.wdev);
+        g.y = m.y;
+        g.acc = m.acc;
+        g.w_scale = m.w_scale;
+        g.M = int32_t(m.M);
+        g.N = int32_t(m.N);
+        g.K = int32_t(m.K);
+        g.tiles = int32_t(ceil_div(m.N, bt::kTileN));
+        g.steps = int32_t(ceil_div(m.K, bt::kSuperK));
+        g.m_tiles = int32_t(ceil_div(m.M, bt::kPersistBM));
+        g.n_tiles = int32_t(ceil_div(m.N, bt::kPersistBN));
+        const int64_t tiles = int64_t(g.m_tiles) * g.n_tiles;
+        if (tiles > (int64_t(1) << 31) - 1) return BT_ERR_SHAPE;
+        g.per_xcd = int32_t(ceil_div(tiles, bt::kXcds));
+        g.group_m = bt::gemm_group_m(g.m_tiles, g.n_tiles, g.per_xcd);
+        g.splits = 1;
+        g.sps = int32_t(ceil_div(m.K, 128));
+        total_work += double(tiles) * double(g.sps);
+        out[i] = g;
+    }
+    const int64_t slots_xcd = std::max<int64_t>(bt::kSlotsPerXcd, 2 * int64_t(count));
+    for (int32_t i = 0; i < count; ++i) {
+        bt::GemmArgs& g = out[i];
+        const double work = double(int64_t(g.m_tiles) * g.n_tiles) * double(g.sps);
+        const int64_t want = int64_t(double(slots_xcd) * work / total_work + 0.5);
+        g.slots = int32_t(std::max<int64_t>(1, std::min<int64_t>(want, g.per_xcd)));
+    }
+    // longest walk per workgroup first
+    std::stable_sort(out, out + count, [](const bt::GemmArgs& a, const bt::GemmArgs& b) {
+        return int64_t(ceil_div(a.per_xcd, a.slots)) * a.sps >
+               int64_t(ceil_div(b.per_xcd, b.slots)) * b.sps;
+    });
+    int64_t slot = 0;
+    for (int32_t i = 0; i < count; ++i) {
+        out[i].slot_begin = int32_t(slot);
+        slot += out[i].slots;
+    }
+    if (slot * bt::kXcds > (int64_t(1) << 31) - 1) return BT_ERR_SHAPE;
+    hdr->magic = bt::kPlanMagicGemm;
+    hdr->count = count;
+    hdr->total_blocks = slot;   // slots per XCD; the grid is 8 x this
+    return BT_OK;
 }
 
 static bt_status check_matmul_desc(const bt_matmul_desc& m, bool fused) {
@@ -336,6 +414,14 @@ extern "C" bt_status bt_matmul_plan_build(const bt_matmul_desc* descs, int32_t c
     if (!descs || !plan_host) return BT_ERR_NULL;
     if (count < 1) return BT_ERR_SHAPE;
     if (plan_bytes < bt_matmul_plan_bytes(count)) return BT_ERR_WORKSPACE;
+    if (descs[0].M > BT_GEMV_MAX_M) {
+        // a GEMM plan: every projection has M > BT_GEMV_MAX_M
+        for (int32_t i = 0; i < count; ++i) {
+            const bt_status st = check_gemm_desc(descs[i]);
+            if (st != BT_OK) return st;
+        }
+        return build_gemm_plan(descs, count, plan_host);
+    }
     const bool fused = descs[0].x != nullptr;
     for (int32_t i = 0; i < count; ++i) {
         if ((descs[i].x != nullptr) != fused) return BT_ERR_VALUE;   // all fused or none

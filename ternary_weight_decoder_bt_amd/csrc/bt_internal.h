@@ -19,6 +19,7 @@ constexpr uint32_t kPlanMagicQuant = 0x42545141u;   // "AQTB"
 constexpr uint32_t kPlanMagicGemv = 0x42544d47u;    // "GMTB"
 constexpr uint32_t kPlanMagicGemvFused = 0x42544646u;   // "FFTB"
 constexpr uint32_t kPlanMagicRepack = 0x4254504bu;      // "KPTB"
+constexpr uint32_t kPlanMagicGemm = 0x42544d4du;        // "MMTB"
 
 inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
@@ -63,6 +64,8 @@ struct GemmArgs {
     int32_t splits, sps;    // K ranges per tile and stages per range (1, all: no split)
     int32_t* ws;            // split K: one M x N int32 slice of partial sums per range
     int64_t ws_slice;       // int32 elements from one slice to the next
+    int32_t slots;          // grouped persistent launch: this problem's workgroups per XCD
+    int32_t slot_begin;     // and the first of them (workgroup id / 8)
 };
 
 struct GemvDesc {
@@ -100,8 +103,12 @@ struct QuantDesc {
     float* xscale;
     int32_t* xsum;
     int64_t M, K;
-    int64_t row_begin;      // first workgroup (= row) of this problem in a grouped launch
+    int64_t row_begin;      // first workgroup of this problem in a grouped launch
 };
+
+// Quantization of rows short enough for one wave each (the row in registers,
+// four rows per 256-thread workgroup); longer rows take a workgroup each.
+constexpr bool quant_wave_rows(int64_t K) { return K % 4 == 0 && K <= 2048; }
 
 struct RepackDesc {
     const uint8_t* packed;
@@ -155,11 +162,28 @@ inline size_t gemm_slice_bytes(int64_t M, int64_t N) {
 
 inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
+// The persistent GEMM's output tiles (kPersistBM token rows x kPersistBN
+// weight rows), the XCDs a launch spreads them over, and the resident
+// workgroup slots of one XCD (two per compute unit, 32 compute units).
+constexpr int kPersistBM = 128;
+constexpr int kPersistBN = 256;
+constexpr int kXcds = 8;
+constexpr int kSlotsPerXcd = kGemmSlots / kXcds;
+
+// Token-row bands per tile group of the GEMM's tile order: as many as one
+// XCD's share of the tiles spans, so that share is one compact block.
+inline int32_t gemm_group_m(int32_t m_tiles, int32_t n_tiles, int64_t tiles_per_xcd) {
+    const int64_t gm = ceil_div(tiles_per_xcd, n_tiles);
+    return int32_t(gm < 1 ? 1 : gm > m_tiles ? m_tiles : gm);
+}
+
 // bt_gemm.hip: the prefill GEMM for M > 16 (shape dispatch, split K and its
 // reduction launch), and that reduction alone for a split single-call GEMV
 // (same slice layout).
 bt_status gemm_dispatch(GemmArgs g, bool int8_weights, void* workspace, size_t workspace_bytes,
                         hipStream_t stream);
 bt_status gemm_reduce_slices(const GemmArgs& g, hipStream_t stream);
+// A grouped GEMM plan's launch (plan_dev: the plan's device copy).
+bt_status gemm_grouped_launch(const PlanHeader* hdr, const void* plan_dev, hipStream_t stream);
 
 }  // namespace bt

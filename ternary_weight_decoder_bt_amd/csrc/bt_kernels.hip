@@ -310,12 +310,12 @@ __global__ __launch_bounds__(bt::kQuantThreads) void quantize_kernel(const float
 // only (no LDS, no barrier). Same arithmetic as quantize_row.
 constexpr int kWaveRowRegs = 8;   // float4 per lane: K <= 64 * 8 * 4 = 2048
 
-__global__ __launch_bounds__(bt::kQuantThreads) void quantize_wave_rows_kernel(
-    const float* __restrict__ x, int64_t M, int64_t K, int8_t* __restrict__ xq,
-    float* __restrict__ xscale, int32_t* __restrict__ xsum) {
+// Row m quantized by one wave (K % 4 == 0, K <= 2048).
+__device__ __forceinline__ void quantize_wave_row(const float* __restrict__ x, int64_t K,
+                                                  int64_t m, int8_t* __restrict__ xq,
+                                                  float* __restrict__ xscale,
+                                                  int32_t* __restrict__ xsum) {
     const int lane = threadIdx.x & 63;
-    const int64_t m = int64_t(blockIdx.x) * (bt::kQuantThreads / 64) + (threadIdx.x >> 6);
-    if (m >= M) return;
     const int64_t K4 = K >> 2;
     const float* xr = x + m * K;
     v4f v[kWaveRowRegs];
@@ -348,6 +348,14 @@ __global__ __launch_bounds__(bt::kQuantThreads) void quantize_wave_rows_kernel(
         gst<float>(xscale + m, dead ? 0.0f : amax / 127.0f);
         if (xsum) gst<int32_t>(xsum + m, s);
     }
+}
+
+__global__ __launch_bounds__(bt::kQuantThreads) void quantize_wave_rows_kernel(
+    const float* __restrict__ x, int64_t M, int64_t K, int8_t* __restrict__ xq,
+    float* __restrict__ xscale, int32_t* __restrict__ xsum) {
+    const int64_t m = int64_t(blockIdx.x) * (bt::kQuantThreads / 64) + (threadIdx.x >> 6);
+    if (m >= M) return;
+    quantize_wave_row(x, K, m, xq, xscale, xsum);
 }
 
 // ----------------------------------- RMS normalization fused with quantization
@@ -515,18 +523,31 @@ __global__ __launch_bounds__(bt::kQuantThreads) void rmsnorm_quantize_kernel(
     }
 }
 
+// Many quantizations in one launch. A workgroup finds its problem with one
+// lane per descriptor (first workgroups compared at once, counted with a
+// ballot), then quantizes four rows, one per wave, where the rows are short
+// (K % 4 == 0, K <= 2048), else one row with the whole workgroup.
 __global__ __launch_bounds__(bt::kQuantThreads) void quantize_grouped_kernel(
     const QuantDesc* __restrict__ descs, int32_t count) {
     __shared__ QuantShared sh;
     const int64_t b = blockIdx.x;
-    int lo = 0, hi = count - 1;
-    while (lo < hi) {
-        const int mid = (lo + hi + 1) >> 1;
-        if (descs[mid].row_begin <= b) lo = mid; else hi = mid - 1;
+    const int lane = threadIdx.x & 63;
+    int p = -1;
+    for (int base = 0; base < count; base += 64) {
+        const int i = base + lane;
+        const int64_t begin = i < count ? descs[i].row_begin : INT64_MAX;
+        p += int(__popcll(__ballot(begin <= b)));
     }
-    const QuantDesc d = descs[lo];
-    const int64_t m = b - d.row_begin;
-    quantize_row(d.x + m * d.K, d.K, d.xq + m * d.K, d.xscale + m, d.xsum + m, sh);
+    p = __builtin_amdgcn_readfirstlane(p);
+    const QuantDesc d = descs[p];
+    const int64_t local = b - d.row_begin;
+    if (bt::quant_wave_rows(d.K)) {
+        const int64_t m = local * (bt::kQuantThreads / 64) + (threadIdx.x >> 6);
+        if (m < d.M) quantize_wave_row(d.x, d.K, m, d.xq, d.xscale, d.xsum);
+        return;
+    }
+    quantize_row(d.x + local * d.K, d.K, d.xq + local * d.K, d.xscale + local,
+                 d.xsum + local, sh);
 }
 
 // -------------------------------------------------------------------- GEMV
@@ -1371,6 +1392,10 @@ extern "C" bt_status bt_ternary_matmul_grouped(const void* plan_host, const void
                                                hipStream_t stream) {
     if (!plan_host || !plan_dev) return BT_ERR_NULL;
     const auto* hdr = static_cast<const bt::PlanHeader*>(plan_host);
+    if (hdr->magic == bt::kPlanMagicGemm && hdr->count >= 1) {
+        if (!bt::aligned16(plan_dev)) return BT_ERR_ALIGN;
+        return bt::gemm_grouped_launch(hdr, plan_dev, stream);
+    }
     const bool fused = hdr->magic == bt::kPlanMagicGemvFused;
     if ((!fused && hdr->magic != bt::kPlanMagicGemv) || hdr->count < 1) return BT_ERR_VALUE;
     if (!bt::aligned16(plan_dev)) return BT_ERR_ALIGN;

@@ -316,7 +316,7 @@ def test_plan_building_on_host():
     host = np.zeros(nb, np.uint8)
     assert L.bt_quant_plan_build(q, 2, host.ctypes.data, nb) == OK
     hdr = host[:16].view(np.int64)
-    assert hdr[1] == 4                                  # total rows = workgroups
+    assert hdr[1] == 2          # workgroups: 3 short rows (one per wave) + 1 long row
     assert L.bt_quant_plan_build(q, 2, host.ctypes.data, nb - 1) == WORKSPACE
     q[1].xsum = None
     assert L.bt_quant_plan_build(q, 2, host.ctypes.data, nb) == NULL
@@ -353,6 +353,45 @@ def test_plan_building_on_host():
     assert first_k == 8960
     # a launch with a plan of the wrong kind is refused on the host
     assert L.bt_quantize_act_grouped(host.ctypes.data, f, None) == VALUE
+
+
+def test_gemm_plan_building_on_host():
+    """Descriptors with M > 16 build a grouped GEMM plan: quantized inputs only,
+    no workspace, every descriptor on the same side of BT_GEMV_MAX_M; workgroup
+    slots shared out by work (tiles x 128-wide K stages), longest walks first."""
+    L = bt.lib()
+    f = FAKE
+    # one decoder layer at M=4096: qkv, o, gate_up (K=1536) and down (K=8960)
+    shapes = [(2048, 1536), (1536, 1536), (17920, 1536), (1536, 8960)]
+    m = (BtMatmulDesc * 4)(*[BtMatmulDesc(4096, n, k, f, f, f, f, 0.02, f, None, None)
+                             for n, k in shapes])
+    nb = L.bt_matmul_plan_bytes(4)
+    host = np.zeros(nb, np.uint8)
+    assert L.bt_matmul_plan_workspace_bytes(m, 4) == 0
+    assert L.bt_matmul_plan_build(m, 4, None, 0, host.ctypes.data, nb) == OK
+    assert host[:4].view(np.uint32)[0] == 0x42544D4D          # a GEMM plan
+    tiles = [32 * -(-n // 256) for n, _ in shapes]             # 128 x 256 output tiles
+    work = [t * k // 128 for t, (_, k) in zip(tiles, shapes)]
+    slots = host[8:16].view(np.int64)[0]                        # slots per XCD in the grid
+    want = [max(1, min(round(64 * w / sum(work)), -(-t // 8))) for w, t in zip(work, tiles)]
+    assert slots == sum(want)
+    # a launch with a GEMM plan is refused by the quantize launcher
+    assert L.bt_quantize_act_grouped(host.ctypes.data, f, None) == VALUE
+    # mixing GEMV (M <= 16) and GEMM projections, fused inputs, missing inputs
+    m[1].M = 16
+    assert L.bt_matmul_plan_build(m, 4, None, 0, host.ctypes.data, nb) == SHAPE
+    m[1].M = 4096
+    m[2].x = f
+    assert L.bt_matmul_plan_build(m, 4, None, 0, host.ctypes.data, nb) == VALUE
+    m[2].x = None
+    m[3].xsum = None
+    assert L.bt_matmul_plan_build(m, 4, None, 0, host.ctypes.data, nb) == NULL
+    m[3].xsum = f
+    m[3].y = f + 4
+    assert L.bt_matmul_plan_build(m, 4, None, 0, host.ctypes.data, nb) == ALIGN
+    m[3].y = f
+    m[0].K = 131072 + 128
+    assert L.bt_matmul_plan_build(m, 4, None, 0, host.ctypes.data, nb) == SHAPE
 
 
 def test_repack_plan_building_on_host():
