@@ -322,16 +322,20 @@ static bt_status check_gemm_desc(const bt_matmul_desc& m) {
 }
 
 // Grouped GEMM plan: every projection runs the persistent GEMM's walk over its
-// own 128 x 256 output tiles on workgroup slots of its own, in every XCD.
-// The slots of one XCD are shared out in proportion to each projection's work
-// (tiles x 128-wide K stages), at least one each and no more than it has
-// tiles in one XCD, over max(64, 2P) slots per XCD for P projections (beyond
-// the 64 resident ones the dispatcher starts them as earlier ones finish).
-// Projections whose workgroups walk the longest runs come first in the grid.
+// own 128 x 256 output tiles with as many workgroups per XCD as its single
+// launch would use (the 64 resident slots of an XCD, or fewer when it has
+// fewer tiles there), one projection after another in the grid: the
+// dispatcher starts a projection's workgroups as the previous one's finish,
+// so the XCDs' resident workgroups mostly share one projection's activation
+// rows in their L2, and no launch ends in a tail. Projections with the same K
+// run back to back (stable sort by K). Measured on MI355X, long prefill M=4096
+// (28 layers x 4 projections, separate activations): 5.23 ms per stack as 112
+// single launches, 4.60 ms grouped in decoder order, 4.43 ms grouped by K;
+// slots shared out in proportion to work, with every projection resident at
+// once, took 5.46 ms (the activation rows of many projections thrash the L2).
 static bt_status build_gemm_plan(const bt_matmul_desc* descs, int32_t count, void* plan_host) {
     auto* hdr = static_cast<bt::PlanHeader*>(plan_host);
     auto* out = reinterpret_cast<bt::GemmArgs*>(hdr + 1);
-    double total_work = 0.0;
     for (int32_t i = 0; i < count; ++i) {
         const bt_matmul_desc& m = descs[i];
         bt::GemmArgs g;
@@ -356,21 +360,11 @@ static bt_status build_gemm_plan(const bt_matmul_desc* descs, int32_t count, voi
         g.group_m = bt::gemm_group_m(g.m_tiles, g.n_tiles, g.per_xcd);
         g.splits = 1;
         g.sps = int32_t(ceil_div(m.K, 128));
-        total_work += double(tiles) * double(g.sps);
+        g.slots = int32_t(std::min<int64_t>(bt::kSlotsPerXcd, g.per_xcd));
         out[i] = g;
     }
-    const int64_t slots_xcd = std::max<int64_t>(bt::kSlotsPerXcd, 2 * int64_t(count));
-    for (int32_t i = 0; i < count; ++i) {
-        bt::GemmArgs& g = out[i];
-        const double work = double(int64_t(g.m_tiles) * g.n_tiles) * double(g.sps);
-        const int64_t want = int64_t(double(slots_xcd) * work / total_work + 0.5);
-        g.slots = int32_t(std::max<int64_t>(1, std::min<int64_t>(want, g.per_xcd)));
-    }
-    // longest walk per workgroup first
-    std::stable_sort(out, out + count, [](const bt::GemmArgs& a, const bt::GemmArgs& b) {
-        return int64_t(ceil_div(a.per_xcd, a.slots)) * a.sps >
-               int64_t(ceil_div(b.per_xcd, b.slots)) * b.sps;
-    });
+    std::stable_sort(out, out + count,
+                     [](const bt::GemmArgs& a, const bt::GemmArgs& b) { return a.K < b.K; });
     int64_t slot = 0;
     for (int32_t i = 0; i < count; ++i) {
         out[i].slot_begin = int32_t(slot);

@@ -357,8 +357,9 @@ def test_plan_building_on_host():
 
 def test_gemm_plan_building_on_host():
     """Descriptors with M > 16 build a grouped GEMM plan: quantized inputs only,
-    no workspace, every descriptor on the same side of BT_GEMV_MAX_M; workgroup
-    slots shared out by work (tiles x 128-wide K stages), longest walks first."""
+    no workspace, every descriptor on the same side of BT_GEMV_MAX_M; each
+    projection gets min(64, its tiles per XCD) workgroup slots per XCD, and the
+    projections are ordered by K (stable)."""
     L = bt.lib()
     f = FAKE
     # one decoder layer at M=4096: qkv, o, gate_up (K=1536) and down (K=8960)
@@ -371,10 +372,11 @@ def test_gemm_plan_building_on_host():
     assert L.bt_matmul_plan_build(m, 4, None, 0, host.ctypes.data, nb) == OK
     assert host[:4].view(np.uint32)[0] == 0x42544D4D          # a GEMM plan
     tiles = [32 * -(-n // 256) for n, _ in shapes]             # 128 x 256 output tiles
-    work = [t * k // 128 for t, (_, k) in zip(tiles, shapes)]
     slots = host[8:16].view(np.int64)[0]                        # slots per XCD in the grid
-    want = [max(1, min(round(64 * w / sum(work)), -(-t // 8))) for w, t in zip(work, tiles)]
-    assert slots == sum(want)
+    assert slots == sum(min(64, -(-t // 8)) for t in tiles) == 32 + 24 + 64 + 24
+    # GemmArgs: 6 pointers, w_scale, then M, N, K (K at byte 60); K=8960 comes last
+    ks = [host[16 + 152 * i + 60:16 + 152 * i + 64].view(np.int32)[0] for i in range(4)]
+    assert ks == [1536, 1536, 1536, 8960]
     # a launch with a GEMM plan is refused by the quantize launcher
     assert L.bt_quantize_act_grouped(host.ctypes.data, f, None) == VALUE
     # mixing GEMV (M <= 16) and GEMM projections, fused inputs, missing inputs
