@@ -777,20 +777,41 @@ __device__ __forceinline__ void gemv_quantize_rows(const GemvDesc& d, const Fuse
             gemv_quant_short_row(r, m, d, writer, kbeg, kend, lds, sh);
         }
     } else {
+        // Long rows, read twice (absmax, then quantize), kLongBatch float4 per
+        // thread in flight at a time: loads at clamped indices, unconditional,
+        // so each batch costs one round trip rather than one per float4.
+        constexpr int kLongBatch = 4;
         for (int m = 0; m < d.M; ++m) {
             const float* xr = d.x + int64_t(m) * d.K;
             float amax = 0.0f;
-            for (int64_t i = tid; i < K4; i += T) {
-                const v4f v = gld<v4f>(xr + 4 * i);
-                amax = fmaxf(amax, fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w))));
+            for (int64_t i0 = tid; i0 < K4; i0 += int64_t(kLongBatch) * T) {
+                v4f v[kLongBatch];
+#pragma unroll
+                for (int u = 0; u < kLongBatch; ++u)
+                    v[u] = gld<v4f>(xr + 4 * min(i0 + int64_t(u) * T, K4 - 1));
+#pragma unroll
+                for (int u = 0; u < kLongBatch; ++u)
+                    if (i0 + int64_t(u) * T < K4)
+                        amax = fmaxf(amax, fmaxf(fmaxf(fabsf(v[u].x), fabsf(v[u].y)),
+                                                 fmaxf(fabsf(v[u].z), fabsf(v[u].w))));
             }
             amax = block_max(amax, sh.red);
             float inv = 127.0f / amax;
             const bool dead = !(inv <= FLT_MAX);
             if (dead) inv = 0.0f;
             int s = 0;
-            for (int64_t i = tid; i < K4; i += T)
-                s += gemv_quant_store(gld<v4f>(xr + 4 * i), inv, 4 * i, m, writer, d, kbeg, kend, lds);
+            for (int64_t i0 = tid; i0 < K4; i0 += int64_t(kLongBatch) * T) {
+                v4f v[kLongBatch];
+#pragma unroll
+                for (int u = 0; u < kLongBatch; ++u)
+                    v[u] = gld<v4f>(xr + 4 * min(i0 + int64_t(u) * T, K4 - 1));
+#pragma unroll
+                for (int u = 0; u < kLongBatch; ++u) {
+                    const int64_t i = i0 + int64_t(u) * T;
+                    if (i < K4)
+                        s += gemv_quant_store(v[u], inv, 4 * i, m, writer, d, kbeg, kend, lds);
+                }
+            }
             s = block_sum(s, sh.red);
             if (tid < bt::kGemvWaves) sh.qs[tid][m] = tid == 0 ? s : 0;
             if (tid == 0) {
