@@ -318,7 +318,18 @@ static bt_status check_gemm_desc(const bt_matmul_desc& m) {
         return BT_ERR_ALIGN;
     if (m.x) return BT_ERR_VALUE;
     if (!std::isfinite(m.w_scale)) return BT_ERR_VALUE;
+    // output tiles and this projection's workgroups must fit the kernel's int32 indexes
+    const int64_t tiles = ceil_div(m.M, bt::kPersistBM) * ceil_div(m.N, bt::kPersistBN);
+    if (tiles > (int64_t(1) << 31) - 1) return BT_ERR_SHAPE;
     return BT_OK;
+}
+
+// Workgroup slots per XCD a projection of a grouped GEMM plan takes: as many as
+// its single launch would use (the resident slots of an XCD, or fewer when it
+// has fewer tiles there).
+static int64_t gemm_plan_slots(const bt_matmul_desc& m) {
+    const int64_t tiles = ceil_div(m.M, bt::kPersistBM) * ceil_div(m.N, bt::kPersistBN);
+    return std::min<int64_t>(bt::kSlotsPerXcd, ceil_div(tiles, bt::kXcds));
 }
 
 // Grouped GEMM plan: every projection runs the persistent GEMM's walk over its
@@ -334,6 +345,7 @@ static bt_status check_gemm_desc(const bt_matmul_desc& m) {
 // slots shared out in proportion to work, with every projection resident at
 // once, took 5.46 ms (the activation rows of many projections thrash the L2).
 static bt_status build_gemm_plan(const bt_matmul_desc* descs, int32_t count, void* plan_host) {
+    // descriptors already checked (check_gemm_desc), total slots within range
     auto* hdr = static_cast<bt::PlanHeader*>(plan_host);
     auto* out = reinterpret_cast<bt::GemmArgs*>(hdr + 1);
     for (int32_t i = 0; i < count; ++i) {
@@ -355,12 +367,11 @@ static bt_status build_gemm_plan(const bt_matmul_desc* descs, int32_t count, voi
         g.m_tiles = int32_t(ceil_div(m.M, bt::kPersistBM));
         g.n_tiles = int32_t(ceil_div(m.N, bt::kPersistBN));
         const int64_t tiles = int64_t(g.m_tiles) * g.n_tiles;
-        if (tiles > (int64_t(1) << 31) - 1) return BT_ERR_SHAPE;
         g.per_xcd = int32_t(ceil_div(tiles, bt::kXcds));
         g.group_m = bt::gemm_group_m(g.m_tiles, g.n_tiles, g.per_xcd);
         g.splits = 1;
         g.sps = int32_t(ceil_div(m.K, 128));
-        g.slots = int32_t(std::min<int64_t>(bt::kSlotsPerXcd, g.per_xcd));
+        g.slots = int32_t(gemm_plan_slots(m));
         out[i] = g;
     }
     std::stable_sort(out, out + count,
@@ -370,7 +381,6 @@ static bt_status build_gemm_plan(const bt_matmul_desc* descs, int32_t count, voi
         out[i].slot_begin = int32_t(slot);
         slot += out[i].slots;
     }
-    if (slot * bt::kXcds > (int64_t(1) << 31) - 1) return BT_ERR_SHAPE;
     hdr->magic = bt::kPlanMagicGemm;
     hdr->count = count;
     hdr->total_blocks = slot;   // slots per XCD; the grid is 8 x this
@@ -409,11 +419,15 @@ extern "C" bt_status bt_matmul_plan_build(const bt_matmul_desc* descs, int32_t c
     if (count < 1) return BT_ERR_SHAPE;
     if (plan_bytes < bt_matmul_plan_bytes(count)) return BT_ERR_WORKSPACE;
     if (descs[0].M > BT_GEMV_MAX_M) {
-        // a GEMM plan: every projection has M > BT_GEMV_MAX_M
+        // a GEMM plan: every projection has M > BT_GEMV_MAX_M; everything is
+        // checked before the plan is written
+        int64_t slots = 0;
         for (int32_t i = 0; i < count; ++i) {
             const bt_status st = check_gemm_desc(descs[i]);
             if (st != BT_OK) return st;
+            slots += gemm_plan_slots(descs[i]);
         }
+        if (slots * bt::kXcds > (int64_t(1) << 31) - 1) return BT_ERR_SHAPE;
         return build_gemm_plan(descs, count, plan_host);
     }
     const bool fused = descs[0].x != nullptr;

@@ -394,6 +394,11 @@ def test_gemm_plan_building_on_host():
     m[3].y = f
     m[0].K = 131072 + 128
     assert L.bt_matmul_plan_build(m, 4, None, 0, host.ctypes.data, nb) == SHAPE
+    # more output tiles than the kernel's int32 indexes hold; the plan is left unwritten
+    m[0].K, m[0].M, m[0].N = 1536, (1 << 31) - 1, 1 << 30
+    host[:] = 0
+    assert L.bt_matmul_plan_build(m, 4, None, 0, host.ctypes.data, nb) == SHAPE
+    assert not host.any()
 
 
 def test_repack_plan_building_on_host():
