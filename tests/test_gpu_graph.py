@@ -137,3 +137,51 @@ def test_graph_replays_match_eager(dev):
             assert same(a, b), ("new inputs", rep, i)
         # the decode outputs did change with the inputs
         assert not same(want[3], eager[3]) and not same(want[-4], eager[-4])
+
+
+def test_graph_grouped_prefill_and_noalloc(dev):
+    """A grouped prefill (grouped quantization, grouped GEMM plan over ragged
+    projections with different K) and the allocation-free matmul on a split
+    shape, captured once: every replay, after eager work and a poisoning of
+    the outputs, equals the eager launches byte for byte."""
+    shapes = [(600, 2048, 1536), (300, 1536, 8960), (129, 130, 384)]
+    cases = [synth.small_problem(30 + i, m, n, k, "t3") for i, (m, n, k) in enumerate(shapes)]
+    ws = [_weights(c, dev) for c in cases]
+    xs = [torch.from_numpy(c["x"]).to(dev) for c in cases]
+    outs = [{"xq": torch.empty(c["x"].shape, dtype=torch.int8, device=dev),
+             "xscale": torch.empty(c["x"].shape[0], dtype=torch.float32, device=dev),
+             "xsum": torch.empty(c["x"].shape[0], dtype=torch.int32, device=dev),
+             "y": torch.empty((c["x"].shape[0], c["N"]), dtype=torch.float32, device=dev)}
+            for c in cases]
+    qplan = bt.QuantPlan([(x, o["xq"], o["xscale"], o["xsum"]) for x, o in zip(xs, outs)])
+    gplan = bt.MatmulPlan([dict(o, wdev=w, n=c["N"], w_scale=c["w_scale"])
+                           for o, w, c in zip(outs, ws, cases)])
+    na = synth.small_problem(35, 16, 1536, 8960)
+    assert bt.matmul_workspace_bytes(16, 1536, 8960) > 0      # K is split
+    na_w, na_q = _weights(na, dev), bt.quantize_act(torch.from_numpy(na["x"]).to(dev))
+    na_y = torch.empty((16, 1536), dtype=torch.float32, device=dev)
+
+    def work():
+        qplan.launch()
+        gplan.launch()
+        bt.ternary_matmul_noalloc(*na_q, na_w, 1536, na["w_scale"], na_y)
+
+    def snapshot():
+        torch.cuda.synchronize()
+        return [t.clone() for o in outs for t in o.values()] + [na_y.clone()]
+
+    work()
+    eager = snapshot()
+    g = _capture(work)
+    for rep in range(3):
+        for o in outs:
+            o["y"].fill_(float("nan"))
+            o["xq"].fill_(99)
+        na_y.fill_(float("nan"))
+        bt.ternary_matmul(*na_q, na_w, 1536, na["w_scale"],
+                          workspace=bt.new_workspace(16, 1536, 8960, dev))
+        torch.cuda.synchronize()
+        g.replay()
+        for i, (a, b) in enumerate(zip(snapshot(), eager)):
+            assert torch.equal(a.view(torch.uint8) if a.dtype == torch.float32 else a,
+                               b.view(torch.uint8) if b.dtype == torch.float32 else b), (rep, i)
