@@ -190,6 +190,39 @@ def test_quantize_tiny_and_zero_rows(dev):
     assert_exact("qsum", xsum.cpu().numpy(), s)
 
 
+def test_grouped_quantize_mixed_rows(dev):
+    """One grouped quantization launch over problems that take each of its paths:
+    short rows four to a workgroup (K % 4 == 0, K <= 2048, with a ragged last
+    workgroup), long rows one to a workgroup (K > 2048, K up to 9216 in registers
+    and beyond), rows whose K is not a multiple of 4, tiny rows and a zero row.
+    Relaunched with new activations in the same buffers."""
+    shapes = [(5, 1536), (3, 100), (17, 2048), (2, 2052), (9, 8960), (1, 7), (4, 9220),
+              (6, 4)]
+    rng = np.random.default_rng(12)
+    xs = [rng.standard_t(3, size=s).astype(np.float32) for s in shapes]
+    xs[2][3] = 0.0
+    dx = [to_dev(x, dev) for x in xs]
+    outs = [(torch.full(s, 99, dtype=torch.int8, device=dev),
+             torch.full((s[0],), float("nan"), dtype=torch.float32, device=dev),
+             torch.full((s[0],), POISON_I32, dtype=torch.int32, device=dev)) for s in shapes]
+    plan = bt.QuantPlan([(x,) + o for x, o in zip(dx, outs)])
+    for rep in range(2):
+        if rep:
+            for x, d in zip(xs, dx):
+                x[...] = rng.standard_normal(x.shape).astype(np.float32)
+                d.copy_(torch.from_numpy(x))
+            for o in outs:
+                o[0].fill_(99)
+                o[1].fill_(float("nan"))
+        plan.launch()
+        torch.cuda.synchronize()
+        for i, (x, (xq, xsc, xsum)) in enumerate(zip(xs, outs)):
+            q, d, s = oracle.quantize_ref(x)
+            assert_exact(f"q[{i}]", xq.cpu().numpy(), q)
+            assert_exact(f"d[{i}]", xsc.cpu().numpy(), d)
+            assert_exact(f"qsum[{i}]", xsum.cpu().numpy(), s)
+
+
 # ----------------------------------------------------------------- matmul
 
 def test_single_gemv_workload(dev):
