@@ -688,6 +688,7 @@ def run_single_projections(torch, bt, dev):
 
     # ---- one-layer prefill, M=512
     pre, tot_ops, tot_us, gemm_us_tot = {}, 0, 0.0, 0.0
+    layer = []
     for proj in range(len(synth.PROJECTIONS)):
         cp = synth.prefill_problem(proj)
         m, n, k = cp["M"], cp["N"], cp["K"]
@@ -717,7 +718,32 @@ def run_single_projections(torch, bt, dev):
         pre[cp["name"]] = {"M": m, "N": n, "K": k, "gemm_us": round(gemm_us, 2),
                            "gemm_tops": round(ops / (gemm_us * 1e-6) / 1e12, 1),
                            "quantize_plus_gemm_us": round(both_us, 2), "parity_ok": good}
-        del packed, wdev, x, q, y, wsp
+        layer.append({"m": m, "n": n, "k": k, "s": cp["w_scale"], "x": x, "wdev": wdev, "y": y,
+                      "xq": torch.empty((m, k), dtype=torch.int8, device=dev),
+                      "xs": torch.empty(m, dtype=torch.float32, device=dev),
+                      "xsum": torch.empty(m, dtype=torch.int32, device=dev),
+                      "y2": torch.empty((m, n), dtype=torch.float32, device=dev), "ws": wsp})
+        del packed, q
+    # the same layer with its four independent projections overlapped: one grouped
+    # quantization launch, one grouped GEMM launch for the three K=1536 projections,
+    # and down as a single call (its K is split there; a grouped plan has no split)
+    qplan = bt.QuantPlan([(L_["x"], L_["xq"], L_["xs"], L_["xsum"]) for L_ in layer])
+    gplan = bt.MatmulPlan([{"xq": L_["xq"], "xscale": L_["xs"], "xsum": L_["xsum"],
+                            "wdev": L_["wdev"], "n": L_["n"], "w_scale": L_["s"], "y": L_["y2"]}
+                           for L_ in layer if L_["k"] == 1536])
+    dn = [L_ for L_ in layer if L_["k"] != 1536][0]
+
+    def grouped_layer():
+        qplan.launch()
+        gplan.launch()
+        bt.ternary_matmul(dn["xq"], dn["xs"], dn["xsum"], dn["wdev"], dn["n"], dn["s"],
+                          y=dn["y2"], workspace=dn["ws"])
+
+    grouped_layer()
+    torch.cuda.synchronize()
+    grouped_same = all(bool(torch.equal(L_["y"], L_["y2"])) for L_ in layer)
+    grouped_us = _graph_us_per_call(torch, [grouped_layer] * 20)
+    del qplan, gplan, layer, dn
     out["prefill_M512_one_layer"] = {
         "workload": "one layer's four projections at M=512 (weights P(-1,0,1) = 0.3/0.4/0.3, "
                     "x ~ N(0,1)), quantize + GEMM each, replayed from a HIP graph "
@@ -725,10 +751,20 @@ def run_single_projections(torch, bt, dev):
         "shapes": pre, "ms_per_layer": round(tot_us * 1e-3, 4),
         "tops": round(tot_ops / (tot_us * 1e-6) / 1e12, 1),
         "gemm_only_tops": round(tot_ops / (gemm_us_tot * 1e-6) / 1e12, 1),
-        "pct_of_int8_peak": round(100 * tot_ops / (tot_us * 1e-6) / 1e12 / I8_PEAK_TOPS, 2)}
+        "pct_of_int8_peak": round(100 * tot_ops / (tot_us * 1e-6) / 1e12 / I8_PEAK_TOPS, 2),
+        "grouped": {"workload": "the four independent projections overlapped: one grouped "
+                                "quantization launch, one grouped GEMM launch (qkv, o, gate_up), "
+                                "down as a single split-K call; replayed from a HIP graph",
+                    "us_per_layer": round(grouped_us, 2),
+                    "tops": round(tot_ops / (grouped_us * 1e-6) / 1e12, 1),
+                    "pct_of_int8_peak": round(100 * tot_ops / (grouped_us * 1e-6) / 1e12 /
+                                              I8_PEAK_TOPS, 2),
+                    "matches_per_projection_bitwise": grouped_same}}
     log(f"prefill M=512 one layer: {tot_us:.1f} us ({tot_ops / (tot_us * 1e-6) / 1e12:.0f} TOPS), "
         f"GEMMs {gemm_us_tot:.1f} us; " + ", ".join(
-            f"{k_} {v['gemm_tops']:.0f}" for k_, v in pre.items()))
+            f"{k_} {v['gemm_tops']:.0f}" for k_, v in pre.items()) +
+        f"; grouped {grouped_us:.1f} us ({tot_ops / (grouped_us * 1e-6) / 1e12:.0f} TOPS), "
+        f"matches per-projection: {grouped_same}")
     torch.cuda.empty_cache()
     return out
 
