@@ -318,7 +318,8 @@ typedef struct bt_quant_desc {
 } bt_quant_desc;
 
 typedef struct bt_matmul_desc {
-    int64_t M, N, K;        /* M <= BT_GEMV_MAX_M in a grouped plan */
+    int64_t M, N, K;        /* a plan holds GEMVs only (every M <= BT_GEMV_MAX_M) or
+                               GEMMs only (every M > BT_GEMV_MAX_M, x NULL) */
     const int8_t* xq;       /* x == NULL: input from bt_quantize_act. x != NULL: optional output */
     const float* xscale;    /* same */
     const int32_t* xsum;    /* same */
@@ -341,16 +342,29 @@ bt_status bt_quantize_act_grouped(const void* plan_host, const void* plan_dev,
                                   hipStream_t stream);
 
 size_t bt_matmul_plan_bytes(int32_t count);
-/* Workspace the grouped launch of these descriptors needs (0 if none): a
- * projection whose M*K int8 activations do not fit one workgroup's LDS slice
- * is split along K, and its partial sums meet in the workspace. */
+/* Workspace the grouped launch of these descriptors needs (0 if none, or if a
+ * descriptor is invalid). GEMVs: a projection whose M*K int8 activations do not
+ * fit one workgroup's LDS slice is split along K, and its partial sums meet in
+ * the workspace through atomics. GEMMs: a projection with fewer 128 x 256
+ * output tiles than a quarter of the GPU's resident workgroups and a K of at
+ * least 24 stages of 128 is split into K ranges of about 12 stages; each range
+ * stores its int32 partial sums in an M x N slice of the workspace, followed by
+ * M int32 zeros. */
 size_t bt_matmul_plan_workspace_bytes(const bt_matmul_desc* descs, int32_t count);
 /* workspace: device memory of at least bt_matmul_plan_workspace_bytes bytes
- * (may be NULL when that is 0), zero-filled before its first use and left
- * zero-filled by every completed launch; it belongs to the plan. */
+ * (may be NULL when that is 0), zero-filled before its first use; it belongs
+ * to the plan, and every completed launch leaves zero whatever a launch reads
+ * as zero (GEMM slices are overwritten by each launch). BT_ERR_WORKSPACE if it
+ * is missing or too small, BT_ERR_ALIGN if not 16-byte aligned; descriptors are
+ * checked first and nothing is written to plan_host on an error. */
 bt_status bt_matmul_plan_build(const bt_matmul_desc* descs, int32_t count, void* workspace,
                                size_t workspace_bytes, void* plan_host, size_t plan_bytes);
-/* Every GEMV of the plan in one launch. */
+/* Every projection of the plan in one launch: GEMVs in one kernel (with the
+ * quantization inside when the plan was built from x); GEMMs in one persistent
+ * kernel, each projection on workgroup slots of its own, plus one launch per
+ * split projection that adds its K ranges' partial sums and stores y (and acc).
+ * Launches from one plan on one stream run in order; two streams launching the
+ * same plan at once race on its workspace. */
 bt_status bt_ternary_matmul_grouped(const void* plan_host, const void* plan_dev,
                                     hipStream_t stream);
 

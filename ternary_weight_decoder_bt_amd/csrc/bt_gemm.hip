@@ -508,9 +508,12 @@ void gemm_kernel(GemmArgs g) {
 // (gemm_persistent_kernel), or many independent problems in one grid
 // (gemm_persistent_grouped_kernel), where each problem owns `per_wg`
 // workgroup slots in every XCD and a workgroup walks only its problem's tiles.
-// `slot` is the workgroup's slot among its problem's slots of one XCD.
+// `slot` is the workgroup's slot among its problem's slots of one XCD. `lda`
+// is the byte stride of the activation rows: g.K, or more when g views one
+// K range of a wider problem. Without y (g.y null) only acc is stored.
 template <int WA, int WW, int NW, int KS, int NS>
-__device__ __forceinline__ void gemm_persistent_body(const GemmArgs& g, int slot, int per_wg) {
+__device__ __forceinline__ void gemm_persistent_body(const GemmArgs& g, int slot, int per_wg,
+                                                     int lda) {
     constexpr int BM = WA;
     constexpr int BN = WW * NW;
     constexpr int TA = WA / 16;
@@ -566,7 +569,7 @@ __device__ __forceinline__ void gemm_persistent_body(const GemmArgs& g, int slot
         tile_coords(g, tile_id, mt, nt);
         const int64_t m0 = int64_t(mt) * BM;
         const int t0 = min(nt * (BN / bt::kTileN) + wave * TW, g.tiles - 1);
-        ra = make_rsrc(g.xq + m0 * g.K, uint32_t(min(int64_t(BM), int64_t(g.M) - m0)) * uint32_t(g.K));
+        ra = make_rsrc(g.xq + m0 * lda, uint32_t(min(int64_t(BM), int64_t(g.M) - m0)) * uint32_t(lda));
         rw = make_rsrc(g.w + int64_t(t0) * tile_bytes, uint32_t(min(TW, g.tiles - t0)) * tile_bytes);
     };
 
@@ -593,7 +596,7 @@ __device__ __forceinline__ void gemm_persistent_body(const GemmArgs& g, int slot
     for (int q = 0; q < 4; ++q) {
         const int r = r0 + RPC * q;
         const int c = slot_of(r, lane % CPR);
-        avoff[q] = uint32_t(r0) * uint32_t(g.K) + uint32_t(c) * 16u;
+        avoff[q] = uint32_t(r0) * uint32_t(lda) + uint32_t(c) * 16u;
         ahigh[q] = c >= 8 ? kNowhere : 0u;
     }
     const bool tail128 = KS == 256 && (g.K & 255) != 0;
@@ -602,7 +605,7 @@ __device__ __forceinline__ void gemm_persistent_body(const GemmArgs& g, int slot
         const uint32_t tail = (tail128 && s == nst - 1) ? 0xffffffffu : 0u;
 #pragma unroll
         for (int j = 0; j < kDmaPerWave; ++j) {
-            const uint32_t voff = (avoff[j & 3] + uint32_t(RPC * j) * uint32_t(g.K)) | pad |
+            const uint32_t voff = (avoff[j & 3] + uint32_t(RPC * j) * uint32_t(lda)) | pad |
                                   (ahigh[j & 3] & tail);
             lds_dma16(ra, stage_buf(buf) + (wave * kDmaPerWave + j) * 1024, voff, kcol);
         }
@@ -716,13 +719,13 @@ __device__ __forceinline__ void gemm_persistent_body(const GemmArgs& g, int slot
                     const float r = rs[i];
                     const v4f yv = {float(a.x) * r, float(a.y) * r, float(a.z) * r, float(a.w) * r};
                     if (full) {
-                        __builtin_nontemporal_store(yv, (BT_GLOBAL v4f*)(yrow + n));
+                        if (g.y) __builtin_nontemporal_store(yv, (BT_GLOBAL v4f*)(yrow + n));
                         if (arow) __builtin_nontemporal_store(a, (BT_GLOBAL v4i*)(arow + n));
                     } else {
 #pragma unroll
                         for (int e = 0; e < 4; ++e) {
                             if (n + e < g.N) {
-                                gst<float>(yrow + n + e, yv[e]);
+                                if (g.y) gst<float>(yrow + n + e, yv[e]);
                                 if (arow) gst<int32_t>(arow + n + e, a[e]);
                             }
                         }
@@ -744,12 +747,18 @@ template <int WA, int WW, int NW, int KS, int NS>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void gemm_persistent_kernel(GemmArgs g) {
     gemm_persistent_body<WA, WW, NW, KS, NS>(g, int(blockIdx.x) / kXcds,
-                                             int(gridDim.x) / kXcds);
+                                             int(gridDim.x) / kXcds, g.K);
 }
 
 // Many problems in one launch: the problem owning slot blockIdx.x / 8 (one
 // lane per descriptor compares its first slot, a ballot counts them), then
 // that problem's persistent walk. Descriptors are ordered by first slot.
+// A problem split along K (splits > 1) has g.slots slots per K range, range r
+// after range r - 1; a workgroup of range r walks the problem viewed as that
+// range alone (activations and weights offset to its first stage, K its
+// length, the full row stride) and stores the raw int32 partial sums in the
+// range's slice of g.ws, with row sums read from the zeros after the slices
+// and no y; splitk_reduce_kernel, launched next, adds the slices.
 template <int WA, int WW, int NW, int KS, int NS>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void gemm_persistent_grouped_kernel(const GemmArgs* __restrict__ descs, int32_t count) {
@@ -762,8 +771,22 @@ void gemm_persistent_grouped_kernel(const GemmArgs* __restrict__ descs, int32_t 
         p += int(__popcll(__ballot(begin <= slot)));
     }
     p = __builtin_amdgcn_readfirstlane(p);
-    const GemmArgs g = descs[p];
-    gemm_persistent_body<WA, WW, NW, KS, NS>(g, slot - g.slot_begin, g.slots);
+    GemmArgs g = descs[p];
+    const int lda = g.K;
+    int local = slot - g.slot_begin;
+    if (g.splits > 1) {
+        const int r = local / g.slots;
+        local -= r * g.slots;
+        const int base = r * g.sps;                 // first 128-wide stage (sps is even)
+        const int nst = (g.K + KS - 1) / KS;
+        g.xq += int64_t(base) * KS;
+        g.w += int64_t(base / 2) * 1024;            // two 128-wide stages per 1 KB step
+        g.K = min(g.sps, nst - base) * KS;
+        g.acc = g.ws + int64_t(r) * g.ws_slice;
+        g.xsum = g.ws + int64_t(g.splits) * g.ws_slice;
+        g.y = nullptr;
+    }
+    gemm_persistent_body<WA, WW, NW, KS, NS>(g, local, g.slots, lda);
 }
 
 // Launch of the tiled GEMM for one tile shape (the shape itself is chosen on
@@ -813,6 +836,7 @@ template <int WA, int WW, int NW, int KS, int NS>
 bt_status launch_gemm_persistent(GemmArgs g, hipStream_t stream) {
     constexpr int BM = WA;
     constexpr int BN = WW * NW;
+    g.splits = 1;   // a single launch walks whole tiles
     g.m_tiles = int32_t(bt::ceil_div(g.M, BM));
     g.n_tiles = int32_t(bt::ceil_div(g.N, BN));
     const int64_t total = int64_t(g.m_tiles) * g.n_tiles;
@@ -857,8 +881,16 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(GemmArgs g) {
         const int32_t qs = kW8 ? 0 : gld<int32_t>(g.xsum + m);
         const float rs = gld<float>(g.xscale + m) * g.w_scale;
         if ((g.N & 3) == 0) {
+            // up to eight slices' loads in flight at once, then their sum
             v4i a = gld<v4i>(g.ws + o);
-            for (int sp = 1; sp < g.splits; ++sp) a += gld<v4i>(g.ws + sp * g.ws_slice + o);
+            for (int sp0 = 1; sp0 < g.splits; sp0 += 8) {
+                v4i p[8];
+#pragma unroll
+                for (int j = 0; j < 8; ++j)
+                    p[j] = sp0 + j < g.splits ? gld<v4i>(g.ws + (sp0 + j) * g.ws_slice + o)
+                                              : v4i{0, 0, 0, 0};
+                a += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
+            }
             a -= qs;
             v4f y = {float(a.x) * rs, float(a.y) * rs, float(a.z) * rs, float(a.w) * rs};
             y = epi_col4(g.epi, y, n);
@@ -1074,7 +1106,13 @@ bt_status gemm_reduce_slices(const GemmArgs& g, hipStream_t stream) {
 bt_status gemm_grouped_launch(const PlanHeader* hdr, const void* plan_dev, hipStream_t stream) {
     const auto* descs = reinterpret_cast<const GemmArgs*>(static_cast<const char*>(plan_dev) +
                                                           sizeof(PlanHeader));
-    return launch_gemm_grouped(hdr, descs, stream);
+    bt_status st = launch_gemm_grouped(hdr, descs, stream);
+    // projections split along K: one more launch each adds the slices (the
+    // kernel boundary orders it after every range's partial sums)
+    const auto* host = reinterpret_cast<const GemmArgs*>(hdr + 1);
+    for (int32_t i = 0; st == BT_OK && i < hdr->count; ++i)
+        if (host[i].splits > 1) st = launch_splitk_reduce<false>(host[i], stream);
+    return st;
 }
 
 }  // namespace bt

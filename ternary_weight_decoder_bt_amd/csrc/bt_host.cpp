@@ -324,12 +324,42 @@ static bt_status check_gemm_desc(const bt_matmul_desc& m) {
     return BT_OK;
 }
 
+// K ranges of a projection in a grouped GEMM plan: 1, unless it has fewer
+// output tiles than a quarter of the resident workgroup slots and a K of at
+// least two ranges of kPlanSplitStages 128-wide stages; then ranges of about
+// that many stages (an even number: a range starts on a 1 KB weight step), at
+// most one range-tile per compute unit. A plan's other projections at K = 1536
+// have 12 stages per tile, so a range of a split projection takes about as
+// long as one of their tiles (one layer at M = 512: down's 24 tiles of 70
+// stages become 6 ranges of 12 stages over the same 24 tiles).
+struct PlanSplit { int64_t splits, sps; };
+static PlanSplit gemm_plan_split(const bt_matmul_desc& m) {
+    const int64_t tiles = ceil_div(m.M, bt::kPersistBM) * ceil_div(m.N, bt::kPersistBN);
+    const int64_t nst = ceil_div(m.K, 128);
+    if (tiles >= bt::kGemmSlots / 4 || nst < 2 * bt::kPlanSplitStages) return {1, nst};
+    const int64_t s = std::max<int64_t>(
+        2, std::min<int64_t>(ceil_div(nst, bt::kPlanSplitStages), (bt::kGemmSlots / 2) / tiles));
+    const int64_t sps = (ceil_div(nst, s) + 1) & ~int64_t(1);
+    return {ceil_div(nst, sps), sps};
+}
+
 // Workgroup slots per XCD a projection of a grouped GEMM plan takes: as many as
 // its single launch would use (the resident slots of an XCD, or fewer when it
-// has fewer tiles there).
-static int64_t gemm_plan_slots(const bt_matmul_desc& m) {
+// has fewer tiles there), for each of its K ranges.
+static int64_t gemm_plan_range_slots(const bt_matmul_desc& m) {
     const int64_t tiles = ceil_div(m.M, bt::kPersistBM) * ceil_div(m.N, bt::kPersistBN);
     return std::min<int64_t>(bt::kSlotsPerXcd, ceil_div(tiles, bt::kXcds));
+}
+static int64_t gemm_plan_slots(const bt_matmul_desc& m) {
+    return gemm_plan_range_slots(m) * gemm_plan_split(m).splits;
+}
+
+// Workspace of a grouped GEMM plan's projection split along K: one M x N int32
+// slice of partial sums per K range, then M int32 zeros (the ranges' row sums).
+static size_t gemm_plan_ws_bytes(const bt_matmul_desc& m) {
+    const PlanSplit sp = gemm_plan_split(m);
+    if (sp.splits <= 1) return 0;
+    return bt::gemm_slice_bytes(m.M, m.N) * size_t(sp.splits) + bt::gemm_slice_bytes(m.M, 1);
 }
 
 // Grouped GEMM plan: every projection runs the persistent GEMM's walk over its
@@ -344,10 +374,16 @@ static int64_t gemm_plan_slots(const bt_matmul_desc& m) {
 // single launches, 4.60 ms grouped in decoder order, 4.43 ms grouped by K;
 // slots shared out in proportion to work, with every projection resident at
 // once, took 5.46 ms (the activation rows of many projections thrash the L2).
-static bt_status build_gemm_plan(const bt_matmul_desc* descs, int32_t count, void* plan_host) {
-    // descriptors already checked (check_gemm_desc), total slots within range
+// A projection split along K (gemm_plan_split) takes its slots once per K
+// range, ranges one after another; its workspace slices and zeros are carved
+// from the plan's workspace in descriptor order.
+static bt_status build_gemm_plan(const bt_matmul_desc* descs, int32_t count, void* workspace,
+                                 void* plan_host) {
+    // descriptors already checked (check_gemm_desc), total slots within range,
+    // workspace large enough
     auto* hdr = static_cast<bt::PlanHeader*>(plan_host);
     auto* out = reinterpret_cast<bt::GemmArgs*>(hdr + 1);
+    char* ws = static_cast<char*>(workspace);
     for (int32_t i = 0; i < count; ++i) {
         const bt_matmul_desc& m = descs[i];
         bt::GemmArgs g;
@@ -369,9 +405,15 @@ static bt_status build_gemm_plan(const bt_matmul_desc* descs, int32_t count, voi
         const int64_t tiles = int64_t(g.m_tiles) * g.n_tiles;
         g.per_xcd = int32_t(ceil_div(tiles, bt::kXcds));
         g.group_m = bt::gemm_group_m(g.m_tiles, g.n_tiles, g.per_xcd);
-        g.splits = 1;
-        g.sps = int32_t(ceil_div(m.K, 128));
-        g.slots = int32_t(gemm_plan_slots(m));
+        const PlanSplit sp = gemm_plan_split(m);
+        g.splits = int32_t(sp.splits);
+        g.sps = int32_t(sp.sps);
+        if (sp.splits > 1) {
+            g.ws = reinterpret_cast<int32_t*>(ws);
+            g.ws_slice = int64_t(bt::gemm_slice_bytes(m.M, m.N) / sizeof(int32_t));
+            ws += gemm_plan_ws_bytes(m);
+        }
+        g.slots = int32_t(gemm_plan_range_slots(m));   // per K range
         out[i] = g;
     }
     std::stable_sort(out, out + count,
@@ -379,7 +421,7 @@ static bt_status build_gemm_plan(const bt_matmul_desc* descs, int32_t count, voi
     int64_t slot = 0;
     for (int32_t i = 0; i < count; ++i) {
         out[i].slot_begin = int32_t(slot);
-        slot += out[i].slots;
+        slot += int64_t(out[i].slots) * out[i].splits;
     }
     hdr->magic = bt::kPlanMagicGemm;
     hdr->count = count;
@@ -402,6 +444,13 @@ static bt_status check_matmul_desc(const bt_matmul_desc& m, bool fused) {
 extern "C" size_t bt_matmul_plan_workspace_bytes(const bt_matmul_desc* descs, int32_t count) {
     if (!descs || count < 1) return 0;
     size_t total = 0;
+    if (descs[0].M > BT_GEMV_MAX_M) {
+        for (int32_t i = 0; i < count; ++i) {
+            if (check_gemm_desc(descs[i]) != BT_OK) return 0;
+            total += gemm_plan_ws_bytes(descs[i]);
+        }
+        return total;
+    }
     for (int32_t i = 0; i < count; ++i) {
         if (descs[i].M < 1 || descs[i].M > BT_GEMV_MAX_M || !valid_nk(descs[i].N, descs[i].K))
             return 0;
@@ -428,7 +477,12 @@ extern "C" bt_status bt_matmul_plan_build(const bt_matmul_desc* descs, int32_t c
             slots += gemm_plan_slots(descs[i]);
         }
         if (slots * bt::kXcds > (int64_t(1) << 31) - 1) return BT_ERR_SHAPE;
-        return build_gemm_plan(descs, count, plan_host);
+        const size_t need = bt_matmul_plan_workspace_bytes(descs, count);
+        if (need) {
+            if (!workspace || workspace_bytes < need) return BT_ERR_WORKSPACE;
+            if (!bt::aligned16(workspace)) return BT_ERR_ALIGN;
+        }
+        return build_gemm_plan(descs, count, workspace, plan_host);
     }
     const bool fused = descs[0].x != nullptr;
     for (int32_t i = 0; i < count; ++i) {
@@ -441,6 +495,13 @@ extern "C" bt_status bt_matmul_plan_build(const bt_matmul_desc* descs, int32_t c
         if (!workspace || workspace_bytes < need) return BT_ERR_WORKSPACE;
         if (!bt::aligned16(workspace)) return BT_ERR_ALIGN;
     }
+    int64_t total_blocks = 0;
+    for (int32_t i = 0; i < count; ++i) {
+        bt::GemvDesc d;
+        bt::gemv_shape(descs[i].M, descs[i].N, descs[i].K, true, &d);
+        total_blocks += d.blocks;
+    }
+    if (total_blocks > int64_t(1) << 31) return BT_ERR_SHAPE;   // nothing written yet
     auto* hdr = static_cast<bt::PlanHeader*>(plan_host);
     auto* out = reinterpret_cast<bt::GemvDesc*>(hdr + 1);
     char* ws = static_cast<char*>(workspace);
@@ -474,7 +535,6 @@ extern "C" bt_status bt_matmul_plan_build(const bt_matmul_desc* descs, int32_t c
         out[i].block_begin = blocks;
         blocks += out[i].blocks;
     }
-    if (blocks > int64_t(1) << 31) return BT_ERR_SHAPE;
     hdr->magic = fused ? bt::kPlanMagicGemvFused : bt::kPlanMagicGemv;
     hdr->count = count;
     hdr->total_blocks = blocks;

@@ -169,6 +169,8 @@ constexpr int kPersistBM = 128;
 constexpr int kPersistBN = 256;
 constexpr int kXcds = 8;
 constexpr int kSlotsPerXcd = kGemmSlots / kXcds;
+// grouped GEMM plans: target 128-wide stages per K range of a split projection
+constexpr int kPlanSplitStages = 12;
 
 // Token-row bands per tile group of the GEMM's tile order: as many as one
 // XCD's share of the tiles spans, so that share is one compact block.

@@ -402,11 +402,13 @@ class QuantPlan(_Plan):
 
 
 class MatmulPlan(_Plan):
-    """Many independent GEMVs (M <= 16) in one launch (bt_ternary_matmul_grouped).
+    """Many independent projections in one launch (bt_ternary_matmul_grouped):
+    all GEMVs (M <= 16) or all GEMMs (M > 16).
 
     items: sequence of dicts with keys wdev, n, w_scale, y, optionally acc, and
-    either xq, xscale, xsum (quantized inputs) or x (fp32 activations quantized
-    inside the launch; xq, xscale, xsum then optional outputs).
+    either xq, xscale, xsum (quantized inputs) or, GEMVs only, x (fp32
+    activations quantized inside the launch; xq, xscale, xsum then optional
+    outputs). The plan owns the workspace its split projections need.
     """
 
     def __init__(self, items):

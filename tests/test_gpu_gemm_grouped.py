@@ -1,6 +1,8 @@
 """Grouped prefill GEMMs: many independent projections with M > 16 in one
 persistent launch (a matmul plan whose descriptors all have M > 16), each
-projection walking its own 128 x 256 output tiles on workgroup slots of its own.
+projection walking its own 128 x 256 output tiles on workgroup slots of its own;
+a projection with few tiles and a long K is split into K ranges whose partial
+sums a second launch adds.
 
 Bar: the int32 accumulators equal the oracle's in every element, y within 1e-6
 relative (exactly 0 where the oracle's is 0), and y equals the single-call
@@ -85,7 +87,23 @@ def test_grouped_gemm_ragged_mixed_k(dev):
              for i, (m, n, k) in enumerate(shapes)]
     items = [_problem(dev, c, with_acc=(i % 2 == 0)) for i, c in enumerate(cases)]
     plan = bt.MatmulPlan(items)
-    assert plan.workspace is None
+    assert plan.workspace is not None   # (1000, 1536, 8960): 48 tiles, split along K
+    _check(dev, cases, items, plan, relaunches=2)
+
+
+def test_grouped_gemm_split_k(dev):
+    """Projections with few output tiles and a long K are split into K ranges
+    (ragged last range, odd stage counts, M just above 16, N not a multiple of
+    the tile), beside unsplit ones; the ranges' partial sums are added by a
+    second launch. Relaunched: the slices are rewritten and the zeros the
+    ranges read as row sums stay zero."""
+    shapes = [(300, 1000, 4480), (17, 40, 3200), (512, 1536, 8960), (129, 600, 1536),
+              (40, 2048, 6144)]
+    cases = [synth.small_problem(100 + i, m, n, k, "t3", (0.2, 0.6, 0.2))
+             for i, (m, n, k) in enumerate(shapes)]
+    items = [_problem(dev, c, with_acc=(i % 2 == 1)) for i, c in enumerate(cases)]
+    plan = bt.MatmulPlan(items)
+    assert plan.workspace is not None
     _check(dev, cases, items, plan, relaunches=2)
 
 

@@ -401,6 +401,39 @@ def test_gemm_plan_building_on_host():
     assert not host.any()
 
 
+def test_gemm_plan_split_k_on_host():
+    """A projection of a GEMM plan with fewer 128 x 256 tiles than a quarter of
+    the 512 resident slots and at least 24 stages of 128 along K is split into
+    ranges of about 12 stages (even): one layer at M=512 has down (24 tiles, 70
+    stages) in 6 ranges of 12, each range on its own 3 slots per XCD; the plan's
+    workspace holds one M x N int32 slice per range and M zeros."""
+    L = bt.lib()
+    f = FAKE
+    shapes = [(2048, 1536), (1536, 1536), (17920, 1536), (1536, 8960)]
+    m = (BtMatmulDesc * 4)(*[BtMatmulDesc(512, n, k, f, f, f, f, 0.02, f, None, None)
+                             for n, k in shapes])
+    nb = L.bt_matmul_plan_bytes(4)
+    host = np.zeros(nb, np.uint8)
+    slice_bytes = (512 * 1536 * 4 + 255) // 256 * 256
+    need = 6 * slice_bytes + 2048
+    assert L.bt_matmul_plan_workspace_bytes(m, 4) == need
+    assert L.bt_matmul_plan_build(m, 4, None, 0, host.ctypes.data, nb) == WORKSPACE
+    assert L.bt_matmul_plan_build(m, 4, f, need - 1, host.ctypes.data, nb) == WORKSPACE
+    assert L.bt_matmul_plan_build(m, 4, f + 8, need, host.ctypes.data, nb) == ALIGN
+    assert L.bt_matmul_plan_build(m, 4, f, need, host.ctypes.data, nb) == OK
+    slots = host[8:16].view(np.int64)[0]
+    assert slots == 4 + 3 + 35 + 6 * 3
+    # the unsplit shapes of the long prefill need no workspace (test above); nor does
+    # a long K with many tiles, or a short K with few
+    one = (BtMatmulDesc * 1)(BtMatmulDesc(4096, 1536, 8960, f, f, f, f, 0.02, f, None, None))
+    assert L.bt_matmul_plan_workspace_bytes(one, 1) == 0
+    one[0] = BtMatmulDesc(512, 1536, 2944, f, f, f, f, 0.02, f, None, None)   # 23 stages
+    assert L.bt_matmul_plan_workspace_bytes(one, 1) == 0
+    # 25 stages, one tile: ranges of 10, 10 and 5 stages
+    one[0] = BtMatmulDesc(17, 40, 3200, f, f, f, f, 0.02, f, None, None)
+    assert L.bt_matmul_plan_workspace_bytes(one, 1) == 3 * 2816 + 256   # 17 x 40 int32, rounded
+
+
 def test_repack_plan_building_on_host():
     L = bt.lib()
     f = FAKE
