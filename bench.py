@@ -977,8 +977,9 @@ def _one_core():
 
 def cpu_baseline_configs(oracle):
     """The oracle on the other workloads, each on a bounded sample (sizes stated):
-    brute int64 dot products on one thread for the single GEMV and the remainder
-    sweep; exact fp64 BLAS on all cores and on one core for the prefills. Timed
+    brute int64 dot products on one thread for the single GEMV, one layer of the
+    decode step and the remainder sweep; exact fp64 BLAS on all cores and on one
+    core for the prefills. Timed
     region: quantize + integer matmul + rescale (oracle.forward_ref) on weights
     already unpacked to int8."""
     out = {}
@@ -992,6 +993,18 @@ def cpu_baseline_configs(oracle):
         "mode": "brute (int64 dot products), 1 thread", "cores": 1, "us": round(t * 1e6, 1),
         "weight_gb_per_s": round(wb / t / 1e9, 4), "all_bytes_gb_per_s": round(allb / t / 1e9, 4),
         "sample": "the whole workload, median of 5 runs after 1 warm-up"}
+    # decode step: brute, one thread, on layer 0's four projections
+    layer = [synth.decode_problem(0, proj) for proj in range(len(synth.PROJECTIONS))]
+    with _one_core():
+        t, _ = _timed(lambda: [oracle.forward_ref(c["x"], c["w"], c["w_scale"], "int64")
+                               for c in layer], 3)
+    lb = sum(c["N"] * c["K"] // 4 for c in layer)
+    out["decode_step_layer0_brute"] = {
+        "mode": "brute (int64 dot products), 1 thread", "cores": 1, "ms": round(t * 1e3, 2),
+        "weight_gb_per_s": round(lb / t / 1e9, 4),
+        "tokens_per_s_28_layers": round(1.0 / (28 * t), 3),
+        "sample": "layer 0's four projections (one of the 28 layers of the decode step), median "
+                  "of 3 after 1 warm-up"}
     # remainder sweep: brute, one thread, every point once
     sweep = {}
     with _one_core():
@@ -1466,23 +1479,34 @@ def main():
         g_stack.replay()
         torch.cuda.synchronize()
         pf_ok = pf_ok and lp.parity_sampled()
-        s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
-        s0.record()
-        for i in range(args.prefill_steps):
-            g_stack.replay()
-        s1.record()
-        torch.cuda.synchronize()
-        ms = s0.elapsed_time(s1) / args.prefill_steps
+
+        def replay_trials(gr):
+            """Each of `prefill_steps` replays between its own two events (ms), after
+            two untimed replays."""
+            for _ in range(2):
+                gr.replay()
+            ts = []
+            for _ in range(args.prefill_steps):
+                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                torch.cuda.synchronize()
+                a.record()
+                gr.replay()
+                b.record()
+                torch.cuda.synchronize()
+                ts.append(a.elapsed_time(b))
+            return ts
+
+        def pcts(ts):
+            return {"p10": round(float(np.percentile(ts, 10)), 4),
+                    "p50": round(float(np.percentile(ts, 50)), 4),
+                    "p90": round(float(np.percentile(ts, 90)), 4),
+                    "trials_ms": [round(t_, 4) for t_ in ts]}
+
+        trials = {"per_projection_stack": replay_trials(g_stack)}
+        ms = float(np.median(trials["per_projection_stack"]))
         # GEMM-only time: the stack's GEMMs back to back (no quantize between)
-        g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
-        g0.record()
-        for i in range(args.prefill_steps):
-            g_gemms.replay()
-        g1.record()
-        torch.cuda.synchronize()
-        gemm_ms = g0.elapsed_time(g1) / args.prefill_steps
+        trials["per_projection_gemms"] = replay_trials(g_gemms)
+        gemm_ms = float(np.median(trials["per_projection_gemms"]))
         tops = lp.ops / (ms * 1e-3) / 1e12
         gemm_tops = lp.ops / (gemm_ms * 1e-3) / 1e12
         # the grouped stack: one quantization launch, one GEMM launch
@@ -1496,14 +1520,9 @@ def main():
         grouped_ok = lp.grouped_matches()
         times = {}
         for name, gr in (("stack", g_gstack), ("gemm", g_ggemm), ("per_projection_stack", g_stack)):
-            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            torch.cuda.synchronize()
-            a.record()
-            for i in range(args.prefill_steps):
-                gr.replay()
-            b.record()
-            torch.cuda.synchronize()
-            times[name] = a.elapsed_time(b) / args.prefill_steps
+            trials["grouped_" + name if name != "per_projection_stack" else
+                   "per_projection_stack_same_trial"] = ts_ = replay_trials(gr)
+            times[name] = float(np.median(ts_))
         g_ms, gg_ms = times["stack"], times["gemm"]
         log(f"prefill grouped: {g_ms:.3f} ms/stack ({lp.ops / (g_ms * 1e-3) / 1e12:.0f} TOPS), "
             f"GEMM launch {gg_ms:.3f} ms ({lp.ops / (gg_ms * 1e-3) / 1e12:.0f} TOPS); "
@@ -1529,6 +1548,9 @@ def main():
                               "4 columns of each (every output of all 112 projections is "
                               "compared by tests/test_gpu_long_prefill_full.py)",
             "steps": args.prefill_steps,
+            "trials": {k: pcts(v) for k, v in trials.items()},
+            "timing": "each figure is the median over `steps` graph replays, each between its "
+                      "own two events, after two untimed replays",
             "grouped": {
                 "workload": "the same stack as one grouped quantization launch over the 112 "
                             "inputs and one grouped GEMM launch over the 112 projections (the "

@@ -141,9 +141,10 @@ def test_graph_replays_match_eager(dev):
 
 def test_graph_grouped_prefill_and_noalloc(dev):
     """A grouped prefill (grouped quantization, grouped GEMM plan over ragged
-    projections with different K) and the allocation-free matmul on a split
-    shape, captured once: every replay, after eager work and a poisoning of
-    the outputs, equals the eager launches byte for byte."""
+    projections with different K, one of them split into K ranges whose reduce
+    launch is part of the plan's launch) and the allocation-free matmul on a
+    split shape, captured once: every replay, after eager work and a poisoning
+    of the outputs, equals the eager launches byte for byte."""
     shapes = [(600, 2048, 1536), (300, 1536, 8960), (129, 130, 384)]
     cases = [synth.small_problem(30 + i, m, n, k, "t3") for i, (m, n, k) in enumerate(shapes)]
     ws = [_weights(c, dev) for c in cases]
