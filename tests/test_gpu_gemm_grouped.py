@@ -107,6 +107,20 @@ def test_grouped_gemm_split_k(dev):
     _check(dev, cases, items, plan, relaunches=2)
 
 
+def test_grouped_gemm_many_ranges(dev):
+    """The longest K the library takes, on one tile: 1024 stages in 86 ranges of
+    12 (the reduce adds 86 slices, eight loads at a time), beside 11 ranges of a
+    16384-wide K."""
+    shapes = [(17, 40, 131072), (40, 60, 16384)]
+    cases = [synth.small_problem(110 + i, m, n, k, "t3", (0.3, 0.4, 0.3))
+             for i, (m, n, k) in enumerate(shapes)]
+    items = [_problem(dev, c, with_acc=True) for c in cases]
+    plan = bt.MatmulPlan(items)
+    slices = [(m * n * 4 + 255) // 256 * 256 for m, n, _ in shapes]
+    assert plan.workspace.numel() == 86 * slices[0] + 256 + 11 * slices[1] + 256
+    _check(dev, cases, items, plan, relaunches=2)
+
+
 def test_grouped_gemm_one_problem(dev):
     """A plan of one projection runs the same walk as the single persistent launch."""
     c = synth.small_problem(80, 4096, 4100, 512, "normal")

@@ -273,8 +273,11 @@ def test_decode_remainder_sweep(dev, proj, m):
     check_full(c, dev, wdev=_REMAINDER_W[key])
 
 
+# (40, 60, 16384): one 64 x 64 tile, K split into 16 ranges, so the reduce launch
+# adds its slices in two rounds of (up to) eight loads
 @pytest.mark.parametrize("m,n,k", [(17, 40, 384), (33, 200, 128), (100, 2048, 1536),
-                                   (128, 128, 256), (129, 130, 1664), (300, 1536, 8960)])
+                                   (128, 128, 256), (129, 130, 1664), (300, 1536, 8960),
+                                   (40, 60, 16384)])
 def test_gemm_shapes(dev, m, n, k):
     check_full(synth.small_problem(4, m, n, k, "t3", (0.3, 0.4, 0.3)), dev)
 
