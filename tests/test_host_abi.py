@@ -434,6 +434,68 @@ def test_gemm_plan_split_k_on_host():
     assert L.bt_matmul_plan_workspace_bytes(one, 1) == 3 * 2816 + 256   # 17 x 40 int32, rounded
 
 
+def _cdiv(a, b):
+    return -(-a // b)
+
+
+def test_gemm_plan_invariants_random():
+    """Random GEMM plans (1-12 projections, M 17-5000, N 1-20000, K up to the cap):
+    the header's slot count, the order by K, contiguous slot ranges, and for every
+    projection split along K (fewer than 128 tiles of 128 x 256, at least 24 stages
+    of 128) ranges of an even number of stages, of about 12 unless the cap of one
+    range-tile per compute unit binds, covering K exactly once; slices and zeros
+    256-byte aligned, disjoint and filling the workspace exactly."""
+    L = bt.lib()
+    f = FAKE
+    rng = np.random.default_rng(7)
+    built = 0
+    for trial in range(200):
+        count = int(rng.integers(1, 13))
+        shapes = [(int(rng.integers(17, 5001)), int(rng.integers(1, 20001)),
+                   128 * int(rng.integers(1, 1025))) for _ in range(count)]
+        m = (BtMatmulDesc * count)(*[BtMatmulDesc(mm, n, k, f, f, f, f, 0.02, f, None, None)
+                                     for mm, n, k in shapes])
+        need = L.bt_matmul_plan_workspace_bytes(m, count)
+        nb = L.bt_matmul_plan_bytes(count)
+        host = np.zeros(nb, np.uint8)
+        base = 0x7E0000000000
+        assert L.bt_matmul_plan_build(m, count, base, need, host.ctypes.data, nb) == OK, trial
+        built += 1
+        d = host[16:16 + 152 * count].reshape(count, 152)
+        i32 = lambda i, o: int(d[i, o:o + 4].view(np.int32)[0])   # noqa: E731
+        i64 = lambda i, o: int(d[i, o:o + 8].view(np.int64)[0])   # noqa: E731
+        assert [i32(i, 60) for i in range(count)] == sorted(k for _, _, k in shapes), trial
+        slot, pieces = 0, []
+        for i in range(count):
+            mm, n, k = i32(i, 52), i32(i, 56), i32(i, 60)
+            splits, sps, slots, slot_begin = i32(i, 120), i32(i, 124), i32(i, 144), i32(i, 148)
+            ws, ws_slice = i64(i, 128), i64(i, 136)
+            tiles = _cdiv(mm, 128) * _cdiv(n, 256)
+            nst = _cdiv(k, 128)
+            assert slots == min(64, _cdiv(tiles, 8)) and slot_begin == slot, (trial, i)
+            slot += slots * splits
+            if tiles >= 128 or nst < 24:
+                assert splits == 1 and ws == 0, (trial, i, splits)
+                continue
+            want = max(2, min(_cdiv(nst, 12), 256 // tiles))
+            assert sps % 2 == 0 and sps == _cdiv(_cdiv(nst, want), 2) * 2, (trial, i, sps)
+            assert (splits - 1) * sps < nst <= splits * sps, (trial, i)   # K covered once
+            assert 2 <= splits <= want and splits * tiles <= 256, (trial, i)
+            slice_bytes = _cdiv(mm * n * 4, 256) * 256
+            assert ws_slice * 4 == slice_bytes and ws % 256 == 0, (trial, i)
+            pieces.append((ws, splits * slice_bytes + _cdiv(mm * 4, 256) * 256))
+        assert host[8:16].view(np.int64)[0] == slot, trial
+        at = base
+        for ws, size in sorted(pieces):
+            assert ws == at, trial          # carved back to back from the start
+            at += size
+        assert at - base == need, trial
+        if need:
+            assert L.bt_matmul_plan_build(m, count, base, need - 1, host.ctypes.data, nb) \
+                == WORKSPACE
+    assert built == 200
+
+
 def test_repack_plan_building_on_host():
     L = bt.lib()
     f = FAKE
