@@ -112,6 +112,34 @@ bt_status bt_ternarize(const float* w, int64_t N, int64_t K, float eps, uint8_t*
                        float* scale, void* workspace, size_t workspace_bytes,
                        hipStream_t stream);
 
+/* The same ternarization for many tensors (a model's weights at conversion
+ * time), two launches in all instead of two per tensor: every tensor's
+ * packed bytes and scale equal bt_ternarize's for it, bit for bit. A plan is
+ * built on the host, copied by the caller into device memory (same bytes),
+ * and launched any number of times: plan_host sizes the grids, plan_dev is
+ * read by the kernels. Each descriptor obeys bt_ternarize's rules, with a
+ * slice of the plan's workspace of bt_ternarize_workspace_bytes(N,K) bytes;
+ * in addition no tensor's packed bytes or scale may overlap another tensor's
+ * w, packed bytes or scale (BT_ERR_VALUE). Every check runs before the plan is
+ * written. */
+typedef struct bt_ternarize_desc {
+    const float* w;     /* device fp32 N x K */
+    int64_t N, K;
+    float eps;
+    uint8_t* packed;    /* device, bt_packed_bytes(N,K) bytes, written */
+    float* scale;       /* device fp32 [1], written */
+} bt_ternarize_desc;
+
+size_t bt_ternarize_plan_bytes(int32_t count);
+/* Sum of bt_ternarize_workspace_bytes over the descriptors (0 if one is invalid). */
+size_t bt_ternarize_plan_workspace_bytes(const bt_ternarize_desc* descs, int32_t count);
+/* workspace: device, at least bt_ternarize_plan_workspace_bytes bytes, owned
+ * by the plan while it is in use (contents on entry do not matter). */
+bt_status bt_ternarize_plan_build(const bt_ternarize_desc* descs, int32_t count,
+                                  void* workspace, size_t workspace_bytes, void* plan_host,
+                                  size_t plan_bytes);
+bt_status bt_ternarize_grouped(const void* plan_host, const void* plan_dev, hipStream_t stream);
+
 /* ---------------------------------------------------------------------------
  * Device repack (once per weight tensor, at load time).
  *

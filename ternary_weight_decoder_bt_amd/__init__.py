@@ -16,6 +16,7 @@ from .ops import (  # noqa: F401
     MatmulPlan,
     QuantPlan,
     RepackPlan,
+    TernarizePlan,
     int8_matmul,
     int8_matmul_workspace_bytes,
     int8_repacked_bytes,

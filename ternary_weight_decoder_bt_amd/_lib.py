@@ -26,6 +26,10 @@ SIGNATURES = {
     "bt_unpack_ternary": (C.c_int, [_p, _i64, _i64, _p]),
     "bt_ternarize_workspace_bytes": (_sz, [_i64, _i64]),
     "bt_ternarize": (C.c_int, [_p, _i64, _i64, _f, _p, _p, _p, _sz, _p]),
+    "bt_ternarize_plan_bytes": (_sz, [_i32]),
+    "bt_ternarize_plan_workspace_bytes": (_sz, [_p, _i32]),
+    "bt_ternarize_plan_build": (C.c_int, [_p, _i32, _p, _sz, _p, _sz]),
+    "bt_ternarize_grouped": (C.c_int, [_p, _p, _p]),
     "bt_repacked_bytes": (_sz, [_i64, _i64]),
     "bt_repack_ternary": (C.c_int, [_p, _i64, _i64, _p, _p]),
     "bt_quantize_act": (C.c_int, [_p, _i64, _i64, _p, _p, _p, _p]),
@@ -57,6 +61,10 @@ SIGNATURES = {
 class BtEpilogue(C.Structure):
     _fields_ = [("bias", _p), ("layer_scale", _p), ("residual", _p), ("relu", _i32),
                 ("reserved", _i32)]
+
+
+class BtTernarizeDesc(C.Structure):
+    _fields_ = [("w", _p), ("N", _i64), ("K", _i64), ("eps", _f), ("packed", _p), ("scale", _p)]
 
 
 class BtRepackDesc(C.Structure):

@@ -20,6 +20,7 @@ constexpr uint32_t kPlanMagicGemv = 0x42544d47u;    // "GMTB"
 constexpr uint32_t kPlanMagicGemvFused = 0x42544646u;   // "FFTB"
 constexpr uint32_t kPlanMagicRepack = 0x4254504bu;      // "KPTB"
 constexpr uint32_t kPlanMagicGemm = 0x42544d4du;        // "MMTB"
+constexpr uint32_t kPlanMagicTern = 0x42545454u;        // "TTTB"
 
 inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
@@ -118,6 +119,23 @@ struct RepackDesc {
     int32_t pad_;
     int64_t block_begin;    // first output block of this tensor in a grouped launch
     int64_t blocks;         // ceil(N / 16) * steps
+};
+
+// One tensor of a grouped ternarization: its first-pass workgroups write
+// `nparts` partial sums of |w| to `partials`, its second-pass workgroups code
+// and pack it. part_begin / pack_begin: its first workgroup of each launch.
+struct TernDesc {
+    const float* w;
+    uint8_t* packed;
+    float* scale;
+    double* partials;
+    int64_t N, K;
+    float eps;
+    int32_t nparts;
+    int32_t pack_blocks;
+    int32_t pad_;
+    int64_t part_begin;
+    int64_t pack_begin;
 };
 
 struct PlanHeader {

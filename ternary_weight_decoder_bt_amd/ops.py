@@ -11,7 +11,8 @@ import ctypes as C
 
 import numpy as np
 
-from ._lib import BtEpilogue, BtMatmulDesc, BtQuantDesc, BtRepackDesc, BtError, check, lib
+from ._lib import (BtEpilogue, BtMatmulDesc, BtQuantDesc, BtRepackDesc, BtTernarizeDesc, BtError,
+                   check, lib)
 
 GROUP_K = 128
 GEMV_MAX_M = 16
@@ -378,6 +379,39 @@ class RepackPlan(_Plan):
         check(lib().bt_repack_ternary_grouped(h, d, _stream(stream)), "bt_repack_ternary_grouped")
 
 
+class TernarizePlan(_Plan):
+    """Many offline ternarizations in one pair of launches (bt_ternarize_grouped).
+
+    items: sequence of (w, packed, scale) CUDA tensors (fp32 (N, K), uint8
+    (N*K/4,), fp32 (1,)); eps as for ternarize. The plan owns its workspace.
+    """
+
+    def __init__(self, items, eps: float = 0.0):
+        torch = _torch()
+        descs = (BtTernarizeDesc * len(items))()
+        self._keep = list(items)
+        for i, (w, packed, scale) in enumerate(items):
+            _dev(w, torch.float32, None, "w")
+            if w.dim() != 2:
+                raise ValueError("w must be (N, K)")
+            n, k = w.shape
+            _dev(packed, torch.uint8, (packed_bytes(n, k),), "packed")
+            _dev(scale, torch.float32, (1,), "scale")
+            descs[i] = BtTernarizeDesc(_ptr(w), n, k, float(eps), _ptr(packed), _ptr(scale))
+        dev = items[0][0].device
+        ws_bytes = int(lib().bt_ternarize_plan_workspace_bytes(descs, len(items)))
+        self.workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+        nbytes = int(lib().bt_ternarize_plan_bytes(len(items)))
+        host = np.zeros(nbytes, np.uint8)
+        check(lib().bt_ternarize_plan_build(descs, len(items), _ptr(self.workspace), ws_bytes,
+                                            _np_ptr(host), nbytes), "bt_ternarize_plan_build")
+        super().__init__(host, dev)
+
+    def launch(self, stream=None):
+        h, d = self._ptrs()
+        check(lib().bt_ternarize_grouped(h, d, _stream(stream)), "bt_ternarize_grouped")
+
+
 class QuantPlan(_Plan):
     """Many independent quantizations in one launch (bt_quantize_act_grouped).
 
@@ -439,6 +473,6 @@ __all__ = [
     "BtError", "GROUP_K", "GEMV_MAX_M", "packed_bytes", "repacked_bytes",
     "matmul_workspace_bytes", "int8_repacked_bytes", "repack_int8", "int8_matmul", "int8_matmul_workspace_bytes", "pack_ternary", "unpack_ternary", "repack_ternary",
     "quantize_act", "rmsnorm_quantize", "new_workspace", "ternary_matmul", "ternary_matmul_noalloc",
-    "ternary_matmul_fused", "RepackPlan",
+    "ternary_matmul_fused", "RepackPlan", "TernarizePlan",
     "QuantPlan", "MatmulPlan",
 ]

@@ -112,3 +112,39 @@ def test_ternarized_weights_feed_the_matmul(dev):
         nz = yr != 0
         assert (got[~nz] == 0).all()
         assert (np.abs(got[nz] - yr[nz]) <= 1e-6 * np.abs(yr[nz])).all()
+
+
+def test_grouped_plan_matches_single_calls_and_oracle(dev):
+    """A grouped plan over tensors of every size class (the decoder's four
+    shapes, ragged small ones, an all-zero one), one eps: each tensor's packed
+    bytes and scale equal bt_ternarize's bit for bit, and the oracle's for a
+    sample; relaunched after the outputs are poisoned, the same again."""
+    shapes = [(2048, 1536, "normal"), (1536, 1536, "outlier"), (17920, 1536, "t3"),
+              (1536, 8960, "normal"), (17, 128, "t3"), (1, 384, "normal"), (4099, 256, "outlier")]
+    eps = 1e-5
+    ws_ = [synth.fp_weights(40 + i, n, k, dist) for i, (n, k, dist) in enumerate(shapes)]
+    ws_.append(np.zeros((5, 256), np.float32))
+    items = []
+    for w in ws_:
+        n, k = w.shape
+        items.append((torch.from_numpy(w).to(dev),
+                      torch.empty(n * k // 4, dtype=torch.uint8, device=dev),
+                      torch.empty(1, dtype=torch.float32, device=dev)))
+    plan = bt.TernarizePlan(items, eps)
+    for rep in range(2):
+        for _, p, sc in items:
+            p.fill_(0xFF)
+            sc.fill_(float("nan"))
+        plan.launch()
+        torch.cuda.synchronize()
+        for i, (w, p, sc) in enumerate(items):
+            want_p, want_g = bt.ternarize(w, eps)
+            torch.cuda.synchronize()
+            assert torch.equal(p, want_p), (rep, i)
+            assert sc.cpu().numpy().view(np.uint32)[0] == want_g.cpu().numpy().view(np.uint32)[0]
+    for i in (0, len(items) - 1, len(items) - 2):
+        w = ws_[i]
+        want_p, want_g = oracle.ternarize_pack_ref(w, eps)
+        got_p = items[i][1].cpu().numpy().reshape(want_p.shape)
+        np.testing.assert_array_equal(got_p, want_p)
+        assert np.float32(items[i][2].cpu().numpy()[0]) == want_g

@@ -16,7 +16,8 @@ import pytest
 import oracle
 import ternary_weight_decoder_bt_amd as bt
 from ternary_weight_decoder_bt_amd import _lib
-from ternary_weight_decoder_bt_amd._lib import BtEpilogue, BtMatmulDesc, BtQuantDesc, BtRepackDesc
+from ternary_weight_decoder_bt_amd._lib import (BtEpilogue, BtMatmulDesc, BtQuantDesc, BtRepackDesc,
+                                                 BtTernarizeDesc)
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "bt.h")
@@ -494,6 +495,62 @@ def test_gemm_plan_invariants_random():
             assert L.bt_matmul_plan_build(m, count, base, need - 1, host.ctypes.data, nb) \
                 == WORKSPACE
     assert built == 200
+
+
+def test_ternarize_plan_building_on_host():
+    """A grouped ternarization plan: each tensor gets bt_ternarize's workspace
+    slice and workgroup counts (first pass min(1024, ceil(N*K/4/2048)), second
+    min(2048, ceil(N*K/16/256))) at consecutive offsets; bt_ternarize's argument
+    errors, a missing workspace and overlapping outputs between tensors are
+    reported before anything is written."""
+    L = bt.lib()
+    base = 0x7F0000000000
+    shapes = [(2048, 1536), (17, 128), (1536, 8960)]
+    addr = [base + (i << 32) for i in range(3)]      # far apart: no overlaps
+    d = (BtTernarizeDesc * 3)(*[BtTernarizeDesc(a, n, k, 1e-5, a + (1 << 31), a + (1 << 31) + (1 << 30))
+                                for a, (n, k) in zip(addr, shapes)])
+    ws_each = [L.bt_ternarize_workspace_bytes(n, k) for n, k in shapes]
+    need = L.bt_ternarize_plan_workspace_bytes(d, 3)
+    assert need == sum(ws_each)
+    nb = L.bt_ternarize_plan_bytes(3)
+    assert nb == 16 + 3 * 80
+    host = np.zeros(nb, np.uint8)
+    wsb = base + (8 << 32)
+    assert L.bt_ternarize_plan_build(d, 3, wsb, need - 1, host.ctypes.data, nb) == WORKSPACE
+    assert not host.any()
+    assert L.bt_ternarize_plan_build(d, 3, wsb, need, host.ctypes.data, nb) == OK
+    assert host[:4].view(np.uint32)[0] == 0x42545454
+    t = host[16:].reshape(3, 80)
+    parts = [min(1024, -(-(n * k // 4) // 2048)) for n, k in shapes]
+    packs = [min(2048, -(-(n * k // 16) // 256)) for n, k in shapes]
+    assert host[8:16].view(np.int64)[0] == sum(parts)
+    for i in range(3):
+        assert t[i, 24:32].view(np.int64)[0] == wsb + sum(ws_each[:i])      # partials
+        assert t[i, 52:56].view(np.int32)[0] == parts[i]
+        assert t[i, 56:60].view(np.int32)[0] == packs[i]
+        assert t[i, 64:72].view(np.int64)[0] == sum(parts[:i])
+        assert t[i, 72:80].view(np.int64)[0] == sum(packs[:i])
+    # errors, each leaving the plan unwritten
+    for field, bad, want in (("K", 100, SHAPE), ("eps", -1.0, VALUE), ("eps", float("nan"), VALUE),
+                             ("w", 0, NULL), ("packed", addr[1] + (1 << 31) + 4, ALIGN)):
+        keep = getattr(d[1], field)
+        setattr(d[1], field, bad)
+        host[:] = 0
+        assert L.bt_ternarize_plan_build(d, 3, wsb, need, host.ctypes.data, nb) == want, field
+        assert not host.any(), field
+        setattr(d[1], field, keep)
+    # tensor 2's packed bytes inside tensor 0's weights
+    keep = d[2].packed
+    d[2].packed = addr[0] + 4096
+    assert L.bt_ternarize_plan_build(d, 3, wsb, need, host.ctypes.data, nb) == VALUE
+    d[2].packed = keep
+    # the workspace inside a tensor's weights, or meeting another tensor's packed bytes
+    assert L.bt_ternarize_plan_build(d, 3, addr[2], need, host.ctypes.data, nb) == VALUE
+    assert L.bt_ternarize_plan_build(d, 3, addr[2] + (1 << 31) - 256, need, host.ctypes.data,
+                                     nb) == VALUE
+    # a launch with another plan kind is refused on the host
+    host[:4] = np.frombuffer(np.uint32(0x42545141).tobytes(), np.uint8)
+    assert L.bt_ternarize_grouped(host.ctypes.data, FAKE, None) == VALUE
 
 
 def test_repack_plan_building_on_host():
