@@ -3,8 +3,8 @@
  * library runs on: the rate at which the int8 matrix-core instruction the
  * ternary matmul is built on (v_mfma_i32_16x16x64_i8) retires, the shader
  * clock while it runs, and the bandwidth of a plain streaming read at a given
- * size. They give the denominators the library's kernels are judged against a
- * measured rather than only a published value.
+ * size. They give the library's kernels denominators that are
+ * measured rather than only published values.
  *
  * A separate library (libbt_ceilings.so): nothing here is part of the matmul
  * path, and the matmul library does not depend on it.
