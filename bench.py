@@ -1475,18 +1475,37 @@ def main():
     del ds
     torch.cuda.empty_cache()
 
+    # A secondary leg that raises is recorded under "errors" and the rest still
+    # runs, so the headline line is always printed.
+    def guarded(name, fn):
+        try:
+            return fn()
+        except Exception as e:  # noqa: BLE001
+            log(f"{name} failed: {e!r}")
+            out.setdefault("errors", {})[name] = repr(e)
+            return None
+
     # ---- offline ternarization of the stack (one-time, like the repack)
     if not args.no_ternarize:
-        out["ternarize"] = run_ternarize_stack(torch, bt, dev, args.layers)
+        out["ternarize"] = guarded("ternarize",
+                                   lambda: run_ternarize_stack(torch, bt, dev, args.layers))
 
     # ---- single-projection calls (one GEMV, remainder sweep, one-layer prefill)
     if not args.no_singles:
-        out["single_projections"] = run_single_projections(torch, bt, dev)
+        out["single_projections"] = guarded("single_projections",
+                                            lambda: run_single_projections(torch, bt, dev))
 
     # ---- long prefill (secondary)
-    if not args.no_prefill:
-        lp = LongPrefill(torch, bt, dev, args.layers, 4096, packed_prefill)
-        del packed_prefill
+    def long_prefill_leg(packed):
+        lp = LongPrefill(torch, bt, dev, args.layers, 4096, packed)
+        packed.clear()
+        try:
+            return long_prefill_report(lp)
+        finally:
+            del lp
+            torch.cuda.empty_cache()
+
+    def long_prefill_report(lp):
         lp.step()
         torch.cuda.synchronize()
         pf_ok = lp.parity_sampled()
@@ -1555,7 +1574,7 @@ def main():
         for k_, (ms_, gbs) in prologues.items():
             log(f"{k_}: {ms_ * 1e3:.1f} us ({gbs:.0f} GB/s, {100 * gbs / HBM_PEAK_GBS:.1f}% of HBM)")
         log(f"prefill: {ms:.3f} ms/stack ({tops:.0f} TOPS), GEMMs {gemm_ms:.3f} ms ({gemm_tops:.0f} TOPS)")
-        out["prefill"] = {
+        return {
             "workload": "long prefill, M=4096 tokens x 28 layers x 4 projections (quantize + GEMM "
                         "each), replayed from a HIP graph",
             "int8_ops_per_stack": lp.ops, "ms_per_stack": round(ms, 4),
@@ -1606,23 +1625,25 @@ def main():
                              "frac": round(gemm_tops / I8_PEAK_TOPS, 4),
                              "traffic": measured_gemm_traffic("per_projection")}},
         }
-        del lp
-        torch.cuda.empty_cache()
+
+    if not args.no_prefill:
+        out["prefill"] = guarded("prefill", lambda: long_prefill_leg(packed_prefill))
+        del packed_prefill
 
     # ---- I8_S (the tokenizer's INT8 GEMMs), secondary
     if not args.no_i8s:
-        out["i8s"] = run_i8s_tokenizer_ffn(torch, bt, dev)
+        out["i8s"] = guarded("i8s", lambda: run_i8s_tokenizer_ffn(torch, bt, dev))
 
     if not args.no_ceilings:
-        out["ceilings"] = run_ceilings(torch, dev)
-        c = out["ceilings"]
-        log(f"ceilings: int8 MFMA {c['int8_peak_tops_measured']} TOPS measured "
-            f"({c['int8_peak_tops_derived_at_2p4ghz']} at 2.4 GHz), streaming read "
-            f"{c['stream_read_peak_gb_per_s']} GB/s")
+        out["ceilings"] = c = guarded("ceilings", lambda: run_ceilings(torch, dev))
+        if c:
+            log(f"ceilings: int8 MFMA {c['int8_peak_tops_measured']} TOPS measured "
+                f"({c['int8_peak_tops_derived_at_2p4ghz']} at 2.4 GHz), streaming read "
+                f"{c['stream_read_peak_gb_per_s']} GB/s")
 
     if not args.no_cpu_baseline:
         log("timing the CPU oracle")
-        out["cpu_baseline"] = cpu_baseline(args.cpu_seconds)
+        out["cpu_baseline"] = guarded("cpu_baseline", lambda: cpu_baseline(args.cpu_seconds))
     print(json.dumps(out), flush=True)
 
 
