@@ -605,3 +605,33 @@ def test_gemm_split_k_exact_and_workspace_clean(dev, m, n, k):
         assert_exact("acc", acc.cpu().numpy(), ref["acc"])
         assert np.array_equal(y.cpu().numpy(), ref["y"])
         ws.fill_(0x5A)
+
+
+# ------------------------------------------------------ the longest K taken
+#
+# K = BT_MAX_K = 131072 on every path: single GEMV unfused (M = 1, 5; K split
+# into workgroup ranges whose slices a reduce launch adds) and fused (the row
+# read twice), GEMM (M = 17, 300: K split into many ranges), random operands
+# against the oracle, and the largest accumulator the bound allows: every q =
+# 127 and every weight +1 gives acc = 127 * 131072 = 16,646,144 < 2^24, exact in
+# int32 and in fp32.
+@pytest.mark.parametrize("m", [1, 5, 17, 300])
+def test_maximum_k_every_path(dev, m):
+    k, n = 131072, 40
+    check_full(synth.small_problem(120 + m, m, n, k, "outlier", (0.3, 0.4, 0.3)), dev)
+    x = np.full((m, k), 0.75, np.float32)
+    w = np.ones((n, k), np.int8)
+    ref = oracle.forward_ref(x, w, np.float32(0.5), "int64")
+    assert int(ref["acc"].max()) == 127 * k
+    y, acc = check_full({"x": x, "w": w, "w_scale": np.float32(0.5)}, dev, mode="int64")
+    assert int(acc.max().item()) == 127 * k
+    if m <= 16:
+        c = synth.small_problem(130 + m, m, n, k, "t3")
+        ref = oracle.forward_ref(c["x"], c["w"], c["w_scale"], "f64")
+        wdev = load_weights(c["w"], dev)
+        y = torch.full((m, n), float("nan"), dtype=torch.float32, device=dev)
+        acc = torch.full((m, n), POISON_I32, dtype=torch.int32, device=dev)
+        bt.ternary_matmul_fused(to_dev(c["x"], dev), wdev, n, c["w_scale"], y=y, acc=acc)
+        torch.cuda.synchronize()
+        assert_exact("fused acc", acc.cpu().numpy(), ref["acc"])
+        assert_rel("fused y", y.cpu().numpy(), ref["y"])
