@@ -635,3 +635,32 @@ def test_maximum_k_every_path(dev, m):
         torch.cuda.synchronize()
         assert_exact("fused acc", acc.cpu().numpy(), ref["acc"])
         assert_rel("fused y", y.cpu().numpy(), ref["y"])
+
+
+# ------------------------------------------------------------ degenerate cases
+#
+# One output row on the GEMM path, one 128-element group, all-zero weights (the
+# code offset then cancels exactly: every code is 1, so sum q*c - sum q = 0 and y
+# is exactly 0), and the GEMV / GEMM boundary: rows 0..15 of an M = 17 GEMM
+# equal the M = 16 GEMV of the same rows bit for bit.
+@pytest.mark.parametrize("m,n,k", [(17, 1, 128), (300, 1, 1536), (1, 7, 128), (40, 300, 128)])
+def test_degenerate_shapes(dev, m, n, k):
+    check_full(synth.small_problem(140, m, n, k, "t3"), dev, mode="int64")
+
+
+@pytest.mark.parametrize("m", [1, 16, 17, 512])
+def test_all_zero_weights(dev, m):
+    c = synth.small_problem(141, m, 100, 1536, "outlier", (0.0, 1.0, 0.0))
+    assert not c["w"].any()
+    y, acc = check_full(c, dev, mode="int64")
+    assert not acc.any().item() and not y.any().item()
+
+
+def test_gemv_gemm_boundary_agree(dev):
+    c = synth.small_problem(142, 17, 1536, 8960, "outlier")
+    wdev = load_weights(c["w"], dev)
+    y17, acc17 = check_full(c, dev, wdev=wdev)
+    c16 = dict(c, x=c["x"][:16])
+    y16, acc16 = check_full(c16, dev, wdev=wdev)
+    assert torch.equal(acc16, acc17[:16])
+    assert torch.equal(y16, y17[:16])
