@@ -97,7 +97,7 @@ def test_grouped_gemm_split_k(dev):
     the tile), beside unsplit ones; the ranges' partial sums are added by a
     second launch. Relaunched: the slices are rewritten and the zeros the
     ranges read as row sums stay zero."""
-    shapes = [(300, 1000, 4480), (17, 40, 3200), (512, 1536, 8960), (129, 600, 1536),
+    shapes = [(300, 1000, 4480), (17, 40, 4224), (512, 1536, 8960), (129, 600, 1536),
               (40, 2048, 6144)]
     cases = [synth.small_problem(100 + i, m, n, k, "t3", (0.2, 0.6, 0.2))
              for i, (m, n, k) in enumerate(shapes)]
@@ -108,8 +108,8 @@ def test_grouped_gemm_split_k(dev):
 
 
 def test_grouped_gemm_many_ranges(dev):
-    """The longest K the library takes, on one tile: 1024 stages in 86 ranges of
-    12 (the reduce adds 86 slices, eight loads at a time), beside 11 ranges of a
+    """The longest K the library takes, on one tile: 1024 stages in 64 ranges of
+    16 (the reduce adds 64 slices, eight loads at a time), beside 8 ranges of a
     16384-wide K."""
     shapes = [(17, 40, 131072), (40, 60, 16384)]
     cases = [synth.small_problem(110 + i, m, n, k, "t3", (0.3, 0.4, 0.3))
@@ -117,7 +117,7 @@ def test_grouped_gemm_many_ranges(dev):
     items = [_problem(dev, c, with_acc=True) for c in cases]
     plan = bt.MatmulPlan(items)
     slices = [(m * n * 4 + 255) // 256 * 256 for m, n, _ in shapes]
-    assert plan.workspace.numel() == 86 * slices[0] + 256 + 11 * slices[1] + 256
+    assert plan.workspace.numel() == 64 * slices[0] + 256 + 8 * slices[1] + 256
     _check(dev, cases, items, plan, relaunches=2)
 
 

@@ -404,9 +404,9 @@ def test_gemm_plan_building_on_host():
 
 def test_gemm_plan_split_k_on_host():
     """A projection of a GEMM plan with fewer 128 x 256 tiles than a quarter of
-    the 512 resident slots and at least 24 stages of 128 along K is split into
-    ranges of about 12 stages (even): one layer at M=512 has down (24 tiles, 70
-    stages) in 6 ranges of 12, each range on its own 3 slots per XCD; the plan's
+    the 512 resident slots and at least 32 stages of 128 along K is split into
+    ranges of at most about 16 stages (even): one layer at M=512 has down (24
+    tiles, 70 stages) in 5 ranges of 14, each range on its own 3 slots per XCD; the plan's
     workspace holds one M x N int32 slice per range and M zeros."""
     L = bt.lib()
     f = FAKE
@@ -416,22 +416,22 @@ def test_gemm_plan_split_k_on_host():
     nb = L.bt_matmul_plan_bytes(4)
     host = np.zeros(nb, np.uint8)
     slice_bytes = (512 * 1536 * 4 + 255) // 256 * 256
-    need = 6 * slice_bytes + 2048
+    need = 5 * slice_bytes + 2048
     assert L.bt_matmul_plan_workspace_bytes(m, 4) == need
     assert L.bt_matmul_plan_build(m, 4, None, 0, host.ctypes.data, nb) == WORKSPACE
     assert L.bt_matmul_plan_build(m, 4, f, need - 1, host.ctypes.data, nb) == WORKSPACE
     assert L.bt_matmul_plan_build(m, 4, f + 8, need, host.ctypes.data, nb) == ALIGN
     assert L.bt_matmul_plan_build(m, 4, f, need, host.ctypes.data, nb) == OK
     slots = host[8:16].view(np.int64)[0]
-    assert slots == 4 + 3 + 35 + 6 * 3
+    assert slots == 4 + 3 + 35 + 5 * 3
     # the unsplit shapes of the long prefill need no workspace (test above); nor does
     # a long K with many tiles, or a short K with few
     one = (BtMatmulDesc * 1)(BtMatmulDesc(4096, 1536, 8960, f, f, f, f, 0.02, f, None, None))
     assert L.bt_matmul_plan_workspace_bytes(one, 1) == 0
-    one[0] = BtMatmulDesc(512, 1536, 2944, f, f, f, f, 0.02, f, None, None)   # 23 stages
+    one[0] = BtMatmulDesc(512, 1536, 3968, f, f, f, f, 0.02, f, None, None)   # 31 stages
     assert L.bt_matmul_plan_workspace_bytes(one, 1) == 0
-    # 25 stages, one tile: ranges of 10, 10 and 5 stages
-    one[0] = BtMatmulDesc(17, 40, 3200, f, f, f, f, 0.02, f, None, None)
+    # 33 stages, one tile: ranges of 12, 12 and 9 stages
+    one[0] = BtMatmulDesc(17, 40, 4224, f, f, f, f, 0.02, f, None, None)
     assert L.bt_matmul_plan_workspace_bytes(one, 1) == 3 * 2816 + 256   # 17 x 40 int32, rounded
 
 
@@ -442,8 +442,8 @@ def _cdiv(a, b):
 def test_gemm_plan_invariants_random():
     """Random GEMM plans (1-12 projections, M 17-5000, N 1-20000, K up to the cap):
     the header's slot count, the order by K, contiguous slot ranges, and for every
-    projection split along K (fewer than 128 tiles of 128 x 256, at least 24 stages
-    of 128) ranges of an even number of stages, of about 12 unless the cap of one
+    projection split along K (fewer than 128 tiles of 128 x 256, at least 32 stages
+    of 128) ranges of an even number of stages, of at most about 16 unless the cap of one
     range-tile per compute unit binds, covering K exactly once; slices and zeros
     256-byte aligned, disjoint and filling the workspace exactly."""
     L = bt.lib()
@@ -475,10 +475,10 @@ def test_gemm_plan_invariants_random():
             nst = _cdiv(k, 128)
             assert slots == min(64, _cdiv(tiles, 8)) and slot_begin == slot, (trial, i)
             slot += slots * splits
-            if tiles >= 128 or nst < 24:
+            if tiles >= 128 or nst < 32:
                 assert splits == 1 and ws == 0, (trial, i, splits)
                 continue
-            want = max(2, min(_cdiv(nst, 12), 256 // tiles))
+            want = max(2, min(_cdiv(nst, 16), 256 // tiles))
             assert sps % 2 == 0 and sps == _cdiv(_cdiv(nst, want), 2) * 2, (trial, i, sps)
             assert (splits - 1) * sps < nst <= splits * sps, (trial, i)   # K covered once
             assert 2 <= splits <= want and splits * tiles <= 256, (trial, i)
