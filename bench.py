@@ -1138,6 +1138,76 @@ def cpu_baseline(seconds: float):
             "configs": configs}
 
 
+def clock_under_load(torch, bt, seconds: float):
+    """The shader clock while the long-prefill stack's grouped GEMM launch (112
+    projections, M=4096, random int8 activations and ternary codes) runs back to
+    back for `seconds`: `rocm-smi --showclocks` is read every half second from a
+    host thread (a read-only query). The published int8 peak is stated at 2.4 GHz;
+    under this load the part runs lower."""
+    import re
+    import subprocess
+    import threading
+    dev = torch.device("cuda:0")
+    m = 4096
+    g = torch.Generator(device=dev).manual_seed(1)
+    xs = torch.rand(m, device=dev, generator=g) * 0.01
+    xsum = torch.randint(-1000, 1000, (m,), dtype=torch.int32, device=dev, generator=g)
+    items = []
+    for _layer in range(synth.N_LAYERS):
+        for _, k, n in synth.PROJECTIONS:
+            w = torch.randint(0, 255, (bt.repacked_bytes(n, k),), dtype=torch.uint8, device=dev,
+                              generator=g) & 0x55        # codes 0 and 1: weights -1 and 0
+            items.append({"xq": torch.randint(-127, 128, (m, k), dtype=torch.int8, device=dev,
+                                              generator=g),
+                          "xscale": xs, "xsum": xsum, "wdev": w, "n": n, "w_scale": 0.02,
+                          "y": torch.empty((m, n), device=dev)})
+    ops = sum(2 * m * it["n"] * it["xq"].shape[1] for it in items)
+    plan = bt.MatmulPlan(items)
+    plan.launch()
+    torch.cuda.synchronize()
+    samples, stop = [], threading.Event()
+
+    def sample():
+        while not stop.is_set():
+            try:
+                txt = subprocess.run(["rocm-smi", "--showclocks"], capture_output=True, text=True,
+                                     timeout=10).stdout
+            except (OSError, subprocess.SubprocessError):
+                return
+            mhz = [int(v) for v in re.findall(r"sclk clock level: \S+: \((\d+)Mhz\)", txt)]
+            if mhz:
+                samples.append(mhz[0])
+            stop.wait(0.5)
+
+    th = threading.Thread(target=sample, daemon=True)
+    started = False
+    t0 = time.time()
+    launches_ms = []
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    while time.time() - t0 < seconds:
+        a.record()
+        for _ in range(20):
+            plan.launch()
+        b.record()
+        torch.cuda.synchronize()
+        launches_ms.append(a.elapsed_time(b) / 20)
+        if not started and time.time() - t0 > 1.0:   # sample once the load is steady
+            th.start()
+            started = True
+        log(f"clock under load: {time.time() - t0:.1f}s, {launches_ms[-1]:.3f} ms per launch, "
+            f"sclk samples {samples[-3:]}")
+    stop.set()
+    if started:
+        th.join(timeout=15)
+    ms = float(np.median(launches_ms))
+    return {"workload": "the long-prefill stack's grouped GEMM launch back to back, random int8 "
+                        "operands", "seconds": seconds, "ms_per_launch_median": round(ms, 4),
+            "tops": round(ops / (ms * 1e-3) / 1e12, 1), "sclk_mhz_samples": samples,
+            "sclk_mhz_median": float(np.median(samples)) if samples else None,
+            "int8_peak_tops_at_that_clock": round(5000.0 * float(np.median(samples)) / 2400.0, 1)
+            if samples else None}
+
+
 def run_batched_decode(ds, out, args):
     """The decode step for a batch of 16 tokens, fused and as two launches."""
     b_ms, b_ok = ds.batched(16, max(1, args.steps // 2), args.trials)
@@ -1263,6 +1333,10 @@ def main():
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy (5 times), to scale the "
                          "FETCH_SIZE / WRITE_SIZE counters of a profiler run")
+    ap.add_argument("--clock-under-load", type=float, default=0.0, metavar="SECONDS",
+                    help="only run the long-prefill stack's grouped GEMM launch back to back "
+                         "for SECONDS (random int8 operands) and read the shader clock with "
+                         "rocm-smi meanwhile")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -1284,6 +1358,11 @@ def main():
 
     # torch before the library: libbt.so binds to the HIP runtime torch loads
     import torch
+
+    if args.clock_under_load > 0:
+        import ternary_weight_decoder_bt_amd as bt
+        print(json.dumps(clock_under_load(torch, bt, args.clock_under_load)), flush=True)
+        return
 
     packed_prefill = None
     if not args.no_prefill and not args.remainder_counters and not args.chain_only:
