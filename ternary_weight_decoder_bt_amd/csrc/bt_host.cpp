@@ -276,8 +276,11 @@ extern "C" bt_status bt_quant_plan_build(const bt_quant_desc* descs, int32_t cou
     if (!descs || !plan_host) return BT_ERR_NULL;
     if (count < 1) return BT_ERR_SHAPE;
     if (plan_bytes < bt_quant_plan_bytes(count)) return BT_ERR_WORKSPACE;
-    auto* hdr = static_cast<bt::PlanHeader*>(plan_host);
-    auto* out = reinterpret_cast<bt::QuantDesc*>(hdr + 1);
+    // everything is checked, the grid size included, before the plan is written
+    auto quant_blocks = [](const bt_quant_desc& q) {
+        return bt::quant_wave_rows(q.K) ? ceil_div(q.M, bt::kQuantThreads / 64) : q.M;
+    };
+    int64_t total = 0;
     for (int32_t i = 0; i < count; ++i) {
         const bt_quant_desc& q = descs[i];
         if (!q.x || !q.xq || !q.xscale || !q.xsum) return BT_ERR_NULL;
@@ -286,14 +289,17 @@ extern "C" bt_status bt_quant_plan_build(const bt_quant_desc* descs, int32_t cou
         if (!bt::aligned16(q.x) || !bt::aligned16(q.xq) || !bt::aligned16(q.xscale) ||
             !bt::aligned16(q.xsum))
             return BT_ERR_ALIGN;
+        total += quant_blocks(q);
     }
+    if (total > (int64_t(1) << 31) - 1) return BT_ERR_SHAPE;
+    auto* hdr = static_cast<bt::PlanHeader*>(plan_host);
+    auto* out = reinterpret_cast<bt::QuantDesc*>(hdr + 1);
     int64_t blocks = 0;
     for (int32_t i = 0; i < count; ++i) {
         const bt_quant_desc& q = descs[i];
         out[i] = bt::QuantDesc{q.x, q.xq, q.xscale, q.xsum, q.M, q.K, blocks};
-        blocks += bt::quant_wave_rows(q.K) ? ceil_div(q.M, bt::kQuantThreads / 64) : q.M;
+        blocks += quant_blocks(q);
     }
-    if (blocks > (int64_t(1) << 31) - 1) return BT_ERR_SHAPE;
     hdr->magic = bt::kPlanMagicQuant;
     hdr->count = count;
     hdr->total_blocks = blocks;

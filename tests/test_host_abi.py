@@ -321,6 +321,18 @@ def test_plan_building_on_host():
     assert L.bt_quant_plan_build(q, 2, host.ctypes.data, nb - 1) == WORKSPACE
     q[1].xsum = None
     assert L.bt_quant_plan_build(q, 2, host.ctypes.data, nb) == NULL
+    # a grid beyond 2^31 - 1 workgroups is refused before the plan is written
+    big = (BtQuantDesc * 2)(BtQuantDesc(f, f, f, f, 1 << 31, 8960),
+                            BtQuantDesc(f, f, f, f, 1 << 31, 8960))
+    host[:] = 0xAB
+    assert L.bt_quant_plan_build(big, 2, host.ctypes.data, nb) == SHAPE
+    assert (host == 0xAB).all()
+    big[1].M = 1            # 2^31 + 1 workgroups: still too many
+    assert L.bt_quant_plan_build(big, 2, host.ctypes.data, nb) == SHAPE
+    assert (host == 0xAB).all()
+    big[0].M = (1 << 31) - 2
+    assert L.bt_quant_plan_build(big, 2, host.ctypes.data, nb) == OK
+    assert host[:16].view(np.int64)[1] == (1 << 31) - 1
 
     m = (BtMatmulDesc * 2)(BtMatmulDesc(1, 2048, 1536, f, f, f, f, 0.02, f, None),
                            BtMatmulDesc(3, 1536, 8960, f, f, f, f, 0.03, f, f))
