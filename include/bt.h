@@ -375,7 +375,7 @@ size_t bt_matmul_plan_bytes(int32_t count);
  * fit one workgroup's LDS slice is split along K, and its partial sums meet in
  * the workspace through atomics. GEMMs: a projection with fewer 128 x 256
  * output tiles than a quarter of the GPU's resident workgroups and a K of at
- * least 32 stages of 128 is split into K ranges of at most about 16 stages; each range
+ * least 32 x 128 elements is split into K ranges of at most about 16 x 128; each range
  * stores its int32 partial sums in an M x N slice of the workspace, followed by
  * M int32 zeros. */
 size_t bt_matmul_plan_workspace_bytes(const bt_matmul_desc* descs, int32_t count);

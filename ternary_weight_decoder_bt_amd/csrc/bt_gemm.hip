@@ -9,8 +9,8 @@
 // (WA*WGM) x (WW*WGN) tile of y (token rows x weight rows); each wave owns a
 // WA x WW sub-tile held as (WA/16) x (WW/16) MFMA accumulators.
 //
-// K advances in stages (256 wide in the tiled ternary kernels, 128 in the
-// persistent one and for int8 weights). The workgroup's activation rows for a
+// K advances in stages (256 wide for ternary weights, 128 for int8 weights).
+// The workgroup's activation rows for a
 // stage (BM x KS int8) are copied from global memory straight into one of NS
 // LDS buffers (buffer_load ... lds: no staging registers), while another
 // buffer feeds the matrix cores. Rows past M, and columns past K, read as
@@ -620,18 +620,28 @@ __device__ __forceinline__ void gemm_persistent_body(const GemmArgs& g, int slot
     int aslot[NK];
 #pragma unroll
     for (int kk = 0; kk < NK; ++kk) aslot[kk] = slot_of(lane & 15, 4 * kk + (lane >> 4)) * 16;
+    // Per 64-wide step: the TW weight fragments unpacked once, then the TA
+    // activation fragments in two halves, each half through all TW weight
+    // tiles (half the activation registers of reading all TA up front).
+    static_assert(TA % 2 == 0, "two halves of activation fragments");
     auto consume = [&](int buf, const BVec (&bc)[TW]) {
         const int8_t* abuf = stage_buf(buf) + afrag;
 #pragma unroll
         for (int kk = 0; kk < NK; ++kk) {
-            v4i af[TA];
+            v4i bf[TW];
 #pragma unroll
-            for (int i = 0; i < TA; ++i) af[i] = lds_ld<v4i>(abuf + i * 16 * KS + aslot[kk]);
+            for (int t = 0; t < TW; ++t) bf[t] = unpack16(bc[t][kk]);
 #pragma unroll
-            for (int t = 0; t < TW; ++t) {
-                const v4i bf = unpack16(bc[t][kk]);
+            for (int h = 0; h < 2; ++h) {
+                v4i af[TA / 2];
 #pragma unroll
-                for (int i = 0; i < TA; ++i) acc[i][t] = mfma16x16x64(bf, af[i], acc[i][t]);
+                for (int i = 0; i < TA / 2; ++i)
+                    af[i] = lds_ld<v4i>(abuf + (h * TA / 2 + i) * 16 * KS + aslot[kk]);
+#pragma unroll
+                for (int t = 0; t < TW; ++t)
+#pragma unroll
+                    for (int i = 0; i < TA / 2; ++i)
+                        acc[h * TA / 2 + i][t] = mfma16x16x64(bf[t], af[i], acc[h * TA / 2 + i][t]);
             }
         }
     };
@@ -775,13 +785,16 @@ void gemm_persistent_grouped_kernel(const GemmArgs* __restrict__ descs, int32_t 
     const int lda = g.K;
     int local = slot - g.slot_begin;
     if (g.splits > 1) {
+        // ranges are counted in 128-element pieces of K (sps is even, so a
+        // range starts on a 256-wide weight step; the last may end half-way
+        // through one, which the body's K tail handles)
         const int r = local / g.slots;
         local -= r * g.slots;
-        const int base = r * g.sps;                 // first 128-wide stage (sps is even)
-        const int nst = (g.K + KS - 1) / KS;
-        g.xq += int64_t(base) * KS;
-        g.w += int64_t(base / 2) * 1024;            // two 128-wide stages per 1 KB step
-        g.K = min(g.sps, nst - base) * KS;
+        const int base = r * g.sps;                 // first 128-element piece of the range
+        const int pieces = (g.K + 127) / 128;
+        g.xq += int64_t(base) * 128;
+        g.w += int64_t(base / 2) * 1024;            // two pieces per 1 KB weight step
+        g.K = min(g.sps, pieces - base) * 128;
         g.acc = g.ws + int64_t(r) * g.ws_slice;
         g.xsum = g.ws + int64_t(g.splits) * g.ws_slice;
         g.y = nullptr;
@@ -814,11 +827,15 @@ bt_status launch_gemm(GemmArgs g, hipStream_t stream) {
 }
 
 // The persistent kernel's shape: waves of 128 tokens x 64 weight rows, four
-// side by side (tiles of 128 x 256), a 3-stage pipeline, two workgroups per
-// compute unit.
+// side by side (tiles of 128 x 256), 256-wide K stages in two buffers (64 KB of
+// LDS, plus 16 KB for the epilogue: two workgroups fill a compute unit's 160
+// KB), two workgroups per compute unit. Measured on the long-prefill stack's
+// grouped launch against 128-wide stages in three buffers: 4.51-4.54 ->
+// 4.41-4.42 ms (fewer waits and barriers per MFMA).
 constexpr int kPersistWA = bt::kPersistBM;
 constexpr int kPersistNW = bt::kPersistBN / 64;
-constexpr int kPersistNS = 3;
+constexpr int kPersistKS = 256;
+constexpr int kPersistNS = 2;
 constexpr int kPersistWgsPerCu = 2;
 
 // Compute units of the current device (queried on every call: the host keeps
@@ -861,7 +878,7 @@ bt_status launch_gemm_grouped(const bt::PlanHeader* hdr, const GemmArgs* dev_des
     const int64_t grid = hdr->total_blocks * kXcds;
     if (grid < 1 || grid > (int64_t(1) << 31) - 1) return BT_ERR_SHAPE;
     (void)hipGetLastError();
-    hipLaunchKernelGGL((gemm_persistent_grouped_kernel<kPersistWA, 64, kPersistNW, 128, kPersistNS>),
+    hipLaunchKernelGGL((gemm_persistent_grouped_kernel<kPersistWA, 64, kPersistNW, kPersistKS, kPersistNS>),
                        dim3(unsigned(grid)), dim3(64 * kPersistNW), 0, stream, dev_descs,
                        hdr->count);
     return hipGetLastError() == hipSuccess ? BT_OK : BT_ERR_DEVICE;
@@ -1081,7 +1098,7 @@ bt_status dispatch_gemm(GemmArgs g, bool int8_weights, void* workspace, size_t w
         return st;
     }
     if (c.kind == 0)
-        return launch_gemm_persistent<kPersistWA, 64, kPersistNW, 128, kPersistNS>(g, stream);
+        return launch_gemm_persistent<kPersistWA, 64, kPersistNW, kPersistKS, kPersistNS>(g, stream);
     st = c.kind == 3   ? launch_gemm<32, 32, 2, 2, 256, 2>(g, stream)
          : c.kind == 5 ? launch_gemm<64, 48, 2, 2, 256, 2>(g, stream)
          : c.kind == 2 ? launch_gemm<64, 64, 2, 2, 256, 2>(g, stream)

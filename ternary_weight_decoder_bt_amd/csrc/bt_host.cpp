@@ -332,12 +332,12 @@ static bt_status check_gemm_desc(const bt_matmul_desc& m) {
 
 // K ranges of a projection in a grouped GEMM plan: 1, unless it has fewer
 // output tiles than a quarter of the resident workgroup slots and a K of at
-// least two ranges of kPlanSplitStages 128-wide stages; then ranges of at most
-// about that many stages (an even number: a range starts on a 1 KB weight
+// least two ranges of kPlanSplitStages 128-element pieces; then ranges of at
+// most about that many pieces (an even number: a range starts on a 1 KB weight
 // step), at most one range-tile per compute unit. A plan's other projections
-// at K = 1536 have 12 stages per tile, so a range of a split projection takes
+// at K = 1536 have 12 pieces per tile, so a range of a split projection takes
 // about as long as one of their tiles (one layer at M = 512: down's 24 tiles of
-// 70 stages become 5 ranges of 14 stages over the same 24 tiles).
+// 70 pieces become 5 ranges of 14 pieces over the same 24 tiles).
 struct PlanSplit { int64_t splits, sps; };
 static PlanSplit gemm_plan_split(const bt_matmul_desc& m) {
     const int64_t tiles = ceil_div(m.M, bt::kPersistBM) * ceil_div(m.N, bt::kPersistBN);

@@ -187,9 +187,9 @@ constexpr int kPersistBM = 128;
 constexpr int kPersistBN = 256;
 constexpr int kXcds = 8;
 constexpr int kSlotsPerXcd = kGemmSlots / kXcds;
-// grouped GEMM plans: target 128-wide stages per K range of a split projection
-// (one layer at M = 512: ranges of 14 stages 43.0-43.8 us, of 12 44.4-44.7 us,
-// of 18 44.2-44.4 us, of 24 46.6-46.7 us)
+// grouped GEMM plans: target 128-element pieces of K per K range of a split
+// projection (one layer at M = 512: ranges of 14 pieces 43.0-43.8 us, of 12
+// 44.4-44.7 us, of 18 44.2-44.4 us, of 24 46.6-46.7 us)
 constexpr int kPlanSplitStages = 16;
 
 // Token-row bands per tile group of the GEMM's tile order: as many as one
