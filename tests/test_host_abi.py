@@ -372,7 +372,7 @@ def test_gemm_plan_building_on_host():
     """Descriptors with M > 16 build a grouped GEMM plan: quantized inputs only,
     no workspace, every descriptor on the same side of BT_GEMV_MAX_M; each
     projection gets min(64, its tiles per XCD) workgroup slots per XCD, and the
-    projections are ordered by K (stable)."""
+    projections are ordered by K, the longest first (stable)."""
     L = bt.lib()
     f = FAKE
     # one decoder layer at M=4096: qkv, o, gate_up (K=1536) and down (K=8960)
@@ -387,9 +387,12 @@ def test_gemm_plan_building_on_host():
     tiles = [32 * -(-n // 256) for n, _ in shapes]             # 128 x 256 output tiles
     slots = host[8:16].view(np.int64)[0]                        # slots per XCD in the grid
     assert slots == sum(min(64, -(-t // 8)) for t in tiles) == 32 + 24 + 64 + 24
-    # GemmArgs: 6 pointers, w_scale, then M, N, K (K at byte 60); K=8960 comes last
+    # GemmArgs: 6 pointers, w_scale, then M, N, K (K at byte 60); K=8960 comes first,
+    # the K=1536 projections keep their order (N at byte 56)
     ks = [host[16 + 152 * i + 60:16 + 152 * i + 64].view(np.int32)[0] for i in range(4)]
-    assert ks == [1536, 1536, 1536, 8960]
+    ns = [host[16 + 152 * i + 56:16 + 152 * i + 60].view(np.int32)[0] for i in range(4)]
+    assert ks == [8960, 1536, 1536, 1536]
+    assert ns == [1536, 2048, 1536, 17920]
     # a launch with a GEMM plan is refused by the quantize launcher
     assert L.bt_quantize_act_grouped(host.ctypes.data, f, None) == VALUE
     # mixing GEMV (M <= 16) and GEMM projections, fused inputs, missing inputs
@@ -453,7 +456,7 @@ def _cdiv(a, b):
 
 def test_gemm_plan_invariants_random():
     """Random GEMM plans (1-12 projections, M 17-5000, N 1-20000, K up to the cap):
-    the header's slot count, the order by K, contiguous slot ranges, and for every
+    the header's slot count, the order by K (longest first), contiguous slot ranges, and for every
     projection split along K (fewer than 128 tiles of 128 x 256, at least 32 stages
     of 128) ranges of an even number of stages, of at most about 16 unless the cap of one
     range-tile per compute unit binds, covering K exactly once; slices and zeros
@@ -477,7 +480,7 @@ def test_gemm_plan_invariants_random():
         d = host[16:16 + 152 * count].reshape(count, 152)
         i32 = lambda i, o: int(d[i, o:o + 4].view(np.int32)[0])   # noqa: E731
         i64 = lambda i, o: int(d[i, o:o + 8].view(np.int64)[0])   # noqa: E731
-        assert [i32(i, 60) for i in range(count)] == sorted(k for _, _, k in shapes), trial
+        assert [i32(i, 60) for i in range(count)] == sorted((k for _, _, k in shapes), reverse=True), trial
         slot, pieces = 0, []
         for i in range(count):
             mm, n, k = i32(i, 52), i32(i, 56), i32(i, 60)
