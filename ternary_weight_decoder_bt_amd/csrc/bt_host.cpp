@@ -99,7 +99,7 @@ namespace bt {
 // kGemvLdsBytes / (256 (M + 1)) steps; K is split only for that. (Splitting
 // K further for parallelism was measured to lose: the cross-workgroup
 // synchronization it needs costs more than the extra workgroups gain.)
-void gemv_shape(int64_t M, int64_t N, int64_t K, bool grouped, GemvDesc* d) {
+void gemv_shape(int64_t M, int64_t N, int64_t K, bool grouped, bool split_rows, GemvDesc* d) {
     memset(d, 0, sizeof(*d));
     d->M = int32_t(M);
     d->N = int32_t(N);
@@ -126,6 +126,20 @@ void gemv_shape(int64_t M, int64_t N, int64_t K, bool grouped, GemvDesc* d) {
             d->waves_per_tile *= 2;
     }
     d->groups = ceil_div(d->tiles, int64_t(kGemvWaves / d->waves_per_tile) * d->tiles_per_wave);
+    // A single call on quantized rows that still has few workgroups (one per
+    // tile of down, o or qkv at M = 1): split each tile's 16 weight rows over 2
+    // workgroups. Each loads only its rows' bytes, so the weights stream
+    // through twice as many compute units, and each stores only its rows, so
+    // nothing has to be combined across workgroups (down at M = 1: 5.40 ->
+    // 5.24 us, qkv 4.17 -> 3.89 us). Fused calls keep whole tiles: there each
+    // extra workgroup would quantize the token rows once more, and the
+    // measured chain of fused calls did not gain.
+    d->row_parts = 1;
+    if (!grouped && split_rows) {
+        while (d->row_parts < kGemvRowPartsMax && d->groups * chunks * d->row_parts * 2 <= kGemvFillBlocks)
+            d->row_parts *= 2;
+    }
+    d->groups *= d->row_parts;
     d->blocks = d->groups * chunks;
 }
 
@@ -214,7 +228,7 @@ extern "C" size_t bt_matmul_workspace_bytes(int64_t M, int64_t N, int64_t K) {
     if (M > BT_GEMV_MAX_M)
         return bt::gemm_workspace_bytes(bt::gemm_choice(M, N, K, false, true), M, N);
     bt::GemvDesc d;
-    bt::gemv_shape(M, N, K, false, &d);
+    bt::gemv_shape(M, N, K, false, true, &d);
     return bt::gemv_single_workspace_bytes(d);
 }
 
@@ -465,7 +479,7 @@ extern "C" size_t bt_matmul_plan_workspace_bytes(const bt_matmul_desc* descs, in
         if (descs[i].M < 1 || descs[i].M > BT_GEMV_MAX_M || !valid_nk(descs[i].N, descs[i].K))
             return 0;
         bt::GemvDesc d;
-        bt::gemv_shape(descs[i].M, descs[i].N, descs[i].K, true, &d);
+        bt::gemv_shape(descs[i].M, descs[i].N, descs[i].K, true, false, &d);
         total += bt::gemv_workspace_bytes(d);
     }
     return total;
@@ -508,7 +522,7 @@ extern "C" bt_status bt_matmul_plan_build(const bt_matmul_desc* descs, int32_t c
     int64_t total_blocks = 0;
     for (int32_t i = 0; i < count; ++i) {
         bt::GemvDesc d;
-        bt::gemv_shape(descs[i].M, descs[i].N, descs[i].K, true, &d);
+        bt::gemv_shape(descs[i].M, descs[i].N, descs[i].K, true, false, &d);
         total_blocks += d.blocks;
     }
     if (total_blocks > int64_t(1) << 31) return BT_ERR_SHAPE;   // nothing written yet
@@ -518,7 +532,7 @@ extern "C" bt_status bt_matmul_plan_build(const bt_matmul_desc* descs, int32_t c
     for (int32_t i = 0; i < count; ++i) {
         const bt_matmul_desc& m = descs[i];
         bt::GemvDesc d;
-        bt::gemv_shape(m.M, m.N, m.K, true, &d);
+        bt::gemv_shape(m.M, m.N, m.K, true, false, &d);
         d.x = m.x;
         d.xq = const_cast<int8_t*>(m.xq);
         d.xscale = const_cast<float*>(m.xscale);

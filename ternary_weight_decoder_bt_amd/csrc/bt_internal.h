@@ -35,6 +35,10 @@ constexpr int64_t kMaxK = BT_MAX_K;
 constexpr int kGemvBatch = 6;
 constexpr int kGemvLdsBytes = 40960;
 constexpr int kGemvFillWaves = 1024;   // waves that keep every compute unit streaming
+// Single calls with fewer workgroups than this split each tile's 16 weight rows
+// over up to kGemvRowPartsMax workgroups (see gemv_shape).
+constexpr int kGemvFillBlocks = 256;
+constexpr int kGemvRowPartsMax = 2;
 constexpr int kGemvGroupedTilesPerWave = 2;
 
 // Epilogue on the fp32 output (all optional): bias add, ReLU, per-output
@@ -92,7 +96,10 @@ struct GemvDesc {
                             // calls); 0 = atomics into ws, last chunk finishes (plans)
     int32_t waves_per_tile; // 1, 2 or 4: a tile's K range within a chunk is split over
                             // this many waves of one workgroup (tiles_per_wave is then 1)
-    int64_t groups;         // workgroups per chunk = ceil(tiles / (4 * tiles_per_wave))
+    int32_t row_parts;      // 1, 2 or 4: a tile's 16 weight rows are split over this many
+                            // workgroups, each loading and storing its 16 / row_parts rows
+    int32_t pad_;
+    int64_t groups;         // workgroups per chunk = ceil(tiles / (4 * tiles_per_wave)) * row_parts
     int64_t block_begin;    // first workgroup of this problem in a grouped launch
     int64_t blocks;         // workgroups of this problem = groups * chunks
     EpiArgs epi;            // zero: no epilogue
@@ -146,7 +153,7 @@ struct PlanHeader {
 
 // Work split of a GEMV: K is split only where the activations do not fit one
 // workgroup's LDS slice.
-void gemv_shape(int64_t M, int64_t N, int64_t K, bool grouped, GemvDesc* d);
+void gemv_shape(int64_t M, int64_t N, int64_t K, bool grouped, bool split_rows, GemvDesc* d);
 size_t gemv_workspace_bytes(const GemvDesc& d);          // plans: atomics + counters
 size_t gemv_partial_bytes(const GemvDesc& d);
 size_t gemv_single_workspace_bytes(const GemvDesc& d);   // single calls: slices + d, row sums

@@ -571,12 +571,15 @@ struct GemvBatch {
 // Loads steps sb .. sb+kB-1 of a tile, clamping the step to `last` (a repeated
 // step is a cache hit and is never consumed): no branches, so the compiler
 // can count the loads in flight exactly.
+// `wl` is the lane whose 16 bytes this lane loads: itself, or with row parts a
+// lane of the same K piece in the workgroup's own rows (two lanes then read one
+// address, which costs one fetch).
 __device__ __forceinline__ void gemv_issue(GemvBatch& b, const uint8_t* wt, int sb, int last,
-                                           int lane) {
+                                           int wl) {
 #pragma unroll
     for (int u = 0; u < kB; ++u) {
         const int st = min(sb + u, last);
-        b.w[u] = gld_stream<v4u>(wt + int64_t(st) * 1024 + lane * 16);
+        b.w[u] = gld_stream<v4u>(wt + int64_t(st) * 1024 + wl * 16);
     }
 }
 
@@ -618,7 +621,11 @@ __device__ __forceinline__ int32_t gemv_row_sum(const GemvShared& sh, int m) {
 // product for a 16-token batch (measured: the down projection 16.5 -> 1.4 us
 // per layer without it).
 __device__ __forceinline__ void gemv_finish(const GemvDesc& d, int64_t tile, v4i c, int lane,
-                                            const GemvShared& sh, int chunk) {
+                                            const GemvShared& sh, int chunk, bool own_row) {
+    // With row parts (single calls only), a lane outside the workgroup's rows
+    // holds a copy of another row's sums and stores nothing. Plans never split
+    // rows, so every lane of a plan's wave reaches the atomics below.
+    if (!own_row) return;
     const int kq = lane >> 4;
     const int64_t n = tile * bt::kTileN + (lane & 15);
     if (d.chunks > 1 && d.slices) {
@@ -840,7 +847,16 @@ __device__ __forceinline__ void gemv_block(const GemvDesc& d, int64_t local_bloc
     const int wave = tid >> 6;
     const int lane = tid & 63;
     const int chunk = int(local_block / d.groups);
-    const int64_t g = local_block - int64_t(chunk) * d.groups;
+    const int64_t gp = local_block - int64_t(chunk) * d.groups;
+    // row part `part` of the tiles of workgroup group g: weight rows
+    // [part * rp, (part + 1) * rp) of each 16-row tile
+    // (grouped launches never split rows: their count is fixed at 1 here)
+    const int parts = kWaveSplit ? d.row_parts : 1;
+    const int64_t g = gp / parts;
+    const int part = int(gp - g * parts);
+    const int rp = bt::kTileN / parts;
+    const int wl = (lane & ~15) | (part * rp + (lane & 15) % rp);
+    const bool own_row = (lane & 15) / rp == part;
     const int s0 = chunk * d.steps_per_chunk;
     const int s1 = min(s0 + d.steps_per_chunk, d.steps);
     const int nsteps = s1 - s0;
@@ -867,7 +883,7 @@ __device__ __forceinline__ void gemv_block(const GemvDesc& d, int64_t local_bloc
         const int r = idx / nb;
         const int bb = idx - r * nb;
         const int64_t t = min(tile0 + int64_t(tile_stride) * r, int64_t(d.tiles) - 1);
-        gemv_issue(b, d.w + t * tile_bytes, ws0 + bb * kB, ws1 - 1, lane);
+        gemv_issue(b, d.w + t * tile_bytes, ws0 + bb * kB, ws1 - 1, wl);
     };
 
     // The first weight batches go out before the activations are staged, so
@@ -903,6 +919,10 @@ __device__ __forceinline__ void gemv_block(const GemvDesc& d, int64_t local_bloc
     }
     FusedRow<R> r0;
     if (kFused) gemv_load_row(r0, d, 0);
+    // Single calls: keep token 0's loads ahead of the weights' (left to itself,
+    // the compiler issued the long-row kernel's weight loads first, and the row
+    // then waited for them); grouped launches already keep this order.
+    if constexpr (kFused && kWaveSplit) __builtin_amdgcn_sched_barrier(0);
     GemvBatch b0, b1;
     issue(b0, 0);
     if (!kFused) issue(b1, min(1, total - 1));
@@ -914,7 +934,7 @@ __device__ __forceinline__ void gemv_block(const GemvDesc& d, int64_t local_bloc
             const int col = (i - m * pieces) * 16;
             if (m == d.M || kbeg + col >= d.K) lds_st<v4i>(lds + m * d.lds_row + col, v4i{0, 0, 0, 0});
         }
-        gemv_quantize_rows(d, r0, chunk == 0 && g == 0, kbeg, kend, lds, sh);
+        gemv_quantize_rows(d, r0, chunk == 0 && gp == 0, kbeg, kend, lds, sh);
         issue(b1, min(1, total - 1));
     } else {
         int first = 0;
@@ -962,7 +982,7 @@ __device__ __forceinline__ void gemv_block(const GemvDesc& d, int64_t local_bloc
         cur = gemv_consume(b, min(kB, nsteps_w - bb * kB), abase + (ws0 - s0 + bb * kB) * 256,
                            cur);
         if (bb == nb - 1 && wpt == 1) {
-            gemv_finish(d, t, cur, lane, sh, chunk);
+            gemv_finish(d, t, cur, lane, sh, chunk, own_row);
             cur = v4i{0, 0, 0, 0};
         }
     };
@@ -989,7 +1009,7 @@ __device__ __forceinline__ void gemv_block(const GemvDesc& d, int64_t local_bloc
         __syncthreads();
         if (sub == 0 && tile0 < d.tiles) {
             for (int s = 1; s < wpt; ++s) cur += part[(wave + s) * 64 + lane];
-            gemv_finish(d, tile0, cur, lane, sh, chunk);
+            gemv_finish(d, tile0, cur, lane, sh, chunk, own_row);
         }
     }
 }
@@ -1157,7 +1177,7 @@ extern "C" bt_status bt_ternary_matmul_fused(int64_t M, int64_t N, int64_t K, co
         return BT_ERR_ALIGN;
     if (!isfinite(w_scale)) return BT_ERR_VALUE;
     GemvDesc d;
-    bt::gemv_shape(M, N, K, false, &d);
+    bt::gemv_shape(M, N, K, false, false, &d);
     const bt_status st = gemv_bind_workspace(d, workspace, workspace_bytes);
     if (st != BT_OK) return st;
     d.x = x;
@@ -1233,7 +1253,7 @@ static bt_status matmul_impl(int64_t M, int64_t N, int64_t K, const int8_t* xq,
     if (est != BT_OK) return est;
     if (M <= BT_GEMV_MAX_M) {
         GemvDesc d;
-        bt::gemv_shape(M, N, K, false, &d);
+        bt::gemv_shape(M, N, K, false, true, &d);
         const bt_status st = gemv_bind_workspace(d, workspace, workspace_bytes);
         if (st != BT_OK) return st;
         d.xq = const_cast<int8_t*>(xq);

@@ -259,6 +259,18 @@ def test_gemv_wave_split_k(dev, m, n, k, fused):
         check_full(c, dev)
 
 
+# Single calls on quantized rows that still have few workgroups split each
+# tile's 16 weight rows over two workgroups, each loading and storing its own 8:
+# N = 8 leaves the second half of the only tile empty, N = 9 one valid row in
+# it, N = 24 half a tile at the end; the down (8960 -> 1536) and qkv
+# (1536 -> 2048) shapes run split too, and K = 8960 also splits each tile's K
+# range over the waves of its workgroup.
+@pytest.mark.parametrize("m,n,k", [(1, 8, 8960), (3, 9, 8960), (2, 24, 1536),
+                                   (1, 1536, 8960), (3, 2048, 1536)])
+def test_gemv_row_parts(dev, m, n, k):
+    check_full(synth.small_problem(37, m, n, k, "outlier"), dev)
+
+
 _REMAINDER_W = {}
 
 
